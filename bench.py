@@ -1,0 +1,243 @@
+#!/usr/bin/env python3
+"""Throughput of lscd_spmm (Load-as-Sparse, Compute-as-Dense skinny SpMM) on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--config 2] [--shape 0] [--n N] [--sparsity S]
+
+A step is one lscd_spmm call, C[N][M] = A_sparse[M][K] . B[N][K]^T, over inputs already
+resident in HBM; the format is encoded once before timing (ahead of time, as the method
+prescribes).  To keep the 256 MB Infinity Cache from serving A, the timed loop rotates over
+several device copies of the encoded matrix whose total exceeds three times that cache.
+
+Printed (one JSON line on stdout):
+  value         effective GB/s = (4*nnz + 4*(tiles+1) + 2*K*N + 2*M*N) / wall time per step
+  tflops        dense-equivalent 2*M*N*K / wall time per step
+  roofline      the product kernel's algorithmic bytes / its average duration from HIP
+                events recorded around every timed launch, against 8 TB/s HBM
+  dense_hipblaslt  the same product as a dense fp16 GEMM (torch -> hipBLASLt), timed the same way
+  cpu_baseline  the CPU oracle on a bounded row sample (reported baseline only)
+"""
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MALL_BYTES = 256 << 20
+HBM_PEAK_GBS = 8000.0
+METRIC = "dense-equiv TFLOPS & effective HBM GB/s (% of roofline) per skinny SpMM, 1 GPU"
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=2, help="1..5: tiny, OPT-30B MLP1, OPT-66B QKV, "
+                                                           "OPT-175B MLP2, OPT-175B layer at 50%%")
+    ap.add_argument("--shape", type=int, default=0, help="config 5 only: 0 QKV, 1 OutProj, 2 MLP1, 3 MLP2")
+    ap.add_argument("--n", type=int, default=None, help="batch width N (default: the config's)")
+    ap.add_argument("--sparsity", type=float, default=None, help="override the config's sparsity")
+    ap.add_argument("--copies", type=int, default=0, help="encoded copies rotated in the timed loop (0: auto)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-dense", action="store_true", help="skip the dense hipBLASLt baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU baseline sample budget")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="only run a plain 1 GiB device copy (scale for the HBM byte counters)")
+    return ap.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for rel in ("unstructured_sparse_skinny_amd/csrc/lscd_kernels.hip",
+                "unstructured_sparse_skinny_amd/csrc/lscd_api.cpp"):
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def calibrate():
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "device copy", "bytes_read_per_dispatch": n, "bytes_written_per_dispatch": n,
+                      "dispatches": 5}))
+
+
+def time_calls(fn_args, steps, warmup, torch):
+    """Run `steps` timed calls (after `warmup`), rotating over fn_args; HIP events around each call."""
+    stream = torch.cuda.current_stream()
+    k = len(fn_args)
+    for i in range(warmup):
+        f, a = fn_args[i % k]
+        f(*a)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        f, a = fn_args[i % k]
+        starts[i].record(stream)
+        f(*a)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    ev.sort()
+    return wall / steps * 1e3, sum(ev) / len(ev), ev[len(ev) // 2], ev[len(ev) // 10], ev[(len(ev) * 9) // 10]
+
+
+def cpu_baseline(case, alg_bytes, flops, budget_s):
+    """The oracle's fp64 product on a bounded sample of rows, scaled to the same units as `value`."""
+    import numpy as np
+    from oracle import spmm as osp
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"), default=1)
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    rng = np.random.default_rng(0)
+    probe = np.sort(rng.choice(case.M, size=min(case.M, 256), replace=False))
+    t0 = time.perf_counter()
+    osp.spmm_f64(case.A16, case.mask, case.B16, rows=probe)
+    t_probe = time.perf_counter() - t0
+    rows_n = int(min(case.M, max(len(probe), len(probe) * budget_s / max(t_probe, 1e-6))))
+    rows = np.sort(rng.choice(case.M, size=rows_n, replace=False))
+    t0 = time.perf_counter()
+    osp.spmm_f64(case.A16, case.mask, case.B16, rows=rows)
+    dt = time.perf_counter() - t0
+    frac = rows_n / case.M
+    return {"value": round(alg_bytes * frac / dt / 1e9, 3), "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle", "tflops": round(flops * frac / dt / 1e12, 5), "seconds": round(dt, 2),
+            "sample": f"{rows_n} of {case.M} rows (random, seed 0) of the same matrices; fp64 numpy/BLAS product "
+                      f"of the masked rows; bytes and flops scaled by the row fraction"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); multi-GPU runs are not part of this "
+              "build: the product shards by rows or by K with no kernel change (see the design notes).",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    if args.calibrate:
+        calibrate()
+        return
+    import lscd_synth as syn
+    import unstructured_sparse_skinny_amd as L
+
+    torch.cuda.set_device(0)
+    props = torch.cuda.get_device_properties(0)
+    t_gen = time.perf_counter()
+    case = syn.make_config(args.config, args.shape, N=args.n, sparsity=args.sparsity)
+    M, K, N = case.M, case.K, case.N
+    log(f"[bench] {case.name}: M={M} K={K} N={N} sparsity={case.sparsity:.4f} "
+        f"(generated in {time.perf_counter() - t_gen:.1f}s)")
+
+    t_enc = time.perf_counter()
+    words, offs = L.lscd_pack(case.A16, case.mask)
+    h0 = L.lscd_import(words, offs, M, K)
+    info = h0.info
+    fmt_bytes = info["format_bytes"]
+    copies = args.copies or max(2, min(32, math.ceil(3 * MALL_BYTES / fmt_bytes) + 1))
+    handles = [h0] + [L.lscd_import(words, offs, M, K) for _ in range(copies - 1)]
+    del words, offs
+    log(f"[bench] encoded {copies} copies of {fmt_bytes / 1e6:.1f} MB in {time.perf_counter() - t_enc:.1f}s; "
+        f"splits={info['splits']} reg_vectors={info['reg_vectors']} max_tile_words={info['max_tile_words']}")
+
+    nnz, tiles = info["nnz"], info["num_tiles"]
+    alg_bytes = 4 * nnz + 4 * (tiles + 1) + 2 * K * N + 2 * M * N
+    flops = 2 * M * N * K
+
+    B = torch.from_numpy(case.B16.view(np.float16)).to("cuda")
+    C = torch.empty((N, M), dtype=torch.float16, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    fn = L._lib.lscd_spmm
+
+    def checked(*a):
+        st = fn(*a)
+        if st != 0:
+            raise L.LSCDError(st, "lscd_spmm")
+
+    calls = [(checked, (ctypes.c_void_p(h.ptr), ctypes.c_void_p(B.data_ptr()), ctypes.c_void_p(C.data_ptr()),
+                        N, ctypes.c_void_p(stream))) for h in handles]
+    log("[bench] timing lscd_spmm")
+    ms_step, ev_mean, ev_med, ev_p10, ev_p90 = time_calls(calls, args.steps, args.warmup, torch)
+    if not torch.isfinite(C.float()).all():
+        raise RuntimeError("non-finite output")
+    value = alg_bytes / (ms_step * 1e-3) / 1e9
+    achieved = alg_bytes / (ev_mean * 1e-3) / 1e9
+    log(f"[bench] lscd: {ms_step * 1e3:.1f} us/step wall, kernel events mean {ev_mean * 1e3:.1f} us "
+        f"(p10 {ev_p10 * 1e3:.1f}, p50 {ev_med * 1e3:.1f}, p90 {ev_p90 * 1e3:.1f}) -> {achieved:.0f} GB/s")
+
+    dense = None
+    if not args.no_dense:
+        log("[bench] timing dense fp16 GEMM (torch -> hipBLASLt)")
+        dense_bytes = 2 * M * K + 2 * K * N + 2 * M * N
+        Ad = torch.from_numpy(np.where(case.mask.astype(bool), case.A16, 0).astype(np.uint16).view(np.float16))
+        ncopy = max(2, min(16, math.ceil(3 * MALL_BYTES / (2 * M * K)) + 1))
+        Ads = [Ad.to("cuda") for _ in range(ncopy)]
+        del Ad
+        Cd = torch.empty((N, M), dtype=torch.float16, device="cuda")
+        dcalls = [(lambda x, y: torch.mm(x, y, out=Cd), (B, a.t())) for a in Ads]
+        d_ms, d_mean, d_med, _, _ = time_calls(dcalls, args.steps, args.warmup, torch)
+        dense = {"ms_per_step": round(d_ms, 5), "kernel_ms_mean": round(d_mean, 5),
+                 "effective_gbs": round(dense_bytes / (d_ms * 1e-3) / 1e9, 1),
+                 "tflops": round(flops / (d_ms * 1e-3) / 1e12, 2), "copies": ncopy,
+                 "lscd_speedup": round(d_ms / ms_step, 3),
+                 "blas": str(torch.backends.cuda.preferred_blas_library())}
+        log(f"[bench] dense: {d_ms * 1e3:.1f} us/step -> speedup of lscd {d_ms / ms_step:.2f}x")
+        del Ads
+
+    cpu = None
+    if not args.no_cpu:
+        log("[bench] CPU oracle baseline")
+        cpu = cpu_baseline(case, alg_bytes, flops, args.cpu_seconds)
+
+    traffic = None
+    tpath = os.path.join(ROOT, "profiles", f"traffic_{case.name}.json")
+    if os.path.exists(tpath):
+        with open(tpath) as f:
+            t = json.load(f)
+        if t.get("kernel_source_hash") == kernel_source_hash():
+            traffic = t.get("hbm_bytes_per_launch")
+
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+        "config": {"workload": case.name, "M": M, "K": K, "N": N, "sparsity": round(case.sparsity, 4),
+                   "nnz": nnz, "tile": f"{info['tile_m']}x{info['tile_k']}", "splits": info["splits"],
+                   "copies_rotated": copies, "gpu": props.name, "cus": props.multi_processor_count},
+        "tflops": round(flops / (ms_step * 1e-3) / 1e12, 2),
+        "pct_roofline": round(100 * value / HBM_PEAK_GBS, 1),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "kernel": "lscd_spmm (product kernel + split-K pass)", "bytes_per_launch": alg_bytes,
+                     "kernel_us_mean": round(ev_mean * 1e3, 2), "kernel_us_p50": round(ev_med * 1e3, 2)},
+        "dense_hipblaslt": dense,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,161 @@
+/*
+ * lscd.h -- Load-as-Sparse, Compute-as-Dense (LSCD) sparse x skinny matrix product
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (Flash-LLM paper review, xllm-io, section 3 "core formulas"):
+ *     C = A x B,  A: M x K pruned fp16 weights (unstructured sparsity),
+ *                 B: K x N dense fp16 activations, N small (1..64 here).
+ * The product is memory-bound for small N, so A is moved in a compressed form and
+ * decompressed on chip into a dense tile that the matrix cores multiply (section 2
+ * "solution": load as sparse, compute as dense; redundant multiplications by the
+ * pruned zeros are accepted).
+ *
+ * Memory layouts (the pages leave them open; this library's convention):
+ *   B: device fp16, N rows of K elements, row-major      (B[n*K + k], i.e. K x N column-major)
+ *   C: device fp16, N rows of M elements, row-major      (C[n*M + m], i.e. M x N column-major)
+ *   This is the layout of Y = X . W^T for a batch of N token vectors X[N][K].
+ *   fp16 values travel as their 16-bit patterns (uint16_t) on the host side.
+ *
+ * The compressed format (Tiled-CSL; same review, section 3 "Tiled-CSL sparse encoding
+ * format"): A is cut into tile_m x tile_k tiles, ordered row-block-major
+ * (t = bm * ceil(K/tile_k) + bk).  Each kept entry is one 32-bit word:
+ *     bits [15:0]  fp16 value bits,
+ *     bits [31:16] in-tile index r * tile_k + c (row-major inside the tile),
+ * so tile_m * tile_k <= 65536.  Words are stored tile after tile; a tile holding n
+ * entries occupies round_up(n, 4) words (whole 128-bit vectors), the extra words being
+ * exact copies of one of the tile's real words; an empty tile occupies none.  The word
+ * order inside a tile is free (this library's encoder orders it for LDS banks).
+ * tile_offsets has num_tiles + 1 entries: tile t holds words
+ * [tile_offsets[t], tile_offsets[t+1]); tile_offsets[0] = 0.
+ *
+ * Errors: every call returns a status and never aborts or throws across this ABI.
+ * Thread safety: distinct handles may be used from distinct threads; one handle must
+ * not run lscd_spmm concurrently on two streams (it owns one split-K workspace).
+ */
+#ifndef LSCD_H_
+#define LSCD_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct lscd_handle_s* lscd_handle_t;
+
+typedef enum {
+    LSCD_SUCCESS = 0,
+    LSCD_ERROR_INVALID_VALUE = 1,   /* bad pointer, size, alignment, device or tile shape   */
+    LSCD_ERROR_NOT_SUPPORTED = 2,   /* valid request outside what the kernels implement     */
+    LSCD_ERROR_OUT_OF_MEMORY = 3,   /* host or device allocation failed                      */
+    LSCD_ERROR_INVALID_FORMAT = 4,  /* imported arrays are not a valid encoding              */
+    LSCD_ERROR_HIP = 5              /* a HIP runtime call failed (launch or copy)            */
+} lscd_status_t;
+
+typedef struct {
+    int64_t M, K;               /* matrix shape                                            */
+    int32_t tile_m, tile_k;     /* tile shape of the format                                */
+    int64_t num_tiles;          /* ceil(M/tile_m) * ceil(K/tile_k)                         */
+    int64_t nnz;                /* stored positions (distinct entries), padding excluded   */
+    int64_t nnz_padded;         /* words in the nonzeros array                             */
+    int64_t format_bytes;       /* 4 * nnz_padded + 4 * (num_tiles + 1)                    */
+    int32_t max_tile_words;     /* largest tile, in words                                  */
+    int32_t device;             /* HIP device the handle's buffers live on                 */
+    int64_t workspace_bytes;    /* device split-K workspace owned by the handle            */
+    int32_t splits;             /* K-splits lscd_spmm uses for this matrix                 */
+    int32_t reg_vectors;        /* 128-bit staging registers per lane and tile (kernel cfg) */
+} lscd_info_t;
+
+#define LSCD_DEFAULT_TILE_M 64
+#define LSCD_DEFAULT_TILE_K 64
+#define LSCD_MAX_N 64
+
+/*
+ * lscd_pack_size -- host only, no GPU needed.  Sizes of the encoding of (A, mask).
+ *   A      host, M*K fp16 bit patterns, row-major; read only.
+ *   mask   host, M*K bytes, nonzero = keep; NULL keeps every entry whose value is not
+ *          +0/-0 ((bits & 0x7FFF) != 0).  With a mask, kept zeros are stored as well.
+ *   tile_m, tile_k  tile shape, 1 <= tile_m*tile_k <= 65536.
+ *   nnz_padded, num_tiles  out: words and tiles of the encoding.
+ * Returns INVALID_VALUE for null outputs/A, M or K < 1, or a bad tile; NOT_SUPPORTED when
+ * the encoding would need 2^32 words or more.
+ */
+lscd_status_t lscd_pack_size(const uint16_t* A, const uint8_t* mask, int64_t M, int64_t K,
+                             int32_t tile_m, int32_t tile_k, int64_t* nnz_padded, int64_t* num_tiles);
+
+/*
+ * lscd_pack -- host only, no GPU needed.  Ahead-of-time encoding of (A, mask) into
+ * caller-owned host arrays (Flash-LLM review, section 3: the format is built offline).
+ *   nonzeros      out, nonzeros_len >= nnz_padded words.
+ *   tile_offsets  out, tile_offsets_len >= num_tiles + 1 entries.
+ * Same argument rules as lscd_pack_size; INVALID_VALUE if an output is too short.
+ */
+lscd_status_t lscd_pack(const uint16_t* A, const uint8_t* mask, int64_t M, int64_t K,
+                        int32_t tile_m, int32_t tile_k,
+                        uint32_t* nonzeros, int64_t nonzeros_len,
+                        uint32_t* tile_offsets, int64_t tile_offsets_len);
+
+/*
+ * lscd_encode -- pack (A, mask) with the default 64 x 64 tiles and upload it to the
+ * current HIP device.  Synchronous: the upload is complete on return.  *out receives a
+ * handle that owns all device buffers (format and split-K workspace) until
+ * lscd_destroy.  A and mask are read only during the call.
+ */
+lscd_status_t lscd_encode(const uint16_t* A, const uint8_t* mask, int64_t M, int64_t K,
+                          lscd_handle_t* out);
+
+/* lscd_encode_tiled -- lscd_encode with an explicit tile shape. */
+lscd_status_t lscd_encode_tiled(const uint16_t* A, const uint8_t* mask, int64_t M, int64_t K,
+                                int32_t tile_m, int32_t tile_k, lscd_handle_t* out);
+
+/*
+ * lscd_import -- validate a caller-built encoding (host arrays, as described above) and
+ * upload it to the current device.  Returns INVALID_FORMAT when tile_offsets is not
+ * non-decreasing from 0, a tile's word count is not a multiple of 4, the last offset is
+ * not the word count given, an index leaves its tile or the matrix, or two words of a
+ * tile address one position with different values.
+ *   nnz_padded  number of words in nonzeros (must equal tile_offsets[num_tiles]).
+ */
+lscd_status_t lscd_import(const uint32_t* nonzeros, int64_t nnz_padded, const uint32_t* tile_offsets,
+                          int64_t M, int64_t K, int32_t tile_m, int32_t tile_k, lscd_handle_t* out);
+
+/* lscd_export -- copy the handle's encoding back into host arrays of nnz_padded words
+ * and num_tiles + 1 offsets (sizes from lscd_get_info).  Synchronous. */
+lscd_status_t lscd_export(lscd_handle_t h, uint32_t* nonzeros, uint32_t* tile_offsets);
+
+/* lscd_get_info -- describe a handle (no device work). */
+lscd_status_t lscd_get_info(lscd_handle_t h, lscd_info_t* info);
+
+/*
+ * lscd_spmm -- C = A x B on `stream` (a hipStream_t; NULL = the null stream).
+ *   B  device, N x K fp16 row-major, 16-byte aligned, read only.
+ *   C  device, N x M fp16 row-major, 16-byte aligned, fully overwritten.
+ *   N  0 is a no-op; 1..64 supported; > 64 returns NOT_SUPPORTED.
+ * Asynchronous: returns after enqueueing; launch failures return LSCD_ERROR_HIP.  No
+ * allocation or synchronisation inside.  The current device must be the handle's
+ * device (INVALID_VALUE otherwise).  Accumulation is fp32, C is rounded once to fp16
+ * (nearest-even).  When K is split across workgroups, fp32 partial sums are added in
+ * ascending split order by a second pass, so results are bit-reproducible run to run.
+ */
+lscd_status_t lscd_spmm(lscd_handle_t h, const void* B, void* C, int32_t N, void* stream);
+
+/*
+ * lscd_debug_decode -- write the dense M x K fp16 matrix the handle encodes into the
+ * device buffer A_dense (row-major, 16-byte aligned), on `stream`.  Uses the same
+ * load-and-extract device code as lscd_spmm, so it shows exactly what the product
+ * multiplies.  Asynchronous like lscd_spmm.
+ */
+lscd_status_t lscd_debug_decode(lscd_handle_t h, void* A_dense, void* stream);
+
+/* lscd_destroy -- free the handle and its device buffers; NULL is a no-op.  The caller
+ * must make sure no work using the handle is still running. */
+lscd_status_t lscd_destroy(lscd_handle_t h);
+
+/* lscd_status_string -- static text for a status code. */
+const char* lscd_status_string(lscd_status_t s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LSCD_H_ */

@@ -1,0 +1,211 @@
+"""Thin Python binding of liblscd.so (the C ABI declared in include/lscd.h).
+
+Argument marshalling only: every step of the product runs in the HIP library.  The
+functions carry the C names.  Host arrays are numpy (fp16 as uint16 bit patterns);
+device buffers are torch CUDA tensors, used only for their memory and the current
+stream.  Importing this module loads the library and fails loudly if it is not built.
+
+torch is imported before the library is loaded, so the library binds to the HIP runtime
+torch already loaded (both carry the soname libamdhip64.so.7) and torch's stream handles
+are valid in it.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+import torch  # noqa: F401  (must come before loading the library, see above)
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liblscd.so")
+
+LSCD_SUCCESS = 0
+LSCD_ERROR_INVALID_VALUE = 1
+LSCD_ERROR_NOT_SUPPORTED = 2
+LSCD_ERROR_OUT_OF_MEMORY = 3
+LSCD_ERROR_INVALID_FORMAT = 4
+LSCD_ERROR_HIP = 5
+LSCD_DEFAULT_TILE_M = 64
+LSCD_DEFAULT_TILE_K = 64
+LSCD_MAX_N = 64
+
+#: Every entry point include/lscd.h declares.
+EXPORTS = ("lscd_pack_size", "lscd_pack", "lscd_encode", "lscd_encode_tiled", "lscd_import", "lscd_export",
+           "lscd_get_info", "lscd_spmm", "lscd_debug_decode", "lscd_destroy", "lscd_status_string")
+
+
+class lscd_info_t(ctypes.Structure):
+    _fields_ = [("M", ctypes.c_int64), ("K", ctypes.c_int64), ("tile_m", ctypes.c_int32),
+                ("tile_k", ctypes.c_int32), ("num_tiles", ctypes.c_int64), ("nnz", ctypes.c_int64),
+                ("nnz_padded", ctypes.c_int64), ("format_bytes", ctypes.c_int64),
+                ("max_tile_words", ctypes.c_int32), ("device", ctypes.c_int32),
+                ("workspace_bytes", ctypes.c_int64), ("splits", ctypes.c_int32), ("reg_vectors", ctypes.c_int32)]
+
+
+class LSCDError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {lscd_status_string(status)} ({status})")
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built: run `python unstructured_sparse_skinny_amd/build.py` "
+                          "(or __graft_entry__.build())")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I64, I32, VP = ctypes.POINTER, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p
+    sig = {
+        "lscd_pack_size": [VP, VP, I64, I64, I32, I32, P(I64), P(I64)],
+        "lscd_pack": [VP, VP, I64, I64, I32, I32, VP, I64, VP, I64],
+        "lscd_encode": [VP, VP, I64, I64, P(VP)],
+        "lscd_encode_tiled": [VP, VP, I64, I64, I32, I32, P(VP)],
+        "lscd_import": [VP, I64, VP, I64, I64, I32, I32, P(VP)],
+        "lscd_export": [VP, VP, VP],
+        "lscd_get_info": [VP, P(lscd_info_t)],
+        "lscd_spmm": [VP, VP, VP, I32, VP],
+        "lscd_debug_decode": [VP, VP, VP],
+        "lscd_destroy": [VP],
+    }
+    for name, args in sig.items():
+        f = getattr(lib, name)
+        f.argtypes = args
+        f.restype = ctypes.c_int
+    lib.lscd_status_string.argtypes = [ctypes.c_int]
+    lib.lscd_status_string.restype = ctypes.c_char_p
+    return lib
+
+
+_lib = _load()
+
+
+def lscd_status_string(status: int) -> str:
+    return _lib.lscd_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str):
+    if status != LSCD_SUCCESS:
+        raise LSCDError(status, where)
+
+
+class Handle:
+    """Owner of an lscd_handle_t; freed by lscd_destroy (or when collected)."""
+
+    def __init__(self, ptr: int):
+        self.ptr = ptr
+
+    def __del__(self):
+        self.close()
+
+    def close(self):
+        if getattr(self, "ptr", None):
+            _lib.lscd_destroy(ctypes.c_void_p(self.ptr))
+            self.ptr = None
+
+    @property
+    def info(self) -> dict:
+        return lscd_get_info(self)
+
+
+def _host_A(A16, mask):
+    A16 = np.ascontiguousarray(A16, dtype=np.uint16)
+    if A16.ndim != 2:
+        raise ValueError("A must be a 2-D array of fp16 bit patterns")
+    m = None if mask is None else np.ascontiguousarray(mask, dtype=np.uint8)
+    if m is not None and m.shape != A16.shape:
+        raise ValueError("mask must have A's shape")
+    return A16, m, A16.ctypes.data, (None if m is None else m.ctypes.data)
+
+
+def _stream(stream):
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _device_fp16(t, name, shape):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda or t.dtype != torch.float16 or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous float16 CUDA tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def lscd_pack_size(A16, mask=None, tile_m=LSCD_DEFAULT_TILE_M, tile_k=LSCD_DEFAULT_TILE_K):
+    A16, m, pa, pm = _host_A(A16, mask)
+    nw, nt = ctypes.c_int64(), ctypes.c_int64()
+    _check(_lib.lscd_pack_size(pa, pm, A16.shape[0], A16.shape[1], tile_m, tile_k, ctypes.byref(nw),
+                               ctypes.byref(nt)), "lscd_pack_size")
+    return nw.value, nt.value
+
+
+def lscd_pack(A16, mask=None, tile_m=LSCD_DEFAULT_TILE_M, tile_k=LSCD_DEFAULT_TILE_K):
+    """Host-only encoding: returns (nonzeros uint32[nnz_padded], tile_offsets uint32[T+1])."""
+    A16, m, pa, pm = _host_A(A16, mask)
+    nw, nt = lscd_pack_size(A16, m, tile_m, tile_k)
+    words = np.empty(max(nw, 1), dtype=np.uint32)
+    offs = np.empty(nt + 1, dtype=np.uint32)
+    _check(_lib.lscd_pack(pa, pm, A16.shape[0], A16.shape[1], tile_m, tile_k, words.ctypes.data, nw,
+                          offs.ctypes.data, nt + 1), "lscd_pack")
+    return words[:nw], offs
+
+
+def lscd_encode(A16, mask=None) -> Handle:
+    A16, m, pa, pm = _host_A(A16, mask)
+    h = ctypes.c_void_p()
+    _check(_lib.lscd_encode(pa, pm, A16.shape[0], A16.shape[1], ctypes.byref(h)), "lscd_encode")
+    return Handle(h.value)
+
+
+def lscd_encode_tiled(A16, mask, tile_m, tile_k) -> Handle:
+    A16, m, pa, pm = _host_A(A16, mask)
+    h = ctypes.c_void_p()
+    _check(_lib.lscd_encode_tiled(pa, pm, A16.shape[0], A16.shape[1], tile_m, tile_k, ctypes.byref(h)),
+           "lscd_encode_tiled")
+    return Handle(h.value)
+
+
+def lscd_import(nonzeros, tile_offsets, M, K, tile_m=LSCD_DEFAULT_TILE_M, tile_k=LSCD_DEFAULT_TILE_K) -> Handle:
+    w = np.ascontiguousarray(nonzeros, dtype=np.uint32)
+    o = np.ascontiguousarray(tile_offsets, dtype=np.uint32)
+    h = ctypes.c_void_p()
+    _check(_lib.lscd_import(w.ctypes.data if w.size else None, w.size, o.ctypes.data, M, K, tile_m, tile_k,
+                            ctypes.byref(h)), "lscd_import")
+    return Handle(h.value)
+
+
+def lscd_get_info(h: Handle) -> dict:
+    info = lscd_info_t()
+    _check(_lib.lscd_get_info(ctypes.c_void_p(h.ptr), ctypes.byref(info)), "lscd_get_info")
+    return {name: getattr(info, name) for name, _ in lscd_info_t._fields_}
+
+
+def lscd_export(h: Handle):
+    info = lscd_get_info(h)
+    words = np.empty(max(info["nnz_padded"], 1), dtype=np.uint32)
+    offs = np.empty(info["num_tiles"] + 1, dtype=np.uint32)
+    _check(_lib.lscd_export(ctypes.c_void_p(h.ptr), words.ctypes.data, offs.ctypes.data), "lscd_export")
+    return words[:info["nnz_padded"]], offs
+
+
+def lscd_spmm(h: Handle, B, C, stream=None):
+    """C[N][M] = A . B^T for B[N][K] (float16 CUDA tensors), enqueued on `stream`."""
+    info = lscd_get_info(h)
+    N = int(B.shape[0]) if isinstance(B, torch.Tensor) and B.dim() == 2 else -1
+    pb = _device_fp16(B, "B", (N, info["K"]))
+    pc = _device_fp16(C, "C", (N, info["M"]))
+    _check(_lib.lscd_spmm(ctypes.c_void_p(h.ptr), pb, pc, N, _stream(stream)), "lscd_spmm")
+    return C
+
+
+def lscd_debug_decode(h: Handle, A_dense, stream=None):
+    info = lscd_get_info(h)
+    pa = _device_fp16(A_dense, "A_dense", (info["M"], info["K"]))
+    _check(_lib.lscd_debug_decode(ctypes.c_void_p(h.ptr), pa, _stream(stream)), "lscd_debug_decode")
+    return A_dense
+
+
+def lscd_destroy(h: Handle):
+    h.close()

@@ -1,0 +1,314 @@
+// C-ABI layer: handles, argument checks, split-K planning and launches.
+// Entry points are declared and documented in include/lscd.h.
+
+#include <stdlib.h>
+#include <string.h>
+
+#include <algorithm>
+#include <new>
+#include <vector>
+
+#include "lscd_internal.h"
+
+struct lscd_handle_s {
+    lscd::Grid g;
+    int device = 0;
+    int cus = 256;
+    int64_t nnz = 0;
+    int64_t nnz_padded = 0;
+    int32_t max_tile_words = 0;
+    int R = 2;
+    int S = 1;  // K splits used by lscd_spmm
+    uint32_t* d_words = nullptr;
+    uint32_t* d_offs = nullptr;
+    float* d_part = nullptr;
+    int64_t part_bytes = 0;
+};
+
+namespace {
+
+using lscd::Grid;
+
+lscd_status_t hip_status(hipError_t e) {
+    if (e == hipSuccess) return LSCD_SUCCESS;
+    if (e == hipErrorOutOfMemory) return LSCD_ERROR_OUT_OF_MEMORY;
+    return LSCD_ERROR_HIP;
+}
+
+void free_handle(lscd_handle_s* h) {
+    if (!h) return;
+    if (h->d_words) (void)hipFree(h->d_words);
+    if (h->d_offs) (void)hipFree(h->d_offs);
+    if (h->d_part) (void)hipFree(h->d_part);
+    delete h;
+}
+
+// Number of K splits: enough workgroups to give every CU a few, never fewer than four
+// k tiles per split.  LSCD_SPLITK overrides (tuning only).
+int plan_splits(const Grid& g, int cus) {
+    const int64_t groups = (g.MB + lscd::kWaves - 1) / lscd::kWaves;
+    int64_t S = 1;
+    if (const char* e = getenv("LSCD_SPLITK")) {
+        S = atoll(e);
+    } else {
+        const int64_t target = (int64_t)cus * 2;
+        S = (target + groups - 1) / groups;
+        S = std::min<int64_t>(S, std::max<int64_t>(1, g.KT / 4));
+    }
+    S = std::max<int64_t>(1, std::min<int64_t>(S, g.KT));
+    return (int)S;
+}
+
+// Upload an encoding and size the workspace.  Takes ownership of nothing.
+lscd_status_t make_handle(const uint32_t* words, int64_t nwords, const uint32_t* offs, const Grid& g,
+                          int64_t nnz, int32_t maxw, lscd_handle_t* out) {
+    lscd_handle_s* h = new (std::nothrow) lscd_handle_s();
+    if (!h) return LSCD_ERROR_OUT_OF_MEMORY;
+    h->g = g;
+    h->nnz = nnz;
+    h->nnz_padded = nwords;
+    h->max_tile_words = maxw;
+    hipError_t e = hipGetDevice(&h->device);
+    if (e != hipSuccess) {
+        free_handle(h);
+        return LSCD_ERROR_HIP;
+    }
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, h->device) == hipSuccess && cus > 0)
+        h->cus = cus;
+    h->R = lscd::pick_reg_vectors(maxw);
+    const bool kernel_tile = g.tm == lscd::kTileM && g.tk == lscd::kTileK;
+    h->S = kernel_tile ? plan_splits(g, h->cus) : 1;
+    if (getenv("LSCD_TEST_FAIL_ALLOC")) {
+        free_handle(h);
+        return LSCD_ERROR_OUT_OF_MEMORY;
+    }
+    const size_t wbytes = (size_t)std::max<int64_t>(nwords, 4) * 4;
+    if ((e = hipMalloc((void**)&h->d_words, wbytes)) != hipSuccess ||
+        (e = hipMalloc((void**)&h->d_offs, (size_t)(g.T + 1) * 4)) != hipSuccess) {
+        free_handle(h);
+        return hip_status(e);
+    }
+    if (h->S > 1) {
+        h->part_bytes = (int64_t)h->S * g.M * LSCD_MAX_N * 4;
+        if ((e = hipMalloc((void**)&h->d_part, (size_t)h->part_bytes)) != hipSuccess) {
+            free_handle(h);
+            return hip_status(e);
+        }
+    }
+    if (nwords > 0 && (e = hipMemcpy(h->d_words, words, (size_t)nwords * 4, hipMemcpyHostToDevice)) != hipSuccess) {
+        free_handle(h);
+        return hip_status(e);
+    }
+    if ((e = hipMemcpy(h->d_offs, offs, (size_t)(g.T + 1) * 4, hipMemcpyHostToDevice)) != hipSuccess) {
+        free_handle(h);
+        return hip_status(e);
+    }
+    *out = h;
+    return LSCD_SUCCESS;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+lscd_status_t check_device(const lscd_handle_s* h) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return LSCD_ERROR_HIP;
+    return dev == h->device ? LSCD_SUCCESS : LSCD_ERROR_INVALID_VALUE;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* lscd_status_string(lscd_status_t s) {
+    switch (s) {
+        case LSCD_SUCCESS: return "success";
+        case LSCD_ERROR_INVALID_VALUE: return "invalid value";
+        case LSCD_ERROR_NOT_SUPPORTED: return "not supported";
+        case LSCD_ERROR_OUT_OF_MEMORY: return "out of memory";
+        case LSCD_ERROR_INVALID_FORMAT: return "invalid format";
+        case LSCD_ERROR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+lscd_status_t lscd_pack_size(const uint16_t* A, const uint8_t* mask, int64_t M, int64_t K, int32_t tile_m,
+                             int32_t tile_k, int64_t* nnz_padded, int64_t* num_tiles) {
+    try {
+        Grid g;
+        if (!A || !nnz_padded || !num_tiles || !lscd::make_grid(M, K, tile_m, tile_k, &g))
+            return LSCD_ERROR_INVALID_VALUE;
+        std::vector<uint32_t> offs;
+        int64_t nnz = 0;
+        lscd_status_t st = lscd::pack_offsets(A, mask, g, &offs, &nnz);
+        if (st != LSCD_SUCCESS) return st;
+        *nnz_padded = offs[(size_t)g.T];
+        *num_tiles = g.T;
+        return LSCD_SUCCESS;
+    } catch (const std::bad_alloc&) {
+        return LSCD_ERROR_OUT_OF_MEMORY;
+    } catch (...) {
+        return LSCD_ERROR_INVALID_VALUE;
+    }
+}
+
+lscd_status_t lscd_pack(const uint16_t* A, const uint8_t* mask, int64_t M, int64_t K, int32_t tile_m,
+                        int32_t tile_k, uint32_t* nonzeros, int64_t nonzeros_len, uint32_t* tile_offsets,
+                        int64_t tile_offsets_len) {
+    try {
+        Grid g;
+        if (!A || !tile_offsets || !lscd::make_grid(M, K, tile_m, tile_k, &g)) return LSCD_ERROR_INVALID_VALUE;
+        std::vector<uint32_t> offs;
+        int64_t nnz = 0;
+        lscd_status_t st = lscd::pack_offsets(A, mask, g, &offs, &nnz);
+        if (st != LSCD_SUCCESS) return st;
+        const int64_t nw = offs[(size_t)g.T];
+        if (tile_offsets_len < g.T + 1 || nonzeros_len < nw || (nw > 0 && !nonzeros)) return LSCD_ERROR_INVALID_VALUE;
+        lscd::pack_fill(A, mask, g, offs.data(), nonzeros);
+        memcpy(tile_offsets, offs.data(), (size_t)(g.T + 1) * 4);
+        return LSCD_SUCCESS;
+    } catch (const std::bad_alloc&) {
+        return LSCD_ERROR_OUT_OF_MEMORY;
+    } catch (...) {
+        return LSCD_ERROR_INVALID_VALUE;
+    }
+}
+
+lscd_status_t lscd_encode_tiled(const uint16_t* A, const uint8_t* mask, int64_t M, int64_t K, int32_t tile_m,
+                                int32_t tile_k, lscd_handle_t* out) {
+    try {
+        Grid g;
+        if (!A || !out || !lscd::make_grid(M, K, tile_m, tile_k, &g)) return LSCD_ERROR_INVALID_VALUE;
+        *out = nullptr;
+        std::vector<uint32_t> offs;
+        int64_t nnz = 0;
+        lscd_status_t st = lscd::pack_offsets(A, mask, g, &offs, &nnz);
+        if (st != LSCD_SUCCESS) return st;
+        const int64_t nw = offs[(size_t)g.T];
+        std::vector<uint32_t> words((size_t)std::max<int64_t>(nw, 1));
+        lscd::pack_fill(A, mask, g, offs.data(), words.data());
+        int32_t maxw = 0;
+        for (int64_t t = 0; t < g.T; ++t) maxw = std::max<int32_t>(maxw, (int32_t)(offs[t + 1] - offs[t]));
+        return make_handle(words.data(), nw, offs.data(), g, nnz, maxw, out);
+    } catch (const std::bad_alloc&) {
+        return LSCD_ERROR_OUT_OF_MEMORY;
+    } catch (...) {
+        return LSCD_ERROR_INVALID_VALUE;
+    }
+}
+
+lscd_status_t lscd_encode(const uint16_t* A, const uint8_t* mask, int64_t M, int64_t K, lscd_handle_t* out) {
+    return lscd_encode_tiled(A, mask, M, K, LSCD_DEFAULT_TILE_M, LSCD_DEFAULT_TILE_K, out);
+}
+
+lscd_status_t lscd_import(const uint32_t* nonzeros, int64_t nnz_padded, const uint32_t* tile_offsets, int64_t M,
+                          int64_t K, int32_t tile_m, int32_t tile_k, lscd_handle_t* out) {
+    try {
+        Grid g;
+        if (!tile_offsets || !out || nnz_padded < 0 || (nnz_padded > 0 && !nonzeros) ||
+            !lscd::make_grid(M, K, tile_m, tile_k, &g))
+            return LSCD_ERROR_INVALID_VALUE;
+        *out = nullptr;
+        if (nnz_padded >= ((int64_t)1 << 32)) return LSCD_ERROR_NOT_SUPPORTED;
+        int64_t nnz = 0;
+        int32_t maxw = 0;
+        lscd_status_t st = lscd::validate_format(nonzeros, nnz_padded, tile_offsets, g, &nnz, &maxw);
+        if (st != LSCD_SUCCESS) return st;
+        return make_handle(nonzeros, nnz_padded, tile_offsets, g, nnz, maxw, out);
+    } catch (const std::bad_alloc&) {
+        return LSCD_ERROR_OUT_OF_MEMORY;
+    } catch (...) {
+        return LSCD_ERROR_INVALID_VALUE;
+    }
+}
+
+lscd_status_t lscd_export(lscd_handle_t h, uint32_t* nonzeros, uint32_t* tile_offsets) {
+    if (!h || !tile_offsets || (h->nnz_padded > 0 && !nonzeros)) return LSCD_ERROR_INVALID_VALUE;
+    lscd_status_t st = check_device(h);
+    if (st != LSCD_SUCCESS) return st;
+    hipError_t e;
+    if (h->nnz_padded > 0 &&
+        (e = hipMemcpy(nonzeros, h->d_words, (size_t)h->nnz_padded * 4, hipMemcpyDeviceToHost)) != hipSuccess)
+        return hip_status(e);
+    if ((e = hipMemcpy(tile_offsets, h->d_offs, (size_t)(h->g.T + 1) * 4, hipMemcpyDeviceToHost)) != hipSuccess)
+        return hip_status(e);
+    return LSCD_SUCCESS;
+}
+
+lscd_status_t lscd_get_info(lscd_handle_t h, lscd_info_t* info) {
+    if (!h || !info) return LSCD_ERROR_INVALID_VALUE;
+    memset(info, 0, sizeof(*info));
+    info->M = h->g.M;
+    info->K = h->g.K;
+    info->tile_m = h->g.tm;
+    info->tile_k = h->g.tk;
+    info->num_tiles = h->g.T;
+    info->nnz = h->nnz;
+    info->nnz_padded = h->nnz_padded;
+    info->format_bytes = 4 * h->nnz_padded + 4 * (h->g.T + 1);
+    info->max_tile_words = h->max_tile_words;
+    info->device = h->device;
+    info->workspace_bytes = h->part_bytes;
+    info->splits = h->S;
+    info->reg_vectors = h->R;
+    return LSCD_SUCCESS;
+}
+
+lscd_status_t lscd_spmm(lscd_handle_t h, const void* B, void* C, int32_t N, void* stream) {
+    if (!h || N < 0) return LSCD_ERROR_INVALID_VALUE;
+    if (N == 0) return LSCD_SUCCESS;
+    if (!B || !C || !aligned16(B) || !aligned16(C)) return LSCD_ERROR_INVALID_VALUE;
+    if (N > LSCD_MAX_N) return LSCD_ERROR_NOT_SUPPORTED;
+    if (h->g.tm != lscd::kTileM || h->g.tk != lscd::kTileK) return LSCD_ERROR_NOT_SUPPORTED;
+    lscd_status_t st = check_device(h);
+    if (st != LSCD_SUCCESS) return st;
+    hipStream_t s = (hipStream_t)stream;
+    lscd::SpmmArgs a;
+    a.words = h->d_words;
+    a.offs = h->d_offs;
+    a.B = (const uint16_t*)B;
+    a.C = (uint16_t*)C;
+    a.part = h->d_part;
+    a.M = (int32_t)h->g.M;
+    a.K = (int32_t)h->g.K;
+    a.N = N;
+    a.MB = (int32_t)h->g.MB;
+    a.KT = (int32_t)h->g.KT;
+    a.G = (int32_t)((h->g.MB + lscd::kWaves - 1) / lscd::kWaves);
+    a.S = h->S;
+    a.items = a.G * a.S;
+    a.per_xcd = (a.items + 7) / 8;
+    const int npad = N <= 16 ? 16 : (N <= 32 ? 32 : 64);
+    hipError_t e = lscd::launch_spmm(npad, h->R, a, 8 * a.per_xcd, s);
+    if (e != hipSuccess) return hip_status(e);
+    if (h->S > 1) {
+        e = lscd::launch_reduce(h->d_part, (uint16_t*)C, h->S, (int64_t)N * h->g.M, s);
+        if (e != hipSuccess) return hip_status(e);
+    }
+    return LSCD_SUCCESS;
+}
+
+lscd_status_t lscd_debug_decode(lscd_handle_t h, void* A_dense, void* stream) {
+    if (!h || !A_dense || !aligned16(A_dense)) return LSCD_ERROR_INVALID_VALUE;
+    if (h->g.tm != lscd::kTileM || h->g.tk != lscd::kTileK) return LSCD_ERROR_NOT_SUPPORTED;
+    lscd_status_t st = check_device(h);
+    if (st != LSCD_SUCCESS) return st;
+    lscd::DecodeArgs a;
+    a.words = h->d_words;
+    a.offs = h->d_offs;
+    a.A = (uint16_t*)A_dense;
+    a.M = (int32_t)h->g.M;
+    a.K = (int32_t)h->g.K;
+    a.MB = (int32_t)h->g.MB;
+    a.KT = (int32_t)h->g.KT;
+    a.T = h->g.T;
+    const int64_t grid = (h->g.T + lscd::kWaves - 1) / lscd::kWaves;
+    return hip_status(lscd::launch_decode(h->R, a, (int)grid, (hipStream_t)stream));
+}
+
+lscd_status_t lscd_destroy(lscd_handle_t h) {
+    free_handle(h);
+    return LSCD_SUCCESS;
+}
+
+}  // extern "C"

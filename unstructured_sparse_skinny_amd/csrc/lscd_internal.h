@@ -1,0 +1,78 @@
+// Internal declarations shared by the host encoder, the C-ABI layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include <vector>
+
+#include "lscd.h"
+
+namespace lscd {
+
+// Tile shape the gfx950 product kernel is built for: one 64 x 64 tile per wavefront,
+// i.e. 4 row blocks of 16 for the 16x16x32 MFMA and two 32-deep k steps.
+constexpr int kTileM = 64;
+constexpr int kTileK = 64;
+// Wavefronts per workgroup; each owns one row block, all share the staged B tile.
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * 64;
+
+// ---------------------------------------------------------------- host encoder
+struct Grid {
+    int64_t M, K;
+    int32_t tm, tk;
+    int64_t MB, KT, T;
+};
+bool make_grid(int64_t M, int64_t K, int32_t tm, int32_t tk, Grid* g);
+
+struct Packed {
+    std::vector<uint32_t> words;
+    std::vector<uint32_t> offsets;
+    int64_t nnz = 0;
+    int32_t max_tile_words = 0;
+};
+
+// Count pass only: padded words per tile -> offsets (no words).  Returns NOT_SUPPORTED
+// when the total reaches 2^32 words.
+lscd_status_t pack_offsets(const uint16_t* A, const uint8_t* mask, const Grid& g,
+                           std::vector<uint32_t>* offsets, int64_t* nnz);
+// Fill pass into caller storage, offsets from pack_offsets.
+void pack_fill(const uint16_t* A, const uint8_t* mask, const Grid& g, const uint32_t* offsets,
+               uint32_t* words);
+// Validate an imported encoding; fills nnz and the largest tile.
+lscd_status_t validate_format(const uint32_t* words, int64_t nwords, const uint32_t* offsets,
+                              const Grid& g, int64_t* nnz, int32_t* max_tile_words);
+// Whether the encoder orders the words of a tile for LDS banks (env LSCD_NO_REORDER=1 turns
+// it off, for measurements).
+bool reorder_enabled();
+
+// ---------------------------------------------------------------- device side
+struct SpmmArgs {
+    const uint32_t* words;     // nonzeros, tile after tile
+    const uint32_t* offs;      // tile offsets, T + 1
+    const uint16_t* B;         // [N][K] fp16
+    uint16_t* C;               // [N][M] fp16 (used when S == 1)
+    float* part;               // [S][N][M] fp32 partial sums (used when S > 1)
+    int32_t M, K, N;
+    int32_t MB, KT;            // row blocks, k tiles
+    int32_t G, S;              // row groups (kWaves row blocks each), K splits
+    int32_t items, per_xcd;    // G * S work items, items per XCD slot range
+};
+
+struct DecodeArgs {
+    const uint32_t* words;
+    const uint32_t* offs;
+    uint16_t* A;               // [M][K] fp16 out
+    int32_t M, K, MB, KT;
+    int64_t T;
+};
+
+// Staging registers per lane and tile that have kernel instantiations.
+int pick_reg_vectors(int32_t max_tile_words);
+hipError_t launch_spmm(int npad, int R, const SpmmArgs& a, int grid, hipStream_t s);
+hipError_t launch_reduce(const float* part, uint16_t* C, int S, int64_t NM, hipStream_t s);
+hipError_t launch_decode(int R, const DecodeArgs& a, int grid, hipStream_t s);
+
+}  // namespace lscd

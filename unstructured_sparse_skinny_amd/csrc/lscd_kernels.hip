@@ -1,0 +1,431 @@
+// gfx950 kernels of the Load-as-Sparse, Compute-as-Dense skinny product.
+//
+// Method (Flash-LLM paper review, xllm-io, sections 2-4): the sparse weights are
+// streamed from HBM in their packed form, unpacked on chip into a zero-filled dense
+// tile ("sparse-to-dense transform"), and multiplied densely on the matrix cores with
+// fp32 accumulation; loads of later tiles overlap the unpacking and the multiply of the
+// current one.  The pages' design targets A100 Tensor Cores (mma.sync m16n8k16,
+// ldmatrix, cp.async); what is kept here is the method, re-laid for CDNA4:
+//
+//  * one wavefront owns one 64 x 64 format tile per k step: it streams the tile's words
+//    with 128-bit buffer loads straight into VGPRs (no LDS staging for the sparse
+//    stream), zero-fills its own 8 KB LDS tile, scatters each word with a 16-bit LDS
+//    store, and feeds v_mfma_f32_16x16x32_f16 from LDS;
+//  * the loads of the next tiles are in flight while the current one is unpacked and
+//    multiplied (register stages), and the workgroup's four wavefronts share one B tile
+//    staged in LDS, double-buffered, with a single barrier per k step;
+//  * tall-skinny shapes are split along K across workgroups; fp32 partial sums go to a
+//    workspace and a second kernel adds them in ascending split order (deterministic);
+//  * workgroup ids are remapped so that consecutive work items (the same K split,
+//    hence the same slice of B) land on the same XCD and share its L2.
+//
+// LDS tile layout (A and B alike): 128-byte rows of 64 fp16, 16-byte chunks XOR-swizzled
+// by (row & 7), so the 16 rows read by one MFMA operand load spread over the banks.
+
+#include <hip/hip_runtime.h>
+
+#include "lscd_internal.h"
+
+namespace lscd {
+namespace {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kRowBytes = kTileK * 2;           // 128
+constexpr int kTileBytes = kTileM * kRowBytes;  // 8192
+constexpr int kBufWord3 = 0x00020000;           // raw buffer descriptor, word 3 (gfx9)
+
+__device__ __forceinline__ uint32_t lds_chunk(uint32_t r, uint32_t chunk) {
+    return r * kRowBytes + (((chunk ^ r) & 7u) << 4);
+}
+
+__device__ __forceinline__ uint16_t f16_bits(float x) {
+    _Float16 h = (_Float16)x;  // v_cvt_f16_f32, round to nearest even
+    return __builtin_bit_cast(uint16_t, h);
+}
+
+// Extract one packed word into the wavefront's LDS tile: value bits [15:0] go to the
+// row-major in-tile index in bits [31:16].  The index is masked to the 4096-entry tile,
+// so no word can reach outside the wavefront's own 8 KB.
+__device__ __forceinline__ void put_word(unsigned char* As, uint32_t w) {
+    uint32_t b = (w >> 15) & 0x1FFEu;  // byte offset r*128 + c*2
+    b ^= (b >> 3) & 0x70u;             // chunk ^= row & 7
+    *reinterpret_cast<uint16_t*>(As + b) = (uint16_t)w;
+}
+
+// Issue the loads of one tile's words: lane l of slot j gets vector 64*j + l.  The buffer
+// descriptor covers exactly the tile, so lanes past its end read zero without touching
+// memory (and a tile of 0 vectors costs no traffic).
+template <int R>
+__device__ __forceinline__ void load_tile(u32x4 (&wb)[R], const uint32_t* words, uint32_t first,
+                                          int nvec, int lane) {
+    __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(words + first), (short)0, nvec * 16, kBufWord3);
+#pragma unroll
+    for (int j = 0; j < R; ++j) wb[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, (j * 64 + lane) * 16, 0, 0);
+}
+
+__device__ __forceinline__ void zero_tile(unsigned char* As, int lane) {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int j = 0; j < kTileBytes / 1024; ++j) *reinterpret_cast<u32x4*>(As + (j * 64 + lane) * 16) = z;
+}
+
+template <int R>
+__device__ __forceinline__ void scatter_tile(const u32x4 (&wb)[R], int nvec, unsigned char* As,
+                                             const uint32_t* tile_words, int lane) {
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+        if (j * 64 + lane < nvec) {
+            put_word(As, wb[j][0]);
+            put_word(As, wb[j][1]);
+            put_word(As, wb[j][2]);
+            put_word(As, wb[j][3]);
+        }
+    }
+    // Tiles larger than the register stage: the rest is fetched and placed directly.
+    if (nvec > R * 64) {
+        for (int v = R * 64 + lane; v < nvec; v += 64) {
+            const u32x4 x = *reinterpret_cast<const u32x4*>(tile_words + 4 * (size_t)v);
+            put_word(As, x[0]);
+            put_word(As, x[1]);
+            put_word(As, x[2]);
+            put_word(As, x[3]);
+        }
+    }
+}
+
+// B tile (64 k x NPAD n) staging: 16-byte chunks, 8 per row of 64 k.
+template <int NPAD>
+struct BStage {
+    static constexpr int kChunks = NPAD * 8;
+    static constexpr int kPer = (kChunks + kThreads - 1) / kThreads;
+    u32x4 r[kPer];
+
+    __device__ __forceinline__ void load(const uint16_t* B, int N, int K, int kt, int tid, bool vec_ok) {
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) {
+            const int ch = tid + u * kThreads;
+            const int n = ch >> 3, c = ch & 7;
+            u32x4 v = {0u, 0u, 0u, 0u};
+            if (ch < kChunks && n < N) {
+                const int k0 = kt * kTileK + c * 8;
+                const uint16_t* p = B + (size_t)n * K + k0;
+                if (vec_ok && k0 + 8 <= K) {
+                    v = *reinterpret_cast<const u32x4*>(p);
+                } else {
+                    uint32_t h[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) h[e] = (k0 + e < K) ? p[e] : 0u;
+                    v[0] = h[0] | (h[1] << 16);
+                    v[1] = h[2] | (h[3] << 16);
+                    v[2] = h[4] | (h[5] << 16);
+                    v[3] = h[6] | (h[7] << 16);
+                }
+            }
+            r[u] = v;
+        }
+    }
+    __device__ __forceinline__ void store(unsigned char* Bs, int N, int tid) const {
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) {
+            const int ch = tid + u * kThreads;
+            const int n = ch >> 3, c = ch & 7;
+            if (ch < kChunks && n < N) *reinterpret_cast<u32x4*>(Bs + lds_chunk(n, c)) = r[u];
+        }
+    }
+};
+
+// acc[i][j] += A rows 16i..16i+15 (x 64 k) times B columns 16j..16j+15.
+template <int NPAD>
+__device__ __forceinline__ void mma_tile(f32x4 (&acc)[4][NPAD / 16], const unsigned char* As,
+                                         const unsigned char* Bs, int lane) {
+    const uint32_t rl = lane & 15, kq = lane >> 4;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+        half8 bf[NPAD / 16];
+#pragma unroll
+        for (int j = 0; j < NPAD / 16; ++j)
+            bf[j] = *reinterpret_cast<const half8*>(Bs + lds_chunk(j * 16 + rl, ks * 4 + kq));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const half8 af = *reinterpret_cast<const half8*>(As + lds_chunk(i * 16 + rl, ks * 4 + kq));
+#pragma unroll
+            for (int j = 0; j < NPAD / 16; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf[j], acc[i][j], 0, 0, 0);
+        }
+    }
+}
+
+template <int NPAD, int R, int P>
+__global__ __launch_bounds__(kThreads) void spmm_kernel(SpmmArgs a) {
+    __shared__ __attribute__((aligned(16))) unsigned char smem[kWaves * kTileBytes + 2 * NPAD * kRowBytes];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    unsigned char* As = smem + wave * kTileBytes;
+    unsigned char* Bs0 = smem + kWaves * kTileBytes;
+
+    // XCD-aware work mapping: hardware places workgroup b on XCD b % 8; give each XCD a
+    // contiguous run of work items (items are split-major, so a run shares a B slice).
+    const int bid = blockIdx.x;
+    const int item = (bid & 7) * a.per_xcd + (bid >> 3);
+    if (item >= a.items) return;  // whole workgroup
+    const int s = item / a.G;
+    const int g = item - s * a.G;
+    const int kt0 = (int)(((int64_t)s * a.KT) / a.S);
+    const int kt1 = (int)(((int64_t)(s + 1) * a.KT) / a.S);
+    const int rb = g * kWaves + wave;
+    const bool active = rb < a.MB;
+    const uint32_t* toff = a.offs + (int64_t)(active ? rb : 0) * a.KT;
+    const bool vec_ok = (a.K & 7) == 0;
+
+    // B rows n >= N stay zero for the whole kernel (both buffers).
+    for (int ch = tid; ch < 2 * NPAD * 8; ch += kThreads) {
+        const int row = ch >> 3;
+        if (row % NPAD >= a.N) {
+            const u32x4 z = {0u, 0u, 0u, 0u};
+            *reinterpret_cast<u32x4*>(Bs0 + row * kRowBytes + (ch & 7) * 16) = z;
+        }
+    }
+
+    u32x4 wb[P][R];
+    int nv[P];
+    uint32_t first[P];
+#pragma unroll
+    for (int q = 0; q < P; ++q) {
+        const int k = kt0 + q;
+        uint32_t o0 = 0, o1 = 0;
+        if (active && k < kt1) {
+            o0 = toff[k];
+            o1 = toff[k + 1];
+        }
+        first[q] = o0;
+        nv[q] = (int)((o1 - o0) >> 2);
+        load_tile<R>(wb[q], a.words, o0, nv[q], lane);
+    }
+    BStage<NPAD> bst;
+    bst.load(a.B, a.N, a.K, kt0, tid, vec_ok);
+
+    f32x4 acc[4][NPAD / 16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < NPAD / 16; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    for (int kt = kt0; kt < kt1; kt += P) {
+#pragma unroll
+        for (int q = 0; q < P; ++q) {
+            const int k = kt + q;
+            if (k < kt1) {  // uniform over the workgroup
+                unsigned char* Bs = Bs0 + (k & 1) * NPAD * kRowBytes;
+                bst.store(Bs, a.N, tid);
+                if (k + 1 < kt1) bst.load(a.B, a.N, a.K, k + 1, tid, vec_ok);
+                const int n = nv[q];
+                if (n > 0) {
+                    zero_tile(As, lane);
+                    scatter_tile<R>(wb[q], n, As, a.words + first[q], lane);
+                }
+                // refill this register stage with tile k + P
+                const int kn = k + P;
+                uint32_t o0 = 0, o1 = 0;
+                if (active && kn < kt1) {
+                    o0 = toff[kn];
+                    o1 = toff[kn + 1];
+                }
+                first[q] = o0;
+                nv[q] = (int)((o1 - o0) >> 2);
+                load_tile<R>(wb[q], a.words, o0, nv[q], lane);
+                __syncthreads();
+                if (n > 0) mma_tile<NPAD>(acc, As, Bs, lane);
+            }
+        }
+    }
+    if (!active) return;
+
+    // MFMA 16x16 result layout: lane holds column (lane & 15), rows 4*(lane >> 4) + 0..3.
+    const int ncol = lane & 15;
+    const int mrow = rb * kTileM + (lane >> 4) * 4;
+    const bool vec_m = (a.M & 3) == 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int j = 0; j < NPAD / 16; ++j) {
+            const int n = j * 16 + ncol;
+            const int m = mrow + i * 16;
+            if (n >= a.N || m >= a.M) continue;
+            const f32x4 v = acc[i][j];
+            if (a.S == 1) {
+                uint16_t* dst = a.C + (int64_t)n * a.M + m;
+                if (vec_m && m + 3 < a.M) {
+                    uint2 pk;
+                    pk.x = (uint32_t)f16_bits(v[0]) | ((uint32_t)f16_bits(v[1]) << 16);
+                    pk.y = (uint32_t)f16_bits(v[2]) | ((uint32_t)f16_bits(v[3]) << 16);
+                    *reinterpret_cast<uint2*>(dst) = pk;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (m + e < a.M) dst[e] = f16_bits(v[e]);
+                }
+            } else {
+                float* dst = a.part + ((int64_t)s * a.N + n) * a.M + m;
+                if (vec_m && m + 3 < a.M) {
+                    *reinterpret_cast<f32x4*>(dst) = v;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (m + e < a.M) dst[e] = v[e];
+                }
+            }
+        }
+    }
+}
+
+// Second pass of split-K: C = fp16( ((P0 + P1) + P2) + ... ), fixed ascending order.
+__global__ __launch_bounds__(256) void reduce_kernel(const float* __restrict__ part, uint16_t* __restrict__ C,
+                                                     int S, int64_t NM) {
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    if ((NM & 3) == 0) {
+        const int64_t n4 = NM >> 2;
+        for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += stride) {
+            f32x4 acc = reinterpret_cast<const f32x4*>(part)[i];
+            for (int s = 1; s < S; ++s) acc += reinterpret_cast<const f32x4*>(part + (int64_t)s * NM)[i];
+            uint2 pk;
+            pk.x = (uint32_t)f16_bits(acc[0]) | ((uint32_t)f16_bits(acc[1]) << 16);
+            pk.y = (uint32_t)f16_bits(acc[2]) | ((uint32_t)f16_bits(acc[3]) << 16);
+            reinterpret_cast<uint2*>(C)[i] = pk;
+        }
+    } else {
+        for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < NM; i += stride) {
+            float acc = part[i];
+            for (int s = 1; s < S; ++s) acc += part[(int64_t)s * NM + i];
+            C[i] = f16_bits(acc);
+        }
+    }
+}
+
+// Dense view of the encoding through the product's own load and extract path: one
+// wavefront per tile, then the LDS tile is copied out un-swizzled.
+template <int R>
+__global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
+    __shared__ __attribute__((aligned(16))) unsigned char smem[kWaves * kTileBytes];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    unsigned char* As = smem + wave * kTileBytes;
+    const int64_t t = (int64_t)blockIdx.x * kWaves + wave;
+    const bool act = t < a.T;
+    uint32_t o0 = 0, o1 = 0;
+    if (act) {
+        o0 = a.offs[t];
+        o1 = a.offs[t + 1];
+    }
+    const int nvec = (int)((o1 - o0) >> 2);
+    u32x4 wb[R];
+    load_tile<R>(wb, a.words, o0, nvec, lane);
+    zero_tile(As, lane);
+    scatter_tile<R>(wb, nvec, As, a.words + o0, lane);
+    __syncthreads();
+    if (!act) return;
+    const int bm = (int)(t / a.KT), bk = (int)(t % a.KT);
+    const bool vec_ok = (a.K & 7) == 0;
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+        const int ch = p * 64 + lane;
+        const int r = ch >> 3, c = ch & 7;
+        const int gi = bm * kTileM + r, gj = bk * kTileK + c * 8;
+        if (gi >= a.M || gj >= a.K) continue;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(As + lds_chunk(r, c));
+        uint16_t* dst = a.A + (int64_t)gi * a.K + gj;
+        if (vec_ok && gj + 8 <= a.K) {
+            *reinterpret_cast<u32x4*>(dst) = v;
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if (gj + e < a.K) dst[e] = (uint16_t)(v[e >> 1] >> ((e & 1) * 16));
+        }
+    }
+}
+
+template <int NPAD, int R>
+hipError_t launch_spmm_r(const SpmmArgs& a, int grid, hipStream_t st) {
+    constexpr int P = R <= 4 ? 3 : 2;
+    hipLaunchKernelGGL((spmm_kernel<NPAD, R, P>), dim3(grid), dim3(kThreads), 0, st, a);
+    return hipGetLastError();
+}
+
+template <int NPAD>
+hipError_t launch_spmm_n(int R, const SpmmArgs& a, int grid, hipStream_t st) {
+    switch (R) {
+        case 2: return launch_spmm_r<NPAD, 2>(a, grid, st);
+        case 3: return launch_spmm_r<NPAD, 3>(a, grid, st);
+        case 4: return launch_spmm_r<NPAD, 4>(a, grid, st);
+        case 5: return launch_spmm_r<NPAD, 5>(a, grid, st);
+        case 6: return launch_spmm_r<NPAD, 6>(a, grid, st);
+        case 8: return launch_spmm_r<NPAD, 8>(a, grid, st);
+        case 10: return launch_spmm_r<NPAD, 10>(a, grid, st);
+        case 12: return launch_spmm_r<NPAD, 12>(a, grid, st);
+        case 16: return launch_spmm_r<NPAD, 16>(a, grid, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <int R>
+hipError_t launch_decode_r(const DecodeArgs& a, int grid, hipStream_t st) {
+    hipLaunchKernelGGL((decode_kernel<R>), dim3(grid), dim3(kThreads), 0, st, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+static const int kRegChoices[] = {2, 3, 4, 5, 6, 8, 10, 12, 16};
+
+int pick_reg_vectors(int32_t max_tile_words) {
+    const int need = ((max_tile_words / 4) + 63) / 64;
+    int cap = 16;
+    if (const char* e = getenv("LSCD_MAX_R")) cap = atoi(e) > 0 ? atoi(e) : 16;
+    int best = 2;
+    for (int r : kRegChoices) {
+        if (r > cap) break;
+        best = r;
+        if (r >= need) break;
+    }
+    return best;
+}
+
+hipError_t launch_spmm(int npad, int R, const SpmmArgs& a, int grid, hipStream_t st) {
+    switch (npad) {
+        case 16: return launch_spmm_n<16>(R, a, grid, st);
+        case 32: return launch_spmm_n<32>(R, a, grid, st);
+        case 64: return launch_spmm_n<64>(R, a, grid, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_reduce(const float* part, uint16_t* C, int S, int64_t NM, hipStream_t st) {
+    const int64_t work = (NM & 3) == 0 ? NM / 4 : NM;
+    int64_t blocks = (work + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    if (blocks < 1) blocks = 1;
+    hipLaunchKernelGGL(reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, st, part, C, S, NM);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode(int R, const DecodeArgs& a, int grid, hipStream_t st) {
+    switch (R) {
+        case 2: return launch_decode_r<2>(a, grid, st);
+        case 3: return launch_decode_r<3>(a, grid, st);
+        case 4: return launch_decode_r<4>(a, grid, st);
+        case 5: return launch_decode_r<5>(a, grid, st);
+        case 6: return launch_decode_r<6>(a, grid, st);
+        case 8: return launch_decode_r<8>(a, grid, st);
+        case 10: return launch_decode_r<10>(a, grid, st);
+        case 12: return launch_decode_r<12>(a, grid, st);
+        case 16: return launch_decode_r<16>(a, grid, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace lscd

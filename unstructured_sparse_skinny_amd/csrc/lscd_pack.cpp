@@ -1,0 +1,241 @@
+// Host-side Tiled-CSL encoder and import validator.
+//
+// Format (Flash-LLM paper review, xllm-io, section 3 "Tiled-CSL sparse encoding format"):
+// the weight matrix is cut into tiles; each kept entry becomes a 32-bit word of
+// fp16 value (bits 15:0) and in-tile row-major index (bits 31:16); words are stored tile
+// after tile and a per-tile offset array locates each tile.  Tiles are padded to whole
+// 128-bit vectors with copies of one of their own words.
+//
+// Ahead-of-time reorder (same section, "ahead-of-time data reordering"): the order of
+// words inside a tile is free, and the pages reorder them offline so that the lanes of
+// one store instruction hit different shared-memory banks.  Here the order is built for
+// the gfx950 kernel's wave64 scatter: lane l of load slot j holds vector 64*j + l, and
+// store instruction (j, e) writes word e of every lane's vector.  Words are dealt
+// round-robin over the 64 LDS banks of the kernel's swizzled tile layout, so the lanes of
+// one instruction see as many distinct banks as the tile's contents allow.
+
+#include <stdlib.h>
+#include <string.h>
+
+#include <algorithm>
+#include <atomic>
+#include <thread>
+#include <vector>
+
+#include "lscd_internal.h"
+
+namespace lscd {
+
+bool make_grid(int64_t M, int64_t K, int32_t tm, int32_t tk, Grid* g) {
+    if (M < 1 || K < 1 || tm < 1 || tk < 1 || (int64_t)tm * tk > 65536) return false;
+    if (M > (int64_t)1 << 31 || K > (int64_t)1 << 31) return false;
+    g->M = M;
+    g->K = K;
+    g->tm = tm;
+    g->tk = tk;
+    g->MB = (M + tm - 1) / tm;
+    g->KT = (K + tk - 1) / tk;
+    g->T = g->MB * g->KT;
+    return true;
+}
+
+bool reorder_enabled() {
+    const char* e = getenv("LSCD_NO_REORDER");
+    return !(e && e[0] == '1');
+}
+
+namespace {
+
+inline bool kept(const uint16_t* A, const uint8_t* mask, size_t i) {
+    return mask ? mask[i] != 0 : (A[i] & 0x7FFF) != 0;
+}
+
+// Run body(lo, hi) over [0, n) on a few host threads.
+template <class F>
+void parallel_for(int64_t n, F body) {
+    unsigned hw = std::thread::hardware_concurrency();
+    int64_t nt = std::max<int64_t>(1, std::min<int64_t>(hw ? hw : 4, 32));
+    nt = std::min(nt, n);
+    if (nt <= 1) {
+        body(0, n);
+        return;
+    }
+    std::vector<std::thread> pool;
+    std::atomic<int64_t> next(0);
+    const int64_t chunk = std::max<int64_t>(1, n / (nt * 8));
+    for (int64_t t = 0; t < nt; ++t) {
+        pool.emplace_back([&]() {
+            for (;;) {
+                int64_t lo = next.fetch_add(chunk);
+                if (lo >= n) break;
+                body(lo, std::min(n, lo + chunk));
+            }
+        });
+    }
+    for (auto& th : pool) th.join();
+}
+
+// LDS bank (of 64 four-byte banks) that the kernel's store of in-tile index `idx` hits
+// in its 64 x 64 tile: 128-byte rows, 16-byte chunks XOR-swizzled by (row & 7).
+inline int lds_bank(uint32_t idx) {
+    uint32_t b = idx * 2u;
+    b ^= (b >> 3) & 0x70u;
+    return (int)((b >> 2) & 63u);
+}
+
+// Place n real words (+ padding) of one tile into out[0 .. 4*nvec), bank-aware.
+void place_tile(const uint32_t* w, int n, uint32_t* out, bool reorder, std::vector<uint32_t>& seq,
+                std::vector<int>& head, std::vector<int>& nxt) {
+    const int nvec = (n + 3) / 4;
+    const int np = nvec * 4;
+    seq.resize(np);
+    if (reorder) {
+        // bucket by bank (linked lists keep the ascending index order inside a bucket)
+        head.assign(64, -1);
+        nxt.assign(n, -1);
+        std::vector<int> tail(64, -1);
+        for (int i = 0; i < n; ++i) {
+            int bk = lds_bank(w[i] >> 16);
+            if (tail[bk] < 0) head[bk] = i; else nxt[tail[bk]] = i;
+            tail[bk] = i;
+        }
+        int q = 0;
+        while (q < n) {
+            for (int bk = 0; bk < 64; ++bk) {
+                if (head[bk] >= 0) {
+                    seq[q++] = w[head[bk]];
+                    head[bk] = nxt[head[bk]];
+                }
+            }
+        }
+    } else {
+        std::copy(w, w + n, seq.begin());
+    }
+    for (int q = n; q < np; ++q) seq[q] = seq[n - 1];  // padding: copies of a real word
+    // sequence -> (slot j, word e, lane l) instruction-major
+    int q = 0;
+    for (int j = 0; 64 * j < nvec; ++j) {
+        const int L = std::min(64, nvec - 64 * j);
+        for (int e = 0; e < 4; ++e)
+            for (int l = 0; l < L; ++l) out[4 * (64 * j + l) + e] = seq[q++];
+    }
+}
+
+}  // namespace
+
+lscd_status_t pack_offsets(const uint16_t* A, const uint8_t* mask, const Grid& g,
+                           std::vector<uint32_t>* offsets, int64_t* nnz_out) {
+    std::vector<int64_t> cnt((size_t)g.T, 0);
+    parallel_for(g.MB, [&](int64_t lo, int64_t hi) {
+        for (int64_t bm = lo; bm < hi; ++bm) {
+            int64_t* c = cnt.data() + bm * g.KT;
+            const int64_t r1 = std::min<int64_t>(g.M, (bm + 1) * g.tm);
+            for (int64_t r = bm * g.tm; r < r1; ++r) {
+                const size_t base = (size_t)r * (size_t)g.K;
+                for (int64_t bk = 0; bk < g.KT; ++bk) {
+                    const int64_t c1 = std::min<int64_t>(g.K, (bk + 1) * g.tk);
+                    int64_t n = 0;
+                    for (int64_t k = bk * g.tk; k < c1; ++k) n += kept(A, mask, base + (size_t)k);
+                    c[bk] += n;
+                }
+            }
+        }
+    });
+    offsets->assign((size_t)g.T + 1, 0);
+    uint64_t run = 0;
+    int64_t nnz = 0;
+    for (int64_t t = 0; t < g.T; ++t) {
+        nnz += cnt[(size_t)t];
+        run += (uint64_t)((cnt[(size_t)t] + 3) / 4 * 4);
+        if (run >= ((uint64_t)1 << 32)) return LSCD_ERROR_NOT_SUPPORTED;
+        (*offsets)[(size_t)t + 1] = (uint32_t)run;
+    }
+    *nnz_out = nnz;
+    return LSCD_SUCCESS;
+}
+
+void pack_fill(const uint16_t* A, const uint8_t* mask, const Grid& g, const uint32_t* offsets,
+               uint32_t* words) {
+    const bool reorder = reorder_enabled() && g.tm == kTileM && g.tk == kTileK;
+    parallel_for(g.MB, [&](int64_t lo, int64_t hi) {
+        std::vector<uint32_t> buf, seq;
+        std::vector<int> head, nxt;
+        buf.reserve((size_t)g.tm * g.tk);
+        for (int64_t bm = lo; bm < hi; ++bm) {
+            const int64_t r0 = bm * g.tm, r1 = std::min<int64_t>(g.M, r0 + g.tm);
+            for (int64_t bk = 0; bk < g.KT; ++bk) {
+                const int64_t c0 = bk * g.tk, c1 = std::min<int64_t>(g.K, c0 + g.tk);
+                buf.clear();
+                for (int64_t r = r0; r < r1; ++r) {
+                    const size_t base = (size_t)r * (size_t)g.K;
+                    for (int64_t c = c0; c < c1; ++c) {
+                        if (kept(A, mask, base + (size_t)c)) {
+                            uint32_t idx = (uint32_t)((r - r0) * g.tk + (c - c0));
+                            buf.push_back((idx << 16) | A[base + (size_t)c]);
+                        }
+                    }
+                }
+                const int64_t t = bm * g.KT + bk;
+                if (!buf.empty()) place_tile(buf.data(), (int)buf.size(), words + offsets[t], reorder, seq, head, nxt);
+            }
+        }
+    });
+}
+
+lscd_status_t validate_format(const uint32_t* words, int64_t nwords, const uint32_t* offsets,
+                              const Grid& g, int64_t* nnz_out, int32_t* maxw_out) {
+    if (offsets[0] != 0 || (int64_t)offsets[g.T] != nwords) return LSCD_ERROR_INVALID_FORMAT;
+    for (int64_t t = 0; t < g.T; ++t) {
+        if (offsets[t + 1] < offsets[t]) return LSCD_ERROR_INVALID_FORMAT;
+        if ((offsets[t + 1] - offsets[t]) & 3u) return LSCD_ERROR_INVALID_FORMAT;
+    }
+    std::atomic<bool> bad(false);
+    std::atomic<int64_t> nnz(0);
+    std::atomic<int32_t> maxw(0);
+    const uint32_t area = (uint32_t)g.tm * (uint32_t)g.tk;
+    parallel_for(g.T, [&](int64_t lo, int64_t hi) {
+        std::vector<uint32_t> stamp(area, 0), val(area, 0);
+        uint32_t gen = 0;
+        int64_t local = 0;
+        int32_t lmax = 0;
+        for (int64_t t = lo; t < hi && !bad.load(std::memory_order_relaxed); ++t) {
+            if (++gen == 0) {  // stamp wrap-around: clear
+                std::fill(stamp.begin(), stamp.end(), 0);
+                gen = 1;
+            }
+            const int64_t bm = t / g.KT, bk = t % g.KT;
+            const int64_t rows = std::min<int64_t>(g.tm, g.M - bm * g.tm);
+            const int64_t cols = std::min<int64_t>(g.tk, g.K - bk * g.tk);
+            const uint32_t a = offsets[t], b = offsets[t + 1];
+            lmax = std::max<int32_t>(lmax, (int32_t)(b - a));
+            for (uint32_t i = a; i < b; ++i) {
+                const uint32_t w = words[i];
+                const uint32_t idx = w >> 16;
+                if (idx >= area || (int64_t)(idx / g.tk) >= rows || (int64_t)(idx % g.tk) >= cols) {
+                    bad = true;
+                    break;
+                }
+                if (stamp[idx] == gen) {
+                    if (val[idx] != (w & 0xFFFFu)) {
+                        bad = true;
+                        break;
+                    }
+                } else {
+                    stamp[idx] = gen;
+                    val[idx] = w & 0xFFFFu;
+                    ++local;
+                }
+            }
+        }
+        nnz += local;
+        int32_t cur = maxw.load();
+        while (lmax > cur && !maxw.compare_exchange_weak(cur, lmax)) {
+        }
+    });
+    if (bad) return LSCD_ERROR_INVALID_FORMAT;
+    *nnz_out = nnz.load();
+    *maxw_out = maxw.load();
+    return LSCD_SUCCESS;
+}
+
+}  // namespace lscd
