@@ -33,16 +33,26 @@ def _hipcc() -> str:
 def _flags():
     return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-pthread",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-            "-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc")]
+            # MFMA results stay in ordinary VGPRs (no copies through the accumulator registers)
+            "-mllvm", "-amdgpu-mfma-vgpr-form",
+                "-I", os.path.join(ROOT, "include")]
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, pkg_dir: str = HERE, defines=()) -> str:
+    """Compile the sources of `pkg_dir` (default: this package) into `pkg_dir`/liblscd.so.
+
+    `defines` are extra -D options for tuning builds (tile-loop knobs such as LSCD_WAVES).
+    """
     hipcc = _hipcc()
-    os.makedirs(BUILD_DIR, exist_ok=True)
+    build_dir = os.path.join(pkg_dir, "_build")
+    lib = os.path.join(pkg_dir, "liblscd.so")
+    os.makedirs(build_dir, exist_ok=True)
+    extra = [f"-D{d}" for d in defines]
 
     def compile_one(src):
-        obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-        cmd = [hipcc, *_flags(), "-c", os.path.join(HERE, src), "-o", obj]
+        obj = os.path.join(build_dir, os.path.basename(src) + ".o")
+        cmd = [hipcc, *_flags(), "-I", os.path.join(pkg_dir, "csrc"), *extra, "-c", os.path.join(pkg_dir, src),
+               "-o", obj]
         if src.endswith(".cpp"):
             cmd[1:1] = ["-x", "hip"]
         r = subprocess.run(cmd, capture_output=True, text=True)
@@ -54,13 +64,13 @@ def build(verbose: bool = False) -> str:
 
     with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
         objs = list(ex.map(compile_one, SOURCES))
-    tmp = LIB + ".tmp"
+    tmp = lib + ".tmp"
     cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-pthread", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":

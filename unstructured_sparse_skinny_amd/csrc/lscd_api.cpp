@@ -18,7 +18,7 @@ struct lscd_handle_s {
     int64_t nnz_padded = 0;
     int32_t max_tile_words = 0;
     int R = 2;
-    int S = 1;  // K splits used by lscd_spmm
+    int S[3] = {1, 1, 1};  // K splits used by lscd_spmm for N padded to 16, 32, 64
     uint32_t* d_words = nullptr;
     uint32_t* d_offs = nullptr;
     float* d_part = nullptr;
@@ -43,21 +43,25 @@ void free_handle(lscd_handle_s* h) {
     delete h;
 }
 
-// Number of K splits: enough workgroups to give every CU a few, never fewer than four
-// k tiles per split.  LSCD_SPLITK overrides (tuning only).
-int plan_splits(const Grid& g, int cus) {
+// Number of K splits for one N padding: as many workgroups as the GPU holds at once
+// (CUs x resident workgroups per CU, from the kernel's real occupancy), so the whole grid
+// runs in a single wave with no tail, and never fewer than two k tiles per split.
+// LSCD_SPLITK overrides (tuning only).
+int plan_splits(const Grid& g, int cus, int blocks_per_cu) {
     const int64_t groups = (g.MB + lscd::kWaves - 1) / lscd::kWaves;
     int64_t S = 1;
     if (const char* e = getenv("LSCD_SPLITK")) {
         S = atoll(e);
     } else {
-        const int64_t target = (int64_t)cus * 2;
-        S = (target + groups - 1) / groups;
-        S = std::min<int64_t>(S, std::max<int64_t>(1, g.KT / 4));
+        const int64_t slots = (int64_t)cus * std::max(1, blocks_per_cu);
+        S = slots / groups;
+        S = std::min<int64_t>(S, std::max<int64_t>(1, g.KT / 2));
     }
     S = std::max<int64_t>(1, std::min<int64_t>(S, g.KT));
     return (int)S;
 }
+
+int npad_index(int N) { return N <= 16 ? 0 : (N <= 32 ? 1 : 2); }
 
 // Upload an encoding and size the workspace.  Takes ownership of nothing.
 lscd_status_t make_handle(const uint32_t* words, int64_t nwords, const uint32_t* offs, const Grid& g,
@@ -78,7 +82,12 @@ lscd_status_t make_handle(const uint32_t* words, int64_t nwords, const uint32_t*
         h->cus = cus;
     h->R = lscd::pick_reg_vectors(maxw);
     const bool kernel_tile = g.tm == lscd::kTileM && g.tk == lscd::kTileK;
-    h->S = kernel_tile ? plan_splits(g, h->cus) : 1;
+    int max_s = 1;
+    for (int i = 0; i < 3 && kernel_tile; ++i) {
+        const int occ = lscd::spmm_blocks_per_cu(16 << i, h->R, (int)std::min<int64_t>(g.K, 1 << 30));
+        h->S[i] = plan_splits(g, h->cus, occ);
+        max_s = std::max(max_s, h->S[i]);
+    }
     if (getenv("LSCD_TEST_FAIL_ALLOC")) {
         free_handle(h);
         return LSCD_ERROR_OUT_OF_MEMORY;
@@ -89,8 +98,8 @@ lscd_status_t make_handle(const uint32_t* words, int64_t nwords, const uint32_t*
         free_handle(h);
         return hip_status(e);
     }
-    if (h->S > 1) {
-        h->part_bytes = (int64_t)h->S * g.M * LSCD_MAX_N * 4;
+    if (max_s > 1) {
+        h->part_bytes = (int64_t)max_s * g.M * LSCD_MAX_N * 4;
         if ((e = hipMalloc((void**)&h->d_part, (size_t)h->part_bytes)) != hipSuccess) {
             free_handle(h);
             return hip_status(e);
@@ -249,7 +258,7 @@ lscd_status_t lscd_get_info(lscd_handle_t h, lscd_info_t* info) {
     info->max_tile_words = h->max_tile_words;
     info->device = h->device;
     info->workspace_bytes = h->part_bytes;
-    info->splits = h->S;
+    info->splits = h->S[0];
     info->reg_vectors = h->R;
     return LSCD_SUCCESS;
 }
@@ -260,9 +269,11 @@ lscd_status_t lscd_spmm(lscd_handle_t h, const void* B, void* C, int32_t N, void
     if (!B || !C || !aligned16(B) || !aligned16(C)) return LSCD_ERROR_INVALID_VALUE;
     if (N > LSCD_MAX_N) return LSCD_ERROR_NOT_SUPPORTED;
     if (h->g.tm != lscd::kTileM || h->g.tk != lscd::kTileK) return LSCD_ERROR_NOT_SUPPORTED;
+    if ((int64_t)N * h->g.K * 2 >= ((int64_t)1 << 31)) return LSCD_ERROR_NOT_SUPPORTED;  // B as one buffer
     lscd_status_t st = check_device(h);
     if (st != LSCD_SUCCESS) return st;
     hipStream_t s = (hipStream_t)stream;
+    const int S = h->S[npad_index(N)];
     lscd::SpmmArgs a;
     a.words = h->d_words;
     a.offs = h->d_offs;
@@ -275,14 +286,14 @@ lscd_status_t lscd_spmm(lscd_handle_t h, const void* B, void* C, int32_t N, void
     a.MB = (int32_t)h->g.MB;
     a.KT = (int32_t)h->g.KT;
     a.G = (int32_t)((h->g.MB + lscd::kWaves - 1) / lscd::kWaves);
-    a.S = h->S;
+    a.S = S;
     a.items = a.G * a.S;
     a.per_xcd = (a.items + 7) / 8;
     const int npad = N <= 16 ? 16 : (N <= 32 ? 32 : 64);
     hipError_t e = lscd::launch_spmm(npad, h->R, a, 8 * a.per_xcd, s);
     if (e != hipSuccess) return hip_status(e);
-    if (h->S > 1) {
-        e = lscd::launch_reduce(h->d_part, (uint16_t*)C, h->S, (int64_t)N * h->g.M, s);
+    if (S > 1) {
+        e = lscd::launch_reduce(h->d_part, (uint16_t*)C, S, (int64_t)N * h->g.M, s);
         if (e != hipSuccess) return hip_status(e);
     }
     return LSCD_SUCCESS;

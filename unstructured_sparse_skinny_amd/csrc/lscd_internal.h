@@ -16,7 +16,10 @@ namespace lscd {
 constexpr int kTileM = 64;
 constexpr int kTileK = 64;
 // Wavefronts per workgroup; each owns one row block, all share the staged B tile.
-constexpr int kWaves = 4;
+#ifndef LSCD_WAVES
+#define LSCD_WAVES 4
+#endif
+constexpr int kWaves = LSCD_WAVES;
 constexpr int kThreads = kWaves * 64;
 
 // ---------------------------------------------------------------- host encoder
@@ -72,6 +75,8 @@ struct DecodeArgs {
 // Staging registers per lane and tile that have kernel instantiations.
 int pick_reg_vectors(int32_t max_tile_words);
 hipError_t launch_spmm(int npad, int R, const SpmmArgs& a, int grid, hipStream_t s);
+// Workgroups of the product kernel (for this N padding and stage size) resident per CU.
+int spmm_blocks_per_cu(int npad, int R, int K);
 hipError_t launch_reduce(const float* part, uint16_t* C, int S, int64_t NM, hipStream_t s);
 hipError_t launch_decode(int R, const DecodeArgs& a, int grid, hipStream_t s);
 

@@ -33,9 +33,12 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+typedef __attribute__((address_space(4))) const uint32_t kconst_u32;
+
 constexpr int kRowBytes = kTileK * 2;           // 128
 constexpr int kTileBytes = kTileM * kRowBytes;  // 8192
 constexpr int kBufWord3 = 0x00020000;           // raw buffer descriptor, word 3 (gfx9)
+constexpr int kStreamPolicy = 2;                // "nt": the packed words are read exactly once
 
 __device__ __forceinline__ uint32_t lds_chunk(uint32_t r, uint32_t chunk) {
     return r * kRowBytes + (((chunk ^ r) & 7u) << 4);
@@ -64,7 +67,8 @@ __device__ __forceinline__ void load_tile(u32x4 (&wb)[R], const uint32_t* words,
     __amdgpu_buffer_rsrc_t rs =
         __builtin_amdgcn_make_buffer_rsrc((void*)(words + first), (short)0, nvec * 16, kBufWord3);
 #pragma unroll
-    for (int j = 0; j < R; ++j) wb[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, (j * 64 + lane) * 16, 0, 0);
+    for (int j = 0; j < R; ++j)
+        wb[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, (j * 64 + lane) * 16, 0, kStreamPolicy);
 }
 
 __device__ __forceinline__ void zero_tile(unsigned char* As, int lane) {
@@ -97,25 +101,34 @@ __device__ __forceinline__ void scatter_tile(const u32x4 (&wb)[R], int nvec, uns
     }
 }
 
-// B tile (64 k x NPAD n) staging: 16-byte chunks, 8 per row of 64 k.
-template <int NPAD>
+// B tile (64 k x NPAD n) staging: 16-byte chunks, 8 per row of 64 k.  Each pipeline stage
+// holds the B chunks of the same k tile as its packed words, so that waiting for a stage
+// (the oldest loads in flight; the vector-memory counter retires in order) never waits on
+// loads issued for later tiles.
+template <int NPAD, bool VEC>
 struct BStage {
     static constexpr int kChunks = NPAD * 8;
     static constexpr int kPer = (kChunks + kThreads - 1) / kThreads;
     u32x4 r[kPer];
 
-    __device__ __forceinline__ void load(const uint16_t* B, int N, int K, int kt, int tid, bool vec_ok) {
+    // VEC (K % 8 == 0): one 16-byte buffer load per chunk; chunks outside B (n >= N, k >= K,
+    // or a tile past the split) get an out-of-range offset and read zero without a fetch,
+    // so the load sequence has no branches.  Otherwise element-wise guarded loads.
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rb, const uint16_t* B, int N, int K, int kt,
+                                         int tid, bool valid) {
 #pragma unroll
         for (int u = 0; u < kPer; ++u) {
             const int ch = tid + u * kThreads;
             const int n = ch >> 3, c = ch & 7;
-            u32x4 v = {0u, 0u, 0u, 0u};
-            if (ch < kChunks && n < N) {
-                const int k0 = kt * kTileK + c * 8;
-                const uint16_t* p = B + (size_t)n * K + k0;
-                if (vec_ok && k0 + 8 <= K) {
-                    v = *reinterpret_cast<const u32x4*>(p);
-                } else {
+            const int k0 = kt * kTileK + c * 8;
+            const bool in = valid && ch < kChunks && n < N && k0 < K;
+            if constexpr (VEC) {
+                const uint32_t off = in ? (uint32_t)((n * K + k0) * 2) : 0x80000000u;
+                r[u] = __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0);
+            } else {
+                u32x4 v = {0u, 0u, 0u, 0u};
+                if (in) {
+                    const uint16_t* p = B + (size_t)n * K + k0;
                     uint32_t h[8];
 #pragma unroll
                     for (int e = 0; e < 8; ++e) h[e] = (k0 + e < K) ? p[e] : 0u;
@@ -124,8 +137,8 @@ struct BStage {
                     v[2] = h[4] | (h[5] << 16);
                     v[3] = h[6] | (h[7] << 16);
                 }
+                r[u] = v;
             }
-            r[u] = v;
         }
     }
     __device__ __forceinline__ void store(unsigned char* Bs, int N, int tid) const {
@@ -159,7 +172,7 @@ __device__ __forceinline__ void mma_tile(f32x4 (&acc)[4][NPAD / 16], const unsig
     }
 }
 
-template <int NPAD, int R, int P>
+template <int NPAD, int R, int P, bool VEC>
 __global__ __launch_bounds__(kThreads) void spmm_kernel(SpmmArgs a) {
     __shared__ __attribute__((aligned(16))) unsigned char smem[kWaves * kTileBytes + 2 * NPAD * kRowBytes];
     const int tid = threadIdx.x;
@@ -179,8 +192,13 @@ __global__ __launch_bounds__(kThreads) void spmm_kernel(SpmmArgs a) {
     const int kt1 = (int)(((int64_t)(s + 1) * a.KT) / a.S);
     const int rb = g * kWaves + wave;
     const bool active = rb < a.MB;
-    const uint32_t* toff = a.offs + (int64_t)(active ? rb : 0) * a.KT;
-    const bool vec_ok = (a.K & 7) == 0;
+    // Tile offsets are read through the constant address space: the offsets are never
+    // written by the kernel, and this lets the compiler use scalar loads (counted apart
+    // from the vector loads of the packed words) for these wave-uniform addresses.
+    const kconst_u32* toff = (const kconst_u32*)(a.offs) + (int64_t)(active ? rb : 0) * a.KT;
+    // B as a buffer of N*K fp16 (requires N*K*2 < 2^31, checked by the host)
+    const __amdgpu_buffer_rsrc_t bsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)a.B, (short)0, a.N * a.K * 2, kBufWord3);
 
     // B rows n >= N stay zero for the whole kernel (both buffers).
     for (int ch = tid; ch < 2 * NPAD * 8; ch += kThreads) {
@@ -191,7 +209,12 @@ __global__ __launch_bounds__(kThreads) void spmm_kernel(SpmmArgs a) {
         }
     }
 
+    // Tile offsets are scalar loads; the one a refill needs is fetched a step earlier, so the
+    // loads of a tile are never held up by a round trip for its own offset.
+    auto off_at = [&](int i) -> uint32_t { return (active && i <= kt1) ? toff[i] : 0u; };
+
     u32x4 wb[P][R];
+    BStage<NPAD, VEC> bst[P];
     int nv[P];
     uint32_t first[P];
 #pragma unroll
@@ -204,10 +227,11 @@ __global__ __launch_bounds__(kThreads) void spmm_kernel(SpmmArgs a) {
         }
         first[q] = o0;
         nv[q] = (int)((o1 - o0) >> 2);
+        bst[q].load(bsrc, a.B, a.N, a.K, k, tid, k < kt1);
         load_tile<R>(wb[q], a.words, o0, nv[q], lane);
     }
-    BStage<NPAD> bst;
-    bst.load(a.B, a.N, a.K, kt0, tid, vec_ok);
+    uint32_t o_next = off_at(kt0 + P);      // start of the next tile to fetch
+    uint32_t o_pf = off_at(kt0 + P + 1);    // its end, prefetched
 
     f32x4 acc[4][NPAD / 16];
 #pragma unroll
@@ -215,75 +239,84 @@ __global__ __launch_bounds__(kThreads) void spmm_kernel(SpmmArgs a) {
 #pragma unroll
         for (int j = 0; j < NPAD / 16; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+    // Every stage issues its loads on every step, also past the end of the split (those
+    // tiles are empty: zero-length descriptors and out-of-range B offsets fetch nothing).
+    // With no conditional loads the compiler can count exactly how many younger loads are in
+    // flight and waits only for the stage it consumes.
     for (int kt = kt0; kt < kt1; kt += P) {
 #pragma unroll
         for (int q = 0; q < P; ++q) {
             const int k = kt + q;
-            if (k < kt1) {  // uniform over the workgroup
+            {
                 unsigned char* Bs = Bs0 + (k & 1) * NPAD * kRowBytes;
-                bst.store(Bs, a.N, tid);
-                if (k + 1 < kt1) bst.load(a.B, a.N, a.K, k + 1, tid, vec_ok);
+                const int kn = k + P;
+                const uint32_t o_pf2 = off_at(kn + 2);  // issued early: the barrier waits for it
+                bst[q].store(Bs, a.N, tid);
                 const int n = nv[q];
                 if (n > 0) {
                     zero_tile(As, lane);
                     scatter_tile<R>(wb[q], n, As, a.words + first[q], lane);
                 }
                 // refill this register stage with tile k + P
-                const int kn = k + P;
                 uint32_t o0 = 0, o1 = 0;
                 if (active && kn < kt1) {
-                    o0 = toff[kn];
-                    o1 = toff[kn + 1];
+                    o0 = o_next;
+                    o1 = o_pf;
                 }
+                o_next = o_pf;
+                o_pf = o_pf2;
                 first[q] = o0;
                 nv[q] = (int)((o1 - o0) >> 2);
+                bst[q].load(bsrc, a.B, a.N, a.K, kn, tid, kn < kt1);
                 load_tile<R>(wb[q], a.words, o0, nv[q], lane);
                 __syncthreads();
                 if (n > 0) mma_tile<NPAD>(acc, As, Bs, lane);
             }
         }
     }
-    if (!active) return;
-
     // MFMA 16x16 result layout: lane holds column (lane & 15), rows 4*(lane >> 4) + 0..3.
     const int ncol = lane & 15;
     const int mrow = rb * kTileM + (lane >> 4) * 4;
     const bool vec_m = (a.M & 3) == 0;
+    if (active) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < 4; ++i) {
 #pragma unroll
-        for (int j = 0; j < NPAD / 16; ++j) {
-            const int n = j * 16 + ncol;
-            const int m = mrow + i * 16;
-            if (n >= a.N || m >= a.M) continue;
-            const f32x4 v = acc[i][j];
-            if (a.S == 1) {
-                uint16_t* dst = a.C + (int64_t)n * a.M + m;
-                if (vec_m && m + 3 < a.M) {
-                    uint2 pk;
-                    pk.x = (uint32_t)f16_bits(v[0]) | ((uint32_t)f16_bits(v[1]) << 16);
-                    pk.y = (uint32_t)f16_bits(v[2]) | ((uint32_t)f16_bits(v[3]) << 16);
-                    *reinterpret_cast<uint2*>(dst) = pk;
+            for (int j = 0; j < NPAD / 16; ++j) {
+                const int n = j * 16 + ncol;
+                const int m = mrow + i * 16;
+                if (n >= a.N || m >= a.M) continue;
+                const f32x4 v = acc[i][j];
+                if (a.S == 1) {
+                    uint16_t* dst = a.C + (int64_t)n * a.M + m;
+                    if (vec_m && m + 3 < a.M) {
+                        uint2 pk;
+                        pk.x = (uint32_t)f16_bits(v[0]) | ((uint32_t)f16_bits(v[1]) << 16);
+                        pk.y = (uint32_t)f16_bits(v[2]) | ((uint32_t)f16_bits(v[3]) << 16);
+                        *reinterpret_cast<uint2*>(dst) = pk;
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (m + e < a.M) dst[e] = f16_bits(v[e]);
+                    }
                 } else {
+                    float* dst = a.part + ((int64_t)s * a.N + n) * a.M + m;
+                    if (vec_m && m + 3 < a.M) {
+                        *reinterpret_cast<f32x4*>(dst) = v;
+                    } else {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (m + e < a.M) dst[e] = f16_bits(v[e]);
-                }
-            } else {
-                float* dst = a.part + ((int64_t)s * a.N + n) * a.M + m;
-                if (vec_m && m + 3 < a.M) {
-                    *reinterpret_cast<f32x4*>(dst) = v;
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (m + e < a.M) dst[e] = v[e];
+                        for (int e = 0; e < 4; ++e)
+                            if (m + e < a.M) dst[e] = v[e];
+                    }
                 }
             }
         }
     }
 }
 
-// Second pass of split-K: C = fp16( ((P0 + P1) + P2) + ... ), fixed ascending order.
+// Second pass of split-K: C = fp16( ((P0 + P1) + P2) + ... ), fixed ascending order.  A
+// separate launch: the kernel boundary makes every workgroup's partial sums visible to
+// every XCD without cache write-backs inside the product kernel.
 __global__ __launch_bounds__(256) void reduce_kernel(const float* __restrict__ part, uint16_t* __restrict__ C,
                                                      int S, int64_t NM) {
     const int64_t stride = (int64_t)gridDim.x * 256;
@@ -349,25 +382,44 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     }
 }
 
+// Register stages of the prefetch pipeline: deeper when a tile needs few registers.
+template <int R>
+constexpr int stages() {
+#ifdef LSCD_STAGES
+    return LSCD_STAGES;
+#else
+    return R <= 4 ? 4 : (R <= 8 ? 3 : 2);
+#endif
+}
+
+// grid < 0: return the kernel's resident workgroups per CU in *occ instead of launching.
+// K % 8 != 0 (rows of B not 16-byte aligned) runs the element-wise B path, instantiated
+// only with the largest register stage.
 template <int NPAD, int R>
-hipError_t launch_spmm_r(const SpmmArgs& a, int grid, hipStream_t st) {
-    constexpr int P = R <= 4 ? 3 : 2;
-    hipLaunchKernelGGL((spmm_kernel<NPAD, R, P>), dim3(grid), dim3(kThreads), 0, st, a);
+hipError_t launch_spmm_r(const SpmmArgs& a, int grid, hipStream_t st, int* occ) {
+    constexpr int P = stages<R>();
+    if ((a.K & 7) != 0) {
+        if (occ) return hipOccupancyMaxActiveBlocksPerMultiprocessor(occ, spmm_kernel<NPAD, 16, 2, false>, kThreads, 0);
+        hipLaunchKernelGGL((spmm_kernel<NPAD, 16, 2, false>), dim3(grid), dim3(kThreads), 0, st, a);
+        return hipGetLastError();
+    }
+    if (occ) return hipOccupancyMaxActiveBlocksPerMultiprocessor(occ, spmm_kernel<NPAD, R, P, true>, kThreads, 0);
+    hipLaunchKernelGGL((spmm_kernel<NPAD, R, P, true>), dim3(grid), dim3(kThreads), 0, st, a);
     return hipGetLastError();
 }
 
 template <int NPAD>
-hipError_t launch_spmm_n(int R, const SpmmArgs& a, int grid, hipStream_t st) {
+hipError_t launch_spmm_n(int R, const SpmmArgs& a, int grid, hipStream_t st, int* occ) {
     switch (R) {
-        case 2: return launch_spmm_r<NPAD, 2>(a, grid, st);
-        case 3: return launch_spmm_r<NPAD, 3>(a, grid, st);
-        case 4: return launch_spmm_r<NPAD, 4>(a, grid, st);
-        case 5: return launch_spmm_r<NPAD, 5>(a, grid, st);
-        case 6: return launch_spmm_r<NPAD, 6>(a, grid, st);
-        case 8: return launch_spmm_r<NPAD, 8>(a, grid, st);
-        case 10: return launch_spmm_r<NPAD, 10>(a, grid, st);
-        case 12: return launch_spmm_r<NPAD, 12>(a, grid, st);
-        case 16: return launch_spmm_r<NPAD, 16>(a, grid, st);
+        case 2: return launch_spmm_r<NPAD, 2>(a, grid, st, occ);
+        case 3: return launch_spmm_r<NPAD, 3>(a, grid, st, occ);
+        case 4: return launch_spmm_r<NPAD, 4>(a, grid, st, occ);
+        case 5: return launch_spmm_r<NPAD, 5>(a, grid, st, occ);
+        case 6: return launch_spmm_r<NPAD, 6>(a, grid, st, occ);
+        case 8: return launch_spmm_r<NPAD, 8>(a, grid, st, occ);
+        case 10: return launch_spmm_r<NPAD, 10>(a, grid, st, occ);
+        case 12: return launch_spmm_r<NPAD, 12>(a, grid, st, occ);
+        case 16: return launch_spmm_r<NPAD, 16>(a, grid, st, occ);
         default: return hipErrorInvalidValue;
     }
 }
@@ -397,11 +449,24 @@ int pick_reg_vectors(int32_t max_tile_words) {
 
 hipError_t launch_spmm(int npad, int R, const SpmmArgs& a, int grid, hipStream_t st) {
     switch (npad) {
-        case 16: return launch_spmm_n<16>(R, a, grid, st);
-        case 32: return launch_spmm_n<32>(R, a, grid, st);
-        case 64: return launch_spmm_n<64>(R, a, grid, st);
+        case 16: return launch_spmm_n<16>(R, a, grid, st, nullptr);
+        case 32: return launch_spmm_n<32>(R, a, grid, st, nullptr);
+        case 64: return launch_spmm_n<64>(R, a, grid, st, nullptr);
         default: return hipErrorInvalidValue;
     }
+}
+
+int spmm_blocks_per_cu(int npad, int R, int K) {
+    int occ = 0;
+    SpmmArgs dummy{};
+    dummy.K = K;
+    hipError_t e = hipErrorInvalidValue;
+    switch (npad) {
+        case 16: e = launch_spmm_n<16>(R, dummy, 0, nullptr, &occ); break;
+        case 32: e = launch_spmm_n<32>(R, dummy, 0, nullptr, &occ); break;
+        case 64: e = launch_spmm_n<64>(R, dummy, 0, nullptr, &occ); break;
+    }
+    return (e == hipSuccess && occ > 0) ? occ : 1;
 }
 
 hipError_t launch_reduce(const float* part, uint16_t* C, int S, int64_t NM, hipStream_t st) {
