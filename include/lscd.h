@@ -62,8 +62,11 @@ typedef struct {
     int32_t max_tile_words;     /* largest tile, in words                                  */
     int32_t device;             /* HIP device the handle's buffers live on                 */
     int64_t workspace_bytes;    /* device split-K workspace owned by the handle            */
-    int32_t splits;             /* K-splits lscd_spmm uses for this matrix                 */
     int32_t reg_vectors;        /* 128-bit staging registers per lane and tile (kernel cfg) */
+    int32_t splits[3];          /* K-splits across workgroups lscd_spmm uses for N padded to
+                                   16, 32 and 64 (1: no second pass)                        */
+    int32_t variant[3];         /* product kernel variant for N padded to 16, 32, 64:
+                                   0 shared B tile, 1 / 2 independent wavefronts (4 / 8)    */
 } lscd_info_t;
 
 #define LSCD_DEFAULT_TILE_M 64

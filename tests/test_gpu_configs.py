@@ -1,0 +1,83 @@
+"""GPU parity at the full benchmark sizes, in the launch configuration the benchmark times.
+
+For each configuration (the five OPT-shaped workloads of lscd_synth) the product runs on
+the whole matrix; the oracle computes a sample of rows one by one (the first and last
+row blocks and 256 random rows):
+  * Gaussian inputs: the sampled rows pass the tolerance gates (tests/_util.py);
+  * integer-valued inputs with the configuration's own mask: the sampled rows are
+    bit-exact against fp16_rne of the oracle (every fp32 partial sum is an exact integer);
+  * for configuration 2 the decoded matrix (lscd_debug_decode) is compared bit for bit.
+"""
+import numpy as np
+import pytest
+
+import lscd_synth as syn
+from oracle import spmm as osp
+from oracle import tiled_csl as tc
+from tests._util import assert_gates, say
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import unstructured_sparse_skinny_amd as L
+
+
+def _rows(M, seed=0):
+    rng = np.random.default_rng(seed)
+    pick = set(range(min(64, M))) | set(range(max(0, M - 64), M)) | set(rng.choice(M, size=min(M, 256), replace=False).tolist())
+    return np.array(sorted(pick), dtype=np.int64)
+
+
+def _run(h, B16, M):
+    B = torch.from_numpy(np.ascontiguousarray(B16).view(np.float16)).to("cuda")
+    C = torch.full((B16.shape[0], M), float("nan"), dtype=torch.float16, device="cuda")
+    L.lscd_spmm(h, B, C)
+    torch.cuda.synchronize()
+    return C.cpu().numpy().view(np.uint16)
+
+
+CASES = [(1, 0, None), (2, 0, None), (3, 0, None), (4, 0, None),
+         (5, 0, (8, 16, 32, 64)), (5, 1, (8, 16, 32, 64)), (5, 2, (8, 16, 32, 64)), (5, 3, (8, 16, 32, 64))]
+
+
+@pytest.mark.parametrize("cfg,shape,Ns", CASES, ids=[f"cfg{c}s{s}" for c, s, _ in CASES])
+def test_full_size_gaussian(cfg, shape, Ns):
+    case = syn.make_config(cfg, shape)
+    say(f"full {case.name}: M={case.M} K={case.K} sparsity={case.sparsity:.3f}")
+    h = L.lscd_encode(case.A16, case.mask)
+    rows = _rows(case.M)
+    for N in (Ns or (case.N,)):
+        B16 = case.B16 if N == case.N else syn.make_config(cfg, shape, N=N).B16
+        say(f"  N={N}")
+        C = _run(h, B16, case.M)
+        C64 = osp.spmm_f64(case.A16, case.mask, B16, rows=rows)
+        assert np.isfinite(C.view(np.float16)).all()
+        mr, fr = assert_gates(C[:, rows], C64, f"{case.name} N={N}")
+        say(f"    max_rel={mr:.2e} fro_rel={fr:.2e}")
+
+
+@pytest.mark.parametrize("cfg,shape", [(1, 0), (2, 0), (3, 0), (4, 0), (5, 1)])
+def test_full_size_integer_bit_exact(cfg, shape):
+    case = syn.make_config(cfg, shape)
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([4321, cfg, shape])))
+    A16 = syn.int_fp16(rng, case.M, case.K)
+    B16 = syn.int_fp16(rng, case.N, case.K)
+    say(f"int {case.name}")
+    h = L.lscd_encode(A16, case.mask)
+    C = _run(h, B16, case.M)
+    rows = _rows(case.M, seed=1)
+    C64 = osp.spmm_f64(A16, case.mask, B16, rows=rows)
+    assert np.abs(C64).max() < 65504
+    assert np.array_equal(C[:, rows], osp.fp16_rne(C64))
+
+
+def test_full_size_decode_cfg2():
+    case = syn.make_config(2)
+    h = L.lscd_encode(case.A16, case.mask)
+    A = torch.empty((case.M, case.K), dtype=torch.float16, device="cuda")
+    L.lscd_debug_decode(h, A)
+    torch.cuda.synchronize()
+    got = A.cpu().numpy().view(np.uint16)
+    assert np.array_equal(got, tc.masked(case.A16, case.mask))
+    assert h.info["nnz"] == int(case.mask.sum())

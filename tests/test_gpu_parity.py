@@ -67,12 +67,17 @@ def test_decode_dense_and_overflow_paths():
 
 @pytest.mark.parametrize("N", [1, 7, 8, 16, 17, 32, 33, 48, 64])
 @pytest.mark.parametrize("splits", [None, "1", "3"])
-def test_integer_bit_exact(N, splits):
-    """Integer inputs: every partial sum is exact in fp32, so C must equal fp16_rne(C_oracle) bit for bit."""
+@pytest.mark.parametrize("variant", ["indep", "shared"])
+def test_integer_bit_exact(N, splits, variant):
+    """Integer inputs: every partial sum is exact in fp32, so C must equal fp16_rne(C_oracle) bit for bit.
+
+    Runs both product kernel variants (the independent-wavefront one exists for N <= 32; above
+    that the shared-B kernel runs whatever is asked).
+    """
     case = syn.random_case(333, 1000 + 8 * N, N, 0.35, seed=N, values="int3")
-    with env(LSCD_SPLITK=splits):
+    with env(LSCD_SPLITK=splits, LSCD_KERNEL=variant):
         h = L.lscd_encode(case.A16, case.mask)
-    say(f"int N={N} S={h.info['splits']}")
+    say(f"int N={N} S={h.info['splits'][L.npad_index(N)]} variant={h.info['variant'][L.npad_index(N)]}")
     C = run_spmm(h, case.B16, case.M)
     C64 = osp.spmm_f64(case.A16, case.mask, case.B16)
     assert np.abs(C64).max() < 2048
@@ -81,10 +86,12 @@ def test_integer_bit_exact(N, splits):
 
 @pytest.mark.parametrize("M,K,keep", SHAPES)
 @pytest.mark.parametrize("N", [8, 16, 32, 64])
-def test_gaussian_within_tolerance(M, K, keep, N):
+@pytest.mark.parametrize("variant", ["indep", "shared"])
+def test_gaussian_within_tolerance(M, K, keep, N, variant):
     case = syn.random_case(M, K, N, keep, seed=M + N)
-    h = L.lscd_encode(case.A16, case.mask)
-    say(f"gauss M={M} K={K} N={N} S={h.info['splits']} R={h.info['reg_vectors']}")
+    with env(LSCD_KERNEL=variant):
+        h = L.lscd_encode(case.A16, case.mask)
+    say(f"gauss M={M} K={K} N={N} S={h.info['splits'][L.npad_index(N)]} R={h.info['reg_vectors']}")
     C = run_spmm(h, case.B16, M)
     assert_gates(C, osp.spmm_f64(case.A16, case.mask, case.B16), f"M={M} K={K} N={N}")
 

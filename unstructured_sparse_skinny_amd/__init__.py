@@ -40,7 +40,8 @@ class lscd_info_t(ctypes.Structure):
                 ("tile_k", ctypes.c_int32), ("num_tiles", ctypes.c_int64), ("nnz", ctypes.c_int64),
                 ("nnz_padded", ctypes.c_int64), ("format_bytes", ctypes.c_int64),
                 ("max_tile_words", ctypes.c_int32), ("device", ctypes.c_int32),
-                ("workspace_bytes", ctypes.c_int64), ("splits", ctypes.c_int32), ("reg_vectors", ctypes.c_int32)]
+                ("workspace_bytes", ctypes.c_int64), ("reg_vectors", ctypes.c_int32),
+                ("splits", ctypes.c_int32 * 3), ("variant", ctypes.c_int32 * 3)]
 
 
 class LSCDError(RuntimeError):
@@ -179,7 +180,14 @@ def lscd_import(nonzeros, tile_offsets, M, K, tile_m=LSCD_DEFAULT_TILE_M, tile_k
 def lscd_get_info(h: Handle) -> dict:
     info = lscd_info_t()
     _check(_lib.lscd_get_info(ctypes.c_void_p(h.ptr), ctypes.byref(info)), "lscd_get_info")
-    return {name: getattr(info, name) for name, _ in lscd_info_t._fields_}
+    out = {name: getattr(info, name) for name, _ in lscd_info_t._fields_}
+    out["splits"], out["variant"] = list(info.splits), list(info.variant)
+    return out
+
+
+def npad_index(N: int) -> int:
+    """Index into lscd_info_t.splits / .variant for a batch width N."""
+    return 0 if N <= 16 else (1 if N <= 32 else 2)
 
 
 def lscd_export(h: Handle):

@@ -18,7 +18,8 @@ struct lscd_handle_s {
     int64_t nnz_padded = 0;
     int32_t max_tile_words = 0;
     int R = 2;
-    int S[3] = {1, 1, 1};  // K splits used by lscd_spmm for N padded to 16, 32, 64
+    int S[3] = {1, 1, 1};     // K splits used by lscd_spmm for N padded to 16, 32, 64
+    int kind[3] = {0, 0, 0};  // product kernel variant for N padded to 16, 32, 64
     uint32_t* d_words = nullptr;
     uint32_t* d_offs = nullptr;
     float* d_part = nullptr;
@@ -45,20 +46,38 @@ void free_handle(lscd_handle_s* h) {
 
 // Number of K splits for one N padding: as many workgroups as the GPU holds at once
 // (CUs x resident workgroups per CU, from the kernel's real occupancy), so the whole grid
-// runs in a single wave with no tail, and never fewer than two k tiles per split.
+// runs in a single wave with no tail; every wavefront keeps at least two k tiles.
 // LSCD_SPLITK overrides (tuning only).
-int plan_splits(const Grid& g, int cus, int blocks_per_cu) {
-    const int64_t groups = (g.MB + lscd::kWaves - 1) / lscd::kWaves;
+// The independent-wavefront variants already split each row block's k range inside the
+// workgroup; they split across workgroups (fp32 partials + second pass) only when the row
+// blocks fill less than half of the resident slots.
+int plan_splits(const Grid& g, int cus, int blocks_per_cu, int64_t groups, int tiles_per_split_min, bool indep) {
     int64_t S = 1;
     if (const char* e = getenv("LSCD_SPLITK")) {
         S = atoll(e);
     } else {
         const int64_t slots = (int64_t)cus * std::max(1, blocks_per_cu);
-        S = slots / groups;
-        S = std::min<int64_t>(S, std::max<int64_t>(1, g.KT / 2));
+        S = indep ? slots / (2 * groups) : slots / groups;
+        S = std::min<int64_t>(S, std::max<int64_t>(1, g.KT / tiles_per_split_min));
     }
     S = std::max<int64_t>(1, std::min<int64_t>(S, g.KT));
     return (int)S;
+}
+
+int64_t row_groups(const Grid& g, int kind) {
+    return kind == lscd::kKernelShared ? (g.MB + lscd::kWaves - 1) / lscd::kWaves : g.MB;
+}
+
+// Variant per N padding (measured on MI355X): independent wavefronts for N <= 16, where
+// the per-wavefront B fragments are small; the shared B tile above that.
+// LSCD_KERNEL=shared|indep overrides where the variant exists (tuning only).
+int pick_kind(int npad) {
+    const char* e = getenv("LSCD_KERNEL");
+    if (npad > 32) return lscd::kKernelShared;
+    if (e && strcmp(e, "shared") == 0) return lscd::kKernelShared;
+    if (e && strcmp(e, "indep") == 0) return lscd::kKernelIndep;
+    if (e && strcmp(e, "indep8") == 0) return lscd::kKernelIndep8;
+    return npad <= 16 ? lscd::kKernelIndep : lscd::kKernelShared;
 }
 
 int npad_index(int N) { return N <= 16 ? 0 : (N <= 32 ? 1 : 2); }
@@ -84,8 +103,11 @@ lscd_status_t make_handle(const uint32_t* words, int64_t nwords, const uint32_t*
     const bool kernel_tile = g.tm == lscd::kTileM && g.tk == lscd::kTileK;
     int max_s = 1;
     for (int i = 0; i < 3 && kernel_tile; ++i) {
-        const int occ = lscd::spmm_blocks_per_cu(16 << i, h->R, (int)std::min<int64_t>(g.K, 1 << 30));
-        h->S[i] = plan_splits(g, h->cus, occ);
+        h->kind[i] = pick_kind(16 << i);
+        const int occ = lscd::spmm_blocks_per_cu(h->kind[i], 16 << i, h->R, (int)std::min<int64_t>(g.K, 1 << 30));
+        const int min_tiles = h->kind[i] == lscd::kKernelIndep ? 8 : (h->kind[i] == lscd::kKernelIndep8 ? 16 : 2);
+        h->S[i] = plan_splits(g, h->cus, occ, row_groups(g, h->kind[i]), min_tiles,
+                              h->kind[i] != lscd::kKernelShared);
         max_s = std::max(max_s, h->S[i]);
     }
     if (getenv("LSCD_TEST_FAIL_ALLOC")) {
@@ -258,8 +280,11 @@ lscd_status_t lscd_get_info(lscd_handle_t h, lscd_info_t* info) {
     info->max_tile_words = h->max_tile_words;
     info->device = h->device;
     info->workspace_bytes = h->part_bytes;
-    info->splits = h->S[0];
     info->reg_vectors = h->R;
+    for (int i = 0; i < 3; ++i) {
+        info->splits[i] = h->S[i];
+        info->variant[i] = h->kind[i];
+    }
     return LSCD_SUCCESS;
 }
 
@@ -274,6 +299,7 @@ lscd_status_t lscd_spmm(lscd_handle_t h, const void* B, void* C, int32_t N, void
     if (st != LSCD_SUCCESS) return st;
     hipStream_t s = (hipStream_t)stream;
     const int S = h->S[npad_index(N)];
+    const int kind = h->kind[npad_index(N)];
     lscd::SpmmArgs a;
     a.words = h->d_words;
     a.offs = h->d_offs;
@@ -285,12 +311,12 @@ lscd_status_t lscd_spmm(lscd_handle_t h, const void* B, void* C, int32_t N, void
     a.N = N;
     a.MB = (int32_t)h->g.MB;
     a.KT = (int32_t)h->g.KT;
-    a.G = (int32_t)((h->g.MB + lscd::kWaves - 1) / lscd::kWaves);
+    a.G = (int32_t)row_groups(h->g, kind);
     a.S = S;
     a.items = a.G * a.S;
     a.per_xcd = (a.items + 7) / 8;
     const int npad = N <= 16 ? 16 : (N <= 32 ? 32 : 64);
-    hipError_t e = lscd::launch_spmm(npad, h->R, a, 8 * a.per_xcd, s);
+    hipError_t e = lscd::launch_spmm(kind, npad, h->R, a, 8 * a.per_xcd, s);
     if (e != hipSuccess) return hip_status(e);
     if (S > 1) {
         e = lscd::launch_reduce(h->d_part, (uint16_t*)C, S, (int64_t)N * h->g.M, s);

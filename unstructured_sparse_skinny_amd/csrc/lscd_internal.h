@@ -74,9 +74,15 @@ struct DecodeArgs {
 
 // Staging registers per lane and tile that have kernel instantiations.
 int pick_reg_vectors(int32_t max_tile_words);
-hipError_t launch_spmm(int npad, int R, const SpmmArgs& a, int grid, hipStream_t s);
-// Workgroups of the product kernel (for this N padding and stage size) resident per CU.
-int spmm_blocks_per_cu(int npad, int R, int K);
+// Product kernel variants: kKernelShared -- four row blocks per workgroup sharing a B tile
+// in LDS (any N); kKernelIndep -- one row block per workgroup, its k range split over the
+// wavefronts, B in registers (N <= 32).
+constexpr int kKernelShared = 0;
+constexpr int kKernelIndep = 1;   // 4 wavefronts per row block
+constexpr int kKernelIndep8 = 2;  // 8 wavefronts per row block
+hipError_t launch_spmm(int kind, int npad, int R, const SpmmArgs& a, int grid, hipStream_t s);
+// Workgroups of a product kernel (variant, N padding, stage size) resident per CU.
+int spmm_blocks_per_cu(int kind, int npad, int R, int K);
 hipError_t launch_reduce(const float* part, uint16_t* C, int S, int64_t NM, hipStream_t s);
 hipError_t launch_decode(int R, const DecodeArgs& a, int grid, hipStream_t s);
 

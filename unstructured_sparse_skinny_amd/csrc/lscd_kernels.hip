@@ -17,7 +17,10 @@
 //  * tall-skinny shapes are split along K across workgroups; fp32 partial sums go to a
 //    workspace and a second kernel adds them in ascending split order (deterministic);
 //  * workgroup ids are remapped so that consecutive work items (the same K split,
-//    hence the same slice of B) land on the same XCD and share its L2.
+//    hence the same slice of B) land on the same XCD and share its L2;
+//  * for N <= 32 a second variant drops the shared B tile and the barrier: each wavefront
+//    of a workgroup takes a quarter of one row block's k range with B in registers, and
+//    the quarters are added through LDS at the end.
 //
 // LDS tile layout (A and B alike): 128-byte rows of 64 fp16, 16-byte chunks XOR-swizzled
 // by (row & 7), so the 16 rows read by one MFMA operand load spread over the banks.
@@ -314,6 +317,181 @@ __global__ __launch_bounds__(kThreads) void spmm_kernel(SpmmArgs a) {
     }
 }
 
+// Per-wavefront B tile (64 k x NPAD n) staged through registers with coalesced loads: lane l
+// of load u takes row n = 8u + (l >> 3), 16-byte chunk (l & 7), so eight consecutive lanes
+// read one contiguous 128-byte row segment.  (Loading straight into the MFMA operand layout
+// would give every lane of a load a different row of B, one cache access per lane.)  The
+// stage is written to the wavefront's own LDS B area right before its MFMAs read it.
+template <int NPAD, bool VEC>
+struct BWave {
+    static constexpr int kPer = NPAD * 8 / 64;
+    u32x4 r[kPer];
+
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rb, const uint16_t* B, int N, int K, int kt, int lane,
+                                         bool valid) {
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) {
+            const int n = 8 * u + (lane >> 3), c = lane & 7;
+            const int k0 = kt * kTileK + c * 8;
+            const bool in = valid && n < N && k0 < K;
+            if constexpr (VEC) {
+                const uint32_t off = in ? (uint32_t)((n * K + k0) * 2) : 0x80000000u;
+                r[u] = __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0);
+            } else {
+                u32x4 v = {0u, 0u, 0u, 0u};
+                if (in) {
+                    const uint16_t* p = B + (size_t)n * K + k0;
+                    uint32_t h[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) h[e] = (k0 + e < K) ? p[e] : 0u;
+                    v[0] = h[0] | (h[1] << 16);
+                    v[1] = h[2] | (h[3] << 16);
+                    v[2] = h[4] | (h[5] << 16);
+                    v[3] = h[6] | (h[7] << 16);
+                }
+                r[u] = v;
+            }
+        }
+    }
+    // rows n >= N are written too (as zeros): the area is private to the wavefront
+    __device__ __forceinline__ void store(unsigned char* Bw, int lane) const {
+#pragma unroll
+        for (int u = 0; u < kPer; ++u)
+            *reinterpret_cast<u32x4*>(Bw + lds_chunk(8 * u + (lane >> 3), lane & 7)) = r[u];
+    }
+};
+
+// Independent-wavefront variant for N <= 32.  A workgroup owns one 64-row block; its
+// wavefronts split the block's k range among themselves and run with no barrier at all:
+// each keeps its own B fragments in registers (loaded straight from global memory, at the
+// same pipeline depth as its packed words) and its own LDS tile, whose writes and reads
+// the LDS executes in the wavefront's program order.  At the end the wavefronts' fp32
+// sums are added through LDS in a fixed wavefront order, so no cross-workgroup partial
+// sums are needed unless the K range is also split across workgroups.
+template <int NPAD, int R, int P, bool VEC, int WK>
+__global__ __launch_bounds__(WK * 64) void spmm_indep_kernel(SpmmArgs a) {
+    static_assert(NPAD * kTileM * 4 <= kTileBytes, "the reduction reuses each wavefront's tile");
+    constexpr int kBBytes = NPAD * kRowBytes;  // the wavefront's B tile
+    __shared__ __attribute__((aligned(16))) unsigned char smem[WK * (kTileBytes + kBBytes)];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    unsigned char* As = smem + wave * kTileBytes;
+    unsigned char* Bw = smem + WK * kTileBytes + wave * kBBytes;
+
+    const int bid = blockIdx.x;
+    const int item = (bid & 7) * a.per_xcd + (bid >> 3);
+    if (item >= a.items) return;
+    const int s = item / a.G;       // G = row blocks here
+    const int rb = item - s * a.G;
+    const int ks0 = (int)(((int64_t)s * a.KT) / a.S);
+    const int ks1 = (int)(((int64_t)(s + 1) * a.KT) / a.S);
+    const int kt0 = ks0 + (wave * (ks1 - ks0)) / WK;
+    const int kt1 = ks0 + ((wave + 1) * (ks1 - ks0)) / WK;
+    const kconst_u32* toff = (const kconst_u32*)(a.offs) + (int64_t)rb * a.KT;
+    const __amdgpu_buffer_rsrc_t bsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)a.B, (short)0, a.N * a.K * 2, kBufWord3);
+    auto off_at = [&](int i) -> uint32_t { return i <= kt1 ? toff[i] : 0u; };
+
+    u32x4 wb[P][R];
+    BWave<NPAD, VEC> bf[P];
+    int nv[P];
+    uint32_t first[P];
+#pragma unroll
+    for (int q = 0; q < P; ++q) {
+        const int k = kt0 + q;
+        uint32_t o0 = 0, o1 = 0;
+        if (k < kt1) {
+            o0 = toff[k];
+            o1 = toff[k + 1];
+        }
+        first[q] = o0;
+        nv[q] = (int)((o1 - o0) >> 2);
+        bf[q].load(bsrc, a.B, a.N, a.K, k, lane, k < kt1);
+        load_tile<R>(wb[q], a.words, o0, nv[q], lane);
+    }
+    uint32_t o_next = off_at(kt0 + P);
+    uint32_t o_pf = off_at(kt0 + P + 1);
+
+    f32x4 acc[4][NPAD / 16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < NPAD / 16; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    for (int kt = kt0; kt < kt1; kt += P) {
+#pragma unroll
+        for (int q = 0; q < P; ++q) {
+            const int k = kt + q;
+            const int kn = k + P;
+            const uint32_t o_pf2 = off_at(kn + 2);
+            const int n = nv[q];
+            if (n > 0) {
+                zero_tile(As, lane);
+                scatter_tile<R>(wb[q], n, As, a.words + first[q], lane);
+                bf[q].store(Bw, lane);
+                mma_tile<NPAD>(acc, As, Bw, lane);
+            }
+            uint32_t o0 = 0, o1 = 0;
+            if (kn < kt1) {
+                o0 = o_next;
+                o1 = o_pf;
+            }
+            o_next = o_pf;
+            o_pf = o_pf2;
+            first[q] = o0;
+            nv[q] = (int)((o1 - o0) >> 2);
+            bf[q].load(bsrc, a.B, a.N, a.K, kn, lane, kn < kt1);
+            load_tile<R>(wb[q], a.words, o0, nv[q], lane);
+        }
+    }
+
+    // Sum the wavefronts' results: each dumps its fp32 block as [NPAD][64] into its own tile,
+    // then every (n, 4 rows) item is added over wavefronts 0, 1, ..., WK-1 in that order.
+    float* red = reinterpret_cast<float*>(As);
+    const int ncol = lane & 15;
+    const int mq = (lane >> 4) * 4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < NPAD / 16; ++j)
+            *reinterpret_cast<f32x4*>(red + (j * 16 + ncol) * kTileM + i * 16 + mq) = acc[i][j];
+    __syncthreads();
+    const bool vec_m = (a.M & 3) == 0;
+    for (int it = tid; it < a.N * (kTileM / 4); it += WK * 64) {
+        const int n = it / (kTileM / 4);
+        const int ml = (it - n * (kTileM / 4)) * 4;
+        f32x4 sum = *reinterpret_cast<const f32x4*>(smem + (n * kTileM + ml) * 4);
+#pragma unroll
+        for (int w = 1; w < WK; ++w)
+            sum += *reinterpret_cast<const f32x4*>(smem + w * kTileBytes + (n * kTileM + ml) * 4);
+        const int m = rb * kTileM + ml;
+        if (m >= a.M) continue;
+        if (a.S == 1) {
+            uint16_t* dst = a.C + (int64_t)n * a.M + m;
+            if (vec_m) {
+                uint2 pk;
+                pk.x = (uint32_t)f16_bits(sum[0]) | ((uint32_t)f16_bits(sum[1]) << 16);
+                pk.y = (uint32_t)f16_bits(sum[2]) | ((uint32_t)f16_bits(sum[3]) << 16);
+                *reinterpret_cast<uint2*>(dst) = pk;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (m + e < a.M) dst[e] = f16_bits(sum[e]);
+            }
+        } else {
+            float* dst = a.part + ((int64_t)s * a.N + n) * a.M + m;
+            if (vec_m) {
+                *reinterpret_cast<f32x4*>(dst) = sum;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (m + e < a.M) dst[e] = sum[e];
+            }
+        }
+    }
+}
+
 // Second pass of split-K: C = fp16( ((P0 + P1) + P2) + ... ), fixed ascending order.  A
 // separate launch: the kernel boundary makes every workgroup's partial sums visible to
 // every XCD without cache write-backs inside the product kernel.
@@ -391,35 +569,55 @@ constexpr int stages() {
     return R <= 4 ? 4 : (R <= 8 ? 3 : 2);
 #endif
 }
-
-// grid < 0: return the kernel's resident workgroups per CU in *occ instead of launching.
-// K % 8 != 0 (rows of B not 16-byte aligned) runs the element-wise B path, instantiated
-// only with the largest register stage.
 template <int NPAD, int R>
-hipError_t launch_spmm_r(const SpmmArgs& a, int grid, hipStream_t st, int* occ) {
-    constexpr int P = stages<R>();
-    if ((a.K & 7) != 0) {
-        if (occ) return hipOccupancyMaxActiveBlocksPerMultiprocessor(occ, spmm_kernel<NPAD, 16, 2, false>, kThreads, 0);
-        hipLaunchKernelGGL((spmm_kernel<NPAD, 16, 2, false>), dim3(grid), dim3(kThreads), 0, st, a);
-        return hipGetLastError();
-    }
-    if (occ) return hipOccupancyMaxActiveBlocksPerMultiprocessor(occ, spmm_kernel<NPAD, R, P, true>, kThreads, 0);
-    hipLaunchKernelGGL((spmm_kernel<NPAD, R, P, true>), dim3(grid), dim3(kThreads), 0, st, a);
+constexpr int stages_indep() {
+#ifdef LSCD_STAGES_INDEP
+    return LSCD_STAGES_INDEP;
+#else
+    return (NPAD == 16 && R <= 4) ? 3 : 2;
+#endif
+}
+
+template <typename Kern>
+hipError_t run(Kern k, const SpmmArgs& a, int grid, hipStream_t st, int* occ, int threads = kThreads) {
+    if (occ) return hipOccupancyMaxActiveBlocksPerMultiprocessor(occ, k, threads, 0);
+    hipLaunchKernelGGL(k, dim3(grid), dim3(threads), 0, st, a);
     return hipGetLastError();
 }
 
+// K % 8 != 0 (rows of B not 16-byte aligned) runs the element-wise B path, instantiated
+// only with the largest register stage.  occ != nullptr: report resident workgroups per CU
+// instead of launching.
+template <int NPAD, int R>
+hipError_t launch_spmm_r(int kind, const SpmmArgs& a, int grid, hipStream_t st, int* occ) {
+    const bool vec = (a.K & 7) == 0;
+    if constexpr (NPAD <= 32) {
+        if (kind == kKernelIndep) {
+            if (!vec) return run(spmm_indep_kernel<NPAD, 16, 2, false, 4>, a, grid, st, occ, 256);
+            return run(spmm_indep_kernel<NPAD, R, stages_indep<NPAD, R>(), true, 4>, a, grid, st, occ, 256);
+        }
+        if (kind == kKernelIndep8) {
+            if (!vec) return run(spmm_indep_kernel<NPAD, 16, 2, false, 8>, a, grid, st, occ, 512);
+            return run(spmm_indep_kernel<NPAD, R, stages_indep<NPAD, R>(), true, 8>, a, grid, st, occ, 512);
+        }
+    }
+    if (kind != kKernelShared) return hipErrorInvalidValue;
+    if (!vec) return run(spmm_kernel<NPAD, 16, 2, false>, a, grid, st, occ);
+    return run(spmm_kernel<NPAD, R, stages<R>(), true>, a, grid, st, occ);
+}
+
 template <int NPAD>
-hipError_t launch_spmm_n(int R, const SpmmArgs& a, int grid, hipStream_t st, int* occ) {
+hipError_t launch_spmm_n(int kind, int R, const SpmmArgs& a, int grid, hipStream_t st, int* occ) {
     switch (R) {
-        case 2: return launch_spmm_r<NPAD, 2>(a, grid, st, occ);
-        case 3: return launch_spmm_r<NPAD, 3>(a, grid, st, occ);
-        case 4: return launch_spmm_r<NPAD, 4>(a, grid, st, occ);
-        case 5: return launch_spmm_r<NPAD, 5>(a, grid, st, occ);
-        case 6: return launch_spmm_r<NPAD, 6>(a, grid, st, occ);
-        case 8: return launch_spmm_r<NPAD, 8>(a, grid, st, occ);
-        case 10: return launch_spmm_r<NPAD, 10>(a, grid, st, occ);
-        case 12: return launch_spmm_r<NPAD, 12>(a, grid, st, occ);
-        case 16: return launch_spmm_r<NPAD, 16>(a, grid, st, occ);
+        case 2: return launch_spmm_r<NPAD, 2>(kind, a, grid, st, occ);
+        case 3: return launch_spmm_r<NPAD, 3>(kind, a, grid, st, occ);
+        case 4: return launch_spmm_r<NPAD, 4>(kind, a, grid, st, occ);
+        case 5: return launch_spmm_r<NPAD, 5>(kind, a, grid, st, occ);
+        case 6: return launch_spmm_r<NPAD, 6>(kind, a, grid, st, occ);
+        case 8: return launch_spmm_r<NPAD, 8>(kind, a, grid, st, occ);
+        case 10: return launch_spmm_r<NPAD, 10>(kind, a, grid, st, occ);
+        case 12: return launch_spmm_r<NPAD, 12>(kind, a, grid, st, occ);
+        case 16: return launch_spmm_r<NPAD, 16>(kind, a, grid, st, occ);
         default: return hipErrorInvalidValue;
     }
 }
@@ -447,24 +645,24 @@ int pick_reg_vectors(int32_t max_tile_words) {
     return best;
 }
 
-hipError_t launch_spmm(int npad, int R, const SpmmArgs& a, int grid, hipStream_t st) {
+hipError_t launch_spmm(int kind, int npad, int R, const SpmmArgs& a, int grid, hipStream_t st) {
     switch (npad) {
-        case 16: return launch_spmm_n<16>(R, a, grid, st, nullptr);
-        case 32: return launch_spmm_n<32>(R, a, grid, st, nullptr);
-        case 64: return launch_spmm_n<64>(R, a, grid, st, nullptr);
+        case 16: return launch_spmm_n<16>(kind, R, a, grid, st, nullptr);
+        case 32: return launch_spmm_n<32>(kind, R, a, grid, st, nullptr);
+        case 64: return launch_spmm_n<64>(kind, R, a, grid, st, nullptr);
         default: return hipErrorInvalidValue;
     }
 }
 
-int spmm_blocks_per_cu(int npad, int R, int K) {
+int spmm_blocks_per_cu(int kind, int npad, int R, int K) {
     int occ = 0;
     SpmmArgs dummy{};
     dummy.K = K;
     hipError_t e = hipErrorInvalidValue;
     switch (npad) {
-        case 16: e = launch_spmm_n<16>(R, dummy, 0, nullptr, &occ); break;
-        case 32: e = launch_spmm_n<32>(R, dummy, 0, nullptr, &occ); break;
-        case 64: e = launch_spmm_n<64>(R, dummy, 0, nullptr, &occ); break;
+        case 16: e = launch_spmm_n<16>(kind, R, dummy, 0, nullptr, &occ); break;
+        case 32: e = launch_spmm_n<32>(kind, R, dummy, 0, nullptr, &occ); break;
+        case 64: e = launch_spmm_n<64>(kind, R, dummy, 0, nullptr, &occ); break;
     }
     return (e == hipSuccess && occ > 0) ? occ : 1;
 }
