@@ -49,6 +49,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU baseline sample budget")
     ap.add_argument("--eager", action="store_true",
                     help="time eager calls with an event pair around each (default: one HIP graph replay)")
+    ap.add_argument("--sweep-n", default=None, metavar="N1,N2,...",
+                    help="instead of the benchmark line: time the sparse product, the dense GEMM and "
+                         "lscd_linear (cost-model choice) for each N on the config's matrix, one JSON line each")
     ap.add_argument("--calibrate", action="store_true",
                     help="only run a plain 1 GiB device copy (scale for the HBM byte counters)")
     return ap.parse_args()
@@ -158,6 +161,41 @@ def cpu_baseline(case, alg_bytes, flops, budget_s):
                       f"fp64 numpy/BLAS product of the masked rows; bytes and flops scaled by rows computed / M"}
 
 
+def sweep_n(args, case, L, torch, np):
+    """N sweep to the dense crossover: sparse (lscd_spmm), dense (torch.mm -> hipBLASLt) and
+    lscd_linear on the attached dense copy, for every N of --sweep-n."""
+    M, K = case.M, case.K
+    words, offs = L.lscd_pack(case.A16, case.mask)
+    h0 = L.lscd_import(words, offs, M, K)
+    info = h0.info
+    copies = max(1, min(8, math.ceil(3 * MALL_BYTES / info["format_bytes"])))
+    hs = [h0] + [L.lscd_import(words, offs, M, K) for _ in range(copies - 1)]
+    del words, offs
+    Ad = torch.from_numpy(np.where(case.mask.astype(bool), case.A16, 0).astype(np.uint16).view(np.float16))
+    dcopies = max(1, min(4, math.ceil(3 * MALL_BYTES / (2 * M * K))))
+    Ads = [Ad.to("cuda") for _ in range(dcopies)]
+    del Ad
+    L.lscd_attach_dense(h0)
+    gen = torch.Generator().manual_seed(1234)
+    last_sparse_win = None
+    for N in [int(x) for x in args.sweep_n.split(",")]:
+        B = torch.randn(N, K, generator=gen).half().to("cuda")
+        C = torch.empty(N, M, dtype=torch.float16, device="cuda")
+        _, ts, *_ = time_calls([(L.lscd_spmm, (h, B, C)) for h in hs], args.steps, args.warmup, torch)
+        _, td, *_ = time_calls([(torch.mm, (B, a.t())) for a in Ads], args.steps, args.warmup, torch)
+        _, tl, *_ = time_calls([(L.lscd_linear, (h0, B, C))], args.steps, args.warmup, torch, graph=False)
+        ms, md = L.lscd_linear_model(M, K, info["nnz_padded"], info["num_tiles"], N)
+        if ts < td:
+            last_sparse_win = N
+        print(json.dumps({"sweep": "n", "workload": case.name, "M": M, "K": K, "N": N,
+                          "sparsity": round(case.sparsity, 4), "sparse_us": round(ts * 1e3, 1),
+                          "dense_hipblaslt_us": round(td * 1e3, 1), "linear_us": round(tl * 1e3, 1),
+                          "linear_path": ["sparse", "dense"][L.lscd_linear_path(h0, N)],
+                          "model_sparse_us": round(ms, 1), "model_dense_us": round(md, 1),
+                          "sparse_tflops": round(2 * M * N * K / (ts * 1e-3) / 1e12, 1)}), flush=True)
+    print(json.dumps({"sweep": "n", "workload": case.name, "largest_n_sparse_wins": last_sparse_win}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -181,6 +219,9 @@ def main():
     M, K, N = case.M, case.K, case.N
     log(f"[bench] {case.name}: M={M} K={K} N={N} sparsity={case.sparsity:.4f} "
         f"(generated in {time.perf_counter() - t_gen:.1f}s)")
+    if args.sweep_n:
+        sweep_n(args, case, L, torch, np)
+        return
 
     t_enc = time.perf_counter()
     words, offs = L.lscd_pack(case.A16, case.mask)

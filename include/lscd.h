@@ -67,11 +67,15 @@ typedef struct {
                                    16, 32 and 64 (1: no second pass)                        */
     int32_t variant[3];         /* product kernel variant for N padded to 16, 32, 64:
                                    0 shared B tile, 1 / 2 independent wavefronts (4 / 8)    */
+    int32_t splits_wide[3];     /* K-splits for N > 64, per launch of N padded to 128, 192,
+                                   256 (N > 256 runs one launch per 256 columns)            */
+    int32_t reg_vectors_wide;   /* 128-bit staging registers per thread, N > 64 kernel      */
 } lscd_info_t;
 
 #define LSCD_DEFAULT_TILE_M 64
 #define LSCD_DEFAULT_TILE_K 64
-#define LSCD_MAX_N 64
+#define LSCD_NARROW_MAX_N 64   /* largest N of the skinny kernels (one launch)               */
+#define LSCD_MAX_N 65535       /* largest N lscd_spmm accepts                                 */
 
 /*
  * lscd_pack_size -- host only, no GPU needed.  Sizes of the encoding of (A, mask).
@@ -133,7 +137,10 @@ lscd_status_t lscd_get_info(lscd_handle_t h, lscd_info_t* info);
  * lscd_spmm -- C = A x B on `stream` (a hipStream_t; NULL = the null stream).
  *   B  device, N x K fp16 row-major, 16-byte aligned, read only.
  *   C  device, N x M fp16 row-major, 16-byte aligned, fully overwritten.
- *   N  0 is a no-op; 1..64 supported; > 64 returns NOT_SUPPORTED.
+ *   N  0 is a no-op; 1..LSCD_MAX_N.  Up to 64 columns run in one launch of the skinny
+ *      kernels; above that, launches of up to 256 columns each, whose wavefronts share each
+ *      decoded A tile (the packed words are read once per launch).  N > LSCD_MAX_N returns
+ *      NOT_SUPPORTED, as does a launch whose 256 x K slice of B reaches 2^31 bytes.
  * Asynchronous: returns after enqueueing; launch failures return LSCD_ERROR_HIP.  No
  * allocation or synchronisation inside.  The current device must be the handle's
  * device (INVALID_VALUE otherwise).  Accumulation is fp32, C is rounded once to fp16
@@ -149,6 +156,45 @@ lscd_status_t lscd_spmm(lscd_handle_t h, const void* B, void* C, int32_t N, void
  * multiplies.  Asynchronous like lscd_spmm.
  */
 lscd_status_t lscd_debug_decode(lscd_handle_t h, void* A_dense, void* stream);
+
+/*
+ * Dense / sparse selection (Flash-LLM review, section 5 "FasterTransformer integration": the
+ * GEMM wrapper picks the dense or the sparse MatMul per call; section 6: the sparse kernel
+ * wins while N is small and the product memory-bound, the dense GEMM once N is large).
+ *
+ * lscd_attach_dense -- decode the handle's encoding into a dense M x K fp16 copy owned by
+ * the handle (current device = the handle's) and create the dense GEMM library handle.
+ * Synchronous; allocates M*K*2 device bytes; a second call is a no-op.  Freed by
+ * lscd_destroy.  NOT_SUPPORTED for tile shapes the kernels are not built for.
+ */
+lscd_status_t lscd_attach_dense(lscd_handle_t h);
+
+/*
+ * lscd_linear -- C = A x B like lscd_spmm (same B, C layouts, alignment and errors), run as
+ * the sparse product or, when a dense copy is attached and lscd_linear_path says so, as a
+ * rocBLAS fp16 GEMM with fp32 accumulation and one fp16 rounding.  Asynchronous on
+ * `stream`.  The dense path may allocate inside the GEMM library on its first call.
+ */
+lscd_status_t lscd_linear(lscd_handle_t h, const void* B, void* C, int32_t N, void* stream);
+
+/* lscd_linear_path -- the path lscd_linear takes for N: *path = 0 sparse, 1 dense (dense
+ * only with a dense copy attached).  No device work. */
+lscd_status_t lscd_linear_path(lscd_handle_t h, int32_t N, int32_t* path);
+
+/* lscd_set_linear_crossover -- fix the choice: sparse iff N <= n_max_sparse; -1 returns
+ * to the cost model (the default). */
+lscd_status_t lscd_set_linear_crossover(lscd_handle_t h, int32_t n_max_sparse);
+
+/*
+ * lscd_linear_model -- host only.  The cost model behind lscd_linear_path: predicted times
+ * (microseconds, MI355X) of the sparse product and of the dense GEMM for an encoding of
+ * nnz_padded words in num_tiles tiles of an M x K matrix, times B of N columns.  The sparse
+ * estimate counts one read of the packed words per launch of <= 256 columns, B and C once,
+ * and the MFMA work of N padded to the kernel width; the dense one counts the fp16 matrix,
+ * B and C, and 2*M*N*K flops.
+ */
+lscd_status_t lscd_linear_model(int64_t M, int64_t K, int64_t nnz_padded, int64_t num_tiles, int32_t N,
+                                double* t_sparse_us, double* t_dense_us);
 
 /* lscd_destroy -- free the handle and its device buffers; NULL is a no-op.  The caller
  * must make sure no work using the handle is still running. */

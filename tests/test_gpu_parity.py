@@ -149,9 +149,9 @@ def test_edge_cases():
     # N = 0 is a no-op success
     assert L._lib.lscd_spmm(L.ctypes.c_void_p(h.ptr), L.ctypes.c_void_p(B.data_ptr()),
                             L.ctypes.c_void_p(C.data_ptr()), 0, None) == L.LSCD_SUCCESS
-    # N > 64 not supported; misaligned pointers rejected
+    # N above LSCD_MAX_N not supported; misaligned pointers rejected
     assert L._lib.lscd_spmm(L.ctypes.c_void_p(h.ptr), L.ctypes.c_void_p(B.data_ptr()),
-                            L.ctypes.c_void_p(C.data_ptr()), 65, None) == L.LSCD_ERROR_NOT_SUPPORTED
+                            L.ctypes.c_void_p(C.data_ptr()), L.LSCD_MAX_N + 1, None) == L.LSCD_ERROR_NOT_SUPPORTED
     assert L._lib.lscd_spmm(L.ctypes.c_void_p(h.ptr), L.ctypes.c_void_p(B.data_ptr() + 2),
                             L.ctypes.c_void_p(C.data_ptr()), 16, None) == L.LSCD_ERROR_INVALID_VALUE
     torch.cuda.synchronize()

@@ -1,0 +1,106 @@
+"""GPU parity of the N > 64 path (wide kernel, launches of <= 256 columns) and of lscd_linear.
+
+* integer-valued inputs: bit-exact against fp16_rne of the oracle for N across the padding
+  boundaries (65 .. 520, several launches and a skinny last slice), with forced K splits;
+* Gaussian inputs: the tolerance gates (tests/_util.py) on ragged shapes and, with sampled
+  rows, at the full OPT-175B MLP2 shape;
+* lscd_linear: the dense path (rocBLAS GEMM on the decoded copy) and the sparse path both
+  match the oracle; the path follows lscd_set_linear_crossover.
+"""
+import numpy as np
+import pytest
+
+import lscd_synth as syn
+from oracle import spmm as osp
+from tests._util import assert_gates, env, say
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import unstructured_sparse_skinny_amd as L
+
+
+def run(fn, h, B16, M):
+    B = torch.from_numpy(np.ascontiguousarray(B16).view(np.float16)).to("cuda")
+    C = torch.full((B16.shape[0], M), float("nan"), dtype=torch.float16, device="cuda")
+    fn(h, B, C)
+    torch.cuda.synchronize()
+    return C.cpu().numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("N", [65, 96, 128, 129, 192, 200, 256, 257, 300, 520])
+@pytest.mark.parametrize("splits", [None, "1", "3"])
+def test_wide_integer_bit_exact(N, splits):
+    case = syn.random_case(333, 1000, N, 0.35, seed=1000 + N, values="int3")
+    with env(LSCD_SPLITK=splits):
+        h = L.lscd_encode(case.A16, case.mask)
+    say(f"wide int N={N} splits_wide={h.info['splits_wide']} Rw={h.info['reg_vectors_wide']}")
+    C = run(L.lscd_spmm, h, case.B16, case.M)
+    C64 = osp.spmm_f64(case.A16, case.mask, case.B16)
+    assert np.abs(C64).max() < 2048
+    assert np.array_equal(C, osp.fp16_rne(C64))
+
+
+@pytest.mark.parametrize("M,K,keep", [(64, 64, 0.3), (300, 520, 0.3), (1000, 1111, 0.25), (65, 70, 0.6),
+                                      (257, 3000, 0.4), (200, 300, 1.0)])
+@pytest.mark.parametrize("N", [80, 128, 256, 384])
+def test_wide_gaussian_within_tolerance(M, K, keep, N):
+    case = syn.random_case(M, K, N, keep, seed=M + K + N)
+    h = L.lscd_encode(case.A16, case.mask)
+    say(f"wide gauss M={M} K={K} N={N}")
+    C = run(L.lscd_spmm, h, case.B16, M)
+    assert_gates(C, osp.spmm_f64(case.A16, case.mask, case.B16), f"M={M} K={K} N={N}")
+
+
+def test_wide_full_size_sampled_rows():
+    case = syn.make_config(4)
+    h = L.lscd_encode(case.A16, case.mask)
+    rng = np.random.default_rng(3)
+    rows = np.array(sorted(set(range(64)) | set(range(case.M - 64, case.M)) |
+                           set(rng.choice(case.M, 128, replace=False).tolist())), dtype=np.int64)
+    for N in (128, 256):
+        B16 = syn.make_config(4, N=N).B16
+        say(f"wide full {case.name} N={N} splits_wide={h.info['splits_wide']}")
+        C = run(L.lscd_spmm, h, B16, case.M)
+        assert np.isfinite(C.view(np.float16)).all()
+        assert_gates(C[:, rows], osp.spmm_f64(case.A16, case.mask, B16, rows=rows), f"N={N}")
+
+
+def test_linear_paths():
+    case = syn.random_case(500, 900, 96, 0.3, seed=21, values="int3")
+    h = L.lscd_encode(case.A16, case.mask)
+    C64 = osp.spmm_f64(case.A16, case.mask, case.B16)
+    want = osp.fp16_rne(C64)
+    assert L.lscd_linear_path(h, 96) == 0                       # no dense copy yet: sparse
+    assert np.array_equal(run(L.lscd_linear, h, case.B16, case.M), want)
+    L.lscd_attach_dense(h)
+    L.lscd_attach_dense(h)                                      # idempotent
+    L.lscd_set_linear_crossover(h, 0)                           # always dense
+    assert L.lscd_linear_path(h, 96) == 1
+    say("linear dense path")
+    # integer inputs: fp32 accumulation is exact in any order, so the GEMM is bit-exact too
+    assert np.array_equal(run(L.lscd_linear, h, case.B16, case.M), want)
+    L.lscd_set_linear_crossover(h, 1 << 20)                     # always sparse
+    assert L.lscd_linear_path(h, 96) == 0
+    assert np.array_equal(run(L.lscd_linear, h, case.B16, case.M), want)
+    L.lscd_set_linear_crossover(h, -1)                          # back to the cost model
+    g = syn.random_case(500, 900, 300, 0.3, seed=22)
+    hg = L.lscd_encode(g.A16, g.mask)
+    L.lscd_attach_dense(hg)
+    for N, cross in ((300, 0), (300, 1 << 20), (16, 0)):
+        L.lscd_set_linear_crossover(hg, cross)
+        B16 = g.B16[:N]
+        say(f"linear gauss N={N} path={L.lscd_linear_path(hg, N)}")
+        assert_gates(run(L.lscd_linear, hg, B16, g.M), osp.spmm_f64(g.A16, g.mask, B16), f"linear N={N}")
+
+
+def test_wide_limits():
+    case = syn.random_case(130, 200, 8, 0.3, seed=13)
+    h = L.lscd_encode(case.A16, case.mask)
+    B = torch.zeros((1, 200), dtype=torch.float16, device="cuda")
+    C = torch.zeros((1, 130), dtype=torch.float16, device="cuda")
+    st = L._lib.lscd_spmm(L.ctypes.c_void_p(h.ptr), L.ctypes.c_void_p(B.data_ptr()),
+                          L.ctypes.c_void_p(C.data_ptr()), L.LSCD_MAX_N + 1, None)
+    assert st == L.LSCD_ERROR_NOT_SUPPORTED
+    torch.cuda.synchronize()

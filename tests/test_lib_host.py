@@ -148,3 +148,30 @@ def test_argument_errors_are_statuses():
     assert L._lib.lscd_spmm(None, None, None, 16, None) == L.LSCD_ERROR_INVALID_VALUE
     assert L._lib.lscd_destroy(None) == L.LSCD_SUCCESS
     assert L._lib.lscd_get_info(None, None) == L.LSCD_ERROR_INVALID_VALUE
+
+
+def test_linear_cost_model():
+    """The selection model: sparse for skinny N at high sparsity, dense once N is large or the
+    matrix is nearly dense; both estimates grow with N within each kernel regime, the sparse
+    one with the stored words."""
+    M, K = 12288, 12288
+    T = (M // 64) * (K // 64)
+    for keep, small_n_sparse in ((0.2, True), (0.5, None), (1.0, False)):
+        nw = int(keep * M * K)
+        ts, td = L.lscd_linear_model(M, K, nw, T, 8)
+        if small_n_sparse is not None:
+            assert (ts < td) == small_n_sparse, (keep, ts, td)
+        ts_big, td_big = L.lscd_linear_model(M, K, nw, T, 4096)
+        assert td_big < ts_big, keep                       # compute-bound: dense wins
+        for regime in ((1, 8, 16, 32, 64), (65, 128, 256, 257, 1024)):   # skinny kernels / wide kernel
+            prev = (0.0, 0.0)
+            for N in regime:
+                cur = L.lscd_linear_model(M, K, nw, T, N)
+                assert cur[0] >= prev[0] and cur[1] >= prev[1], (keep, N)
+                prev = cur
+    a = L.lscd_linear_model(M, K, 10_000_000, T, 16)[0]
+    b = L.lscd_linear_model(M, K, 20_000_000, T, 16)[0]
+    assert b > a
+    for bad in ((0, K, 0, T, 8), (M, K, -1, T, 8), (M, K, 0, T, 0)):
+        with pytest.raises(L.LSCDError):
+            L.lscd_linear_model(*bad)

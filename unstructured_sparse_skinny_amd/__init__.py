@@ -28,11 +28,14 @@ LSCD_ERROR_INVALID_FORMAT = 4
 LSCD_ERROR_HIP = 5
 LSCD_DEFAULT_TILE_M = 64
 LSCD_DEFAULT_TILE_K = 64
-LSCD_MAX_N = 64
+LSCD_NARROW_MAX_N = 64
+LSCD_MAX_N = 65535
 
 #: Every entry point include/lscd.h declares.
 EXPORTS = ("lscd_pack_size", "lscd_pack", "lscd_encode", "lscd_encode_tiled", "lscd_import", "lscd_export",
-           "lscd_get_info", "lscd_spmm", "lscd_debug_decode", "lscd_destroy", "lscd_status_string")
+           "lscd_get_info", "lscd_spmm", "lscd_debug_decode", "lscd_attach_dense", "lscd_linear",
+           "lscd_linear_path", "lscd_set_linear_crossover", "lscd_linear_model", "lscd_destroy",
+           "lscd_status_string")
 
 
 class lscd_info_t(ctypes.Structure):
@@ -41,7 +44,8 @@ class lscd_info_t(ctypes.Structure):
                 ("nnz_padded", ctypes.c_int64), ("format_bytes", ctypes.c_int64),
                 ("max_tile_words", ctypes.c_int32), ("device", ctypes.c_int32),
                 ("workspace_bytes", ctypes.c_int64), ("reg_vectors", ctypes.c_int32),
-                ("splits", ctypes.c_int32 * 3), ("variant", ctypes.c_int32 * 3)]
+                ("splits", ctypes.c_int32 * 3), ("variant", ctypes.c_int32 * 3),
+                ("splits_wide", ctypes.c_int32 * 3), ("reg_vectors_wide", ctypes.c_int32)]
 
 
 class LSCDError(RuntimeError):
@@ -66,6 +70,11 @@ def _load():
         "lscd_get_info": [VP, P(lscd_info_t)],
         "lscd_spmm": [VP, VP, VP, I32, VP],
         "lscd_debug_decode": [VP, VP, VP],
+        "lscd_attach_dense": [VP],
+        "lscd_linear": [VP, VP, VP, I32, VP],
+        "lscd_linear_path": [VP, I32, P(I32)],
+        "lscd_set_linear_crossover": [VP, I32],
+        "lscd_linear_model": [I64, I64, I64, I64, I32, P(ctypes.c_double), P(ctypes.c_double)],
         "lscd_destroy": [VP],
     }
     for name, args in sig.items():
@@ -99,7 +108,7 @@ class Handle:
         self.close()
 
     def close(self):
-        if getattr(self, "ptr", None):
+        if getattr(self, "ptr", None) and _lib is not None:   # _lib is None during interpreter teardown
             _lib.lscd_destroy(ctypes.c_void_p(self.ptr))
             self.ptr = None
 
@@ -182,6 +191,7 @@ def lscd_get_info(h: Handle) -> dict:
     _check(_lib.lscd_get_info(ctypes.c_void_p(h.ptr), ctypes.byref(info)), "lscd_get_info")
     out = {name: getattr(info, name) for name, _ in lscd_info_t._fields_}
     out["splits"], out["variant"] = list(info.splits), list(info.variant)
+    out["splits_wide"] = list(info.splits_wide)
     return out
 
 
@@ -206,6 +216,38 @@ def lscd_spmm(h: Handle, B, C, stream=None):
     pc = _device_fp16(C, "C", (N, info["M"]))
     _check(_lib.lscd_spmm(ctypes.c_void_p(h.ptr), pb, pc, N, _stream(stream)), "lscd_spmm")
     return C
+
+
+def lscd_attach_dense(h: Handle):
+    _check(_lib.lscd_attach_dense(ctypes.c_void_p(h.ptr)), "lscd_attach_dense")
+
+
+def lscd_linear(h: Handle, B, C, stream=None):
+    """lscd_spmm, or the dense GEMM on the attached dense copy when lscd_linear_path says so."""
+    info = lscd_get_info(h)
+    N = int(B.shape[0]) if isinstance(B, torch.Tensor) and B.dim() == 2 else -1
+    pb = _device_fp16(B, "B", (N, info["K"]))
+    pc = _device_fp16(C, "C", (N, info["M"]))
+    _check(_lib.lscd_linear(ctypes.c_void_p(h.ptr), pb, pc, N, _stream(stream)), "lscd_linear")
+    return C
+
+
+def lscd_linear_path(h: Handle, N: int) -> int:
+    p = ctypes.c_int32()
+    _check(_lib.lscd_linear_path(ctypes.c_void_p(h.ptr), N, ctypes.byref(p)), "lscd_linear_path")
+    return p.value
+
+
+def lscd_set_linear_crossover(h: Handle, n_max_sparse: int):
+    _check(_lib.lscd_set_linear_crossover(ctypes.c_void_p(h.ptr), n_max_sparse), "lscd_set_linear_crossover")
+
+
+def lscd_linear_model(M: int, K: int, nnz_padded: int, num_tiles: int, N: int):
+    """(t_sparse_us, t_dense_us) predicted by the selection cost model (host only)."""
+    ts, td = ctypes.c_double(), ctypes.c_double()
+    _check(_lib.lscd_linear_model(M, K, nnz_padded, num_tiles, N, ctypes.byref(ts), ctypes.byref(td)),
+           "lscd_linear_model")
+    return ts.value, td.value
 
 
 def lscd_debug_decode(h: Handle, A_dense, stream=None):

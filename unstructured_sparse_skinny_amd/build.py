@@ -19,7 +19,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "liblscd.so")
 BUILD_DIR = os.path.join(HERE, "_build")
-SOURCES = ["csrc/lscd_api.cpp", "csrc/lscd_pack.cpp", "csrc/lscd_kernels.hip"]
+SOURCES = ["csrc/lscd_api.cpp", "csrc/lscd_linear.cpp", "csrc/lscd_pack.cpp", "csrc/lscd_kernels.hip"]
 ARCH = os.environ.get("LSCD_OFFLOAD_ARCH", "gfx950")
 
 
@@ -65,7 +65,11 @@ def build(verbose: bool = False, pkg_dir: str = HERE, defines=()) -> str:
     with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
         objs = list(ex.map(compile_one, SOURCES))
     tmp = lib + ".tmp"
-    cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-pthread", *objs, "-o", tmp]
+    rocm_lib = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "lib")
+    # rocBLAS (dense path of lscd_linear): when torch is loaded first, its copy (same soname)
+    # is the one bound.
+    cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-pthread", *objs, "-L", rocm_lib, "-lrocblas",
+           "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")

@@ -10,21 +10,6 @@
 
 #include "lscd_internal.h"
 
-struct lscd_handle_s {
-    lscd::Grid g;
-    int device = 0;
-    int cus = 256;
-    int64_t nnz = 0;
-    int64_t nnz_padded = 0;
-    int32_t max_tile_words = 0;
-    int R = 2;
-    int S[3] = {1, 1, 1};     // K splits used by lscd_spmm for N padded to 16, 32, 64
-    int kind[3] = {0, 0, 0};  // product kernel variant for N padded to 16, 32, 64
-    uint32_t* d_words = nullptr;
-    uint32_t* d_offs = nullptr;
-    float* d_part = nullptr;
-    int64_t part_bytes = 0;
-};
 
 namespace {
 
@@ -41,6 +26,7 @@ void free_handle(lscd_handle_s* h) {
     if (h->d_words) (void)hipFree(h->d_words);
     if (h->d_offs) (void)hipFree(h->d_offs);
     if (h->d_part) (void)hipFree(h->d_part);
+    lscd::release_dense(h);
     delete h;
 }
 
@@ -101,14 +87,21 @@ lscd_status_t make_handle(const uint32_t* words, int64_t nwords, const uint32_t*
         h->cus = cus;
     h->R = lscd::pick_reg_vectors(maxw);
     const bool kernel_tile = g.tm == lscd::kTileM && g.tk == lscd::kTileK;
-    int max_s = 1;
+    int64_t part = 0;
     for (int i = 0; i < 3 && kernel_tile; ++i) {
         h->kind[i] = pick_kind(16 << i);
         const int occ = lscd::spmm_blocks_per_cu(h->kind[i], 16 << i, h->R, (int)std::min<int64_t>(g.K, 1 << 30));
         const int min_tiles = h->kind[i] == lscd::kKernelIndep ? 8 : (h->kind[i] == lscd::kKernelIndep8 ? 16 : 2);
         h->S[i] = plan_splits(g, h->cus, occ, row_groups(g, h->kind[i]), min_tiles,
                               h->kind[i] != lscd::kKernelShared);
-        max_s = std::max(max_s, h->S[i]);
+        if (h->S[i] > 1) part = std::max<int64_t>(part, (int64_t)h->S[i] * g.M * (16 << i) * 4);
+    }
+    h->Rw = lscd::pick_reg_vectors_wide(maxw);
+    for (int i = 0; i < 3 && kernel_tile; ++i) {
+        const int npad = 128 + 64 * i;
+        const int occ = lscd::spmm_blocks_per_cu(lscd::kKernelWide, npad, h->Rw, (int)std::min<int64_t>(g.K, 1 << 30));
+        h->Sw[i] = plan_splits(g, h->cus, occ, g.MB, 4, false);
+        if (h->Sw[i] > 1) part = std::max<int64_t>(part, (int64_t)h->Sw[i] * g.M * npad * 4);
     }
     if (getenv("LSCD_TEST_FAIL_ALLOC")) {
         free_handle(h);
@@ -120,8 +113,8 @@ lscd_status_t make_handle(const uint32_t* words, int64_t nwords, const uint32_t*
         free_handle(h);
         return hip_status(e);
     }
-    if (max_s > 1) {
-        h->part_bytes = (int64_t)max_s * g.M * LSCD_MAX_N * 4;
+    if (part > 0) {
+        h->part_bytes = part;
         if ((e = hipMalloc((void**)&h->d_part, (size_t)h->part_bytes)) != hipSuccess) {
             free_handle(h);
             return hip_status(e);
@@ -284,7 +277,9 @@ lscd_status_t lscd_get_info(lscd_handle_t h, lscd_info_t* info) {
     for (int i = 0; i < 3; ++i) {
         info->splits[i] = h->S[i];
         info->variant[i] = h->kind[i];
+        info->splits_wide[i] = h->Sw[i];
     }
+    info->reg_vectors_wide = h->Rw;
     return LSCD_SUCCESS;
 }
 
@@ -294,33 +289,49 @@ lscd_status_t lscd_spmm(lscd_handle_t h, const void* B, void* C, int32_t N, void
     if (!B || !C || !aligned16(B) || !aligned16(C)) return LSCD_ERROR_INVALID_VALUE;
     if (N > LSCD_MAX_N) return LSCD_ERROR_NOT_SUPPORTED;
     if (h->g.tm != lscd::kTileM || h->g.tk != lscd::kTileK) return LSCD_ERROR_NOT_SUPPORTED;
-    if ((int64_t)N * h->g.K * 2 >= ((int64_t)1 << 31)) return LSCD_ERROR_NOT_SUPPORTED;  // B as one buffer
+    const int nb = std::min(N, lscd::kWideMaxN);  // columns of B read by one launch
+    if ((int64_t)nb * h->g.K * 2 >= ((int64_t)1 << 31)) return LSCD_ERROR_NOT_SUPPORTED;  // B as one buffer
     lscd_status_t st = check_device(h);
     if (st != LSCD_SUCCESS) return st;
     hipStream_t s = (hipStream_t)stream;
-    const int S = h->S[npad_index(N)];
-    const int kind = h->kind[npad_index(N)];
     lscd::SpmmArgs a;
     a.words = h->d_words;
     a.offs = h->d_offs;
-    a.B = (const uint16_t*)B;
-    a.C = (uint16_t*)C;
     a.part = h->d_part;
     a.M = (int32_t)h->g.M;
     a.K = (int32_t)h->g.K;
-    a.N = N;
     a.MB = (int32_t)h->g.MB;
     a.KT = (int32_t)h->g.KT;
-    a.G = (int32_t)row_groups(h->g, kind);
-    a.S = S;
-    a.items = a.G * a.S;
-    a.per_xcd = (a.items + 7) / 8;
-    const int npad = N <= 16 ? 16 : (N <= 32 ? 32 : 64);
-    hipError_t e = lscd::launch_spmm(kind, npad, h->R, a, 8 * a.per_xcd, s);
-    if (e != hipSuccess) return hip_status(e);
-    if (S > 1) {
-        e = lscd::launch_reduce(h->d_part, (uint16_t*)C, S, (int64_t)N * h->g.M, s);
+    // N <= 64: one launch of a skinny kernel.  N > 64: launches of up to 256 columns of the
+    // wide kernel (the packed words are read once per launch); a last slice of <= 64 columns
+    // goes to the skinny kernels.
+    for (int32_t c0 = 0; c0 < N; c0 += lscd::kWideMaxN) {
+        const int32_t n = std::min(N - c0, lscd::kWideMaxN);
+        int kind, npad, R, S;
+        if (n <= LSCD_NARROW_MAX_N) {
+            kind = h->kind[npad_index(n)];
+            npad = n <= 16 ? 16 : (n <= 32 ? 32 : 64);
+            R = h->R;
+            S = h->S[npad_index(n)];
+        } else {
+            kind = lscd::kKernelWide;
+            npad = n <= 128 ? 128 : (n <= 192 ? 192 : 256);
+            R = h->Rw;
+            S = h->Sw[(npad - 128) / 64];
+        }
+        a.B = (const uint16_t*)B + (int64_t)c0 * h->g.K;
+        a.C = (uint16_t*)C + (int64_t)c0 * h->g.M;
+        a.N = n;
+        a.G = (int32_t)(kind == lscd::kKernelWide ? h->g.MB : row_groups(h->g, kind));
+        a.S = S;
+        a.items = a.G * a.S;
+        a.per_xcd = (a.items + 7) / 8;
+        hipError_t e = lscd::launch_spmm(kind, npad, R, a, 8 * a.per_xcd, s);
         if (e != hipSuccess) return hip_status(e);
+        if (S > 1) {
+            e = lscd::launch_reduce(h->d_part, a.C, S, (int64_t)n * h->g.M, s);
+            if (e != hipSuccess) return hip_status(e);
+        }
     }
     return LSCD_SUCCESS;
 }

@@ -80,10 +80,42 @@ int pick_reg_vectors(int32_t max_tile_words);
 constexpr int kKernelShared = 0;
 constexpr int kKernelIndep = 1;   // 4 wavefronts per row block
 constexpr int kKernelIndep8 = 2;  // 8 wavefronts per row block
+// N > 64: one row block per workgroup, its tile decoded by all four wavefronts, 64 columns
+// of B per wavefront (N padded to 128, 192 or 256 per launch).
+constexpr int kKernelWide = 3;
+constexpr int kWideMaxN = 256;
+// Staging registers per thread and tile of the wide variant (1, 2 or 4).
+int pick_reg_vectors_wide(int32_t max_tile_words);
 hipError_t launch_spmm(int kind, int npad, int R, const SpmmArgs& a, int grid, hipStream_t s);
 // Workgroups of a product kernel (variant, N padding, stage size) resident per CU.
 int spmm_blocks_per_cu(int kind, int npad, int R, int K);
 hipError_t launch_reduce(const float* part, uint16_t* C, int S, int64_t NM, hipStream_t s);
 hipError_t launch_decode(int R, const DecodeArgs& a, int grid, hipStream_t s);
 
+// Frees the dense copy and the GEMM library handle of lscd_linear, if any.
+void release_dense(struct ::lscd_handle_s* h);
+
 }  // namespace lscd
+
+// The object behind lscd_handle_t.
+struct lscd_handle_s {
+    lscd::Grid g;
+    int device = 0;
+    int cus = 256;
+    int64_t nnz = 0;
+    int64_t nnz_padded = 0;
+    int32_t max_tile_words = 0;
+    int R = 2;
+    int S[3] = {1, 1, 1};     // K splits used by lscd_spmm for N padded to 16, 32, 64
+    int kind[3] = {0, 0, 0};  // product kernel variant for N padded to 16, 32, 64
+    int Rw = 1;               // staging vectors per thread of the wide (N > 64) variant
+    int Sw[3] = {1, 1, 1};    // K splits of the wide variant for N padded to 128, 192, 256
+    uint32_t* d_words = nullptr;
+    uint32_t* d_offs = nullptr;
+    float* d_part = nullptr;
+    int64_t part_bytes = 0;
+    // dense path of lscd_linear (lscd_attach_dense)
+    uint16_t* d_dense = nullptr;  // M x K fp16, row-major
+    void* blas = nullptr;         // rocblas_handle
+    int32_t crossover = -1;       // sparse iff N <= crossover; -1: cost model
+};

@@ -19,8 +19,10 @@
 //  * workgroup ids are remapped so that consecutive work items (the same K split,
 //    hence the same slice of B) land on the same XCD and share its L2;
 //  * for N <= 32 a second variant drops the shared B tile and the barrier: each wavefront
-//    of a workgroup takes a quarter of one row block's k range with B in registers, and
-//    the quarters are added through LDS at the end.
+//    of a workgroup takes a quarter of one row block's k range with its own B tile, and
+//    the quarters are added through LDS at the end;
+//  * for N > 64 a third variant decodes each A tile once per workgroup and gives every
+//    wavefront 64 columns of B (up to 256 per launch).
 //
 // LDS tile layout (A and B alike): 128-byte rows of 64 fp16, 16-byte chunks XOR-swizzled
 // by (row & 7), so the 16 rows read by one MFMA operand load spread over the banks.
@@ -100,6 +102,31 @@ __device__ __forceinline__ void scatter_tile(const u32x4 (&wb)[R], int nvec, uns
             put_word(As, x[1]);
             put_word(As, x[2]);
             put_word(As, x[3]);
+        }
+    }
+}
+
+// Workgroup-cooperative forms: thread t of the workgroup takes vectors t, t + 256, ...
+// R * 256 vectors cover the largest 64 x 64 tile (1024 vectors) for R = 4.
+template <int R>
+__device__ __forceinline__ void load_tile_wg(u32x4 (&wb)[R], const uint32_t* words, uint32_t first, int nvec,
+                                             int tid) {
+    __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(words + first), (short)0, nvec * 16, kBufWord3);
+#pragma unroll
+    for (int j = 0; j < R; ++j)
+        wb[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, (j * kThreads + tid) * 16, 0, kStreamPolicy);
+}
+
+template <int R>
+__device__ __forceinline__ void scatter_tile_wg(const u32x4 (&wb)[R], int nvec, unsigned char* As, int tid) {
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+        if (j * kThreads + tid < nvec) {
+            put_word(As, wb[j][0]);
+            put_word(As, wb[j][1]);
+            put_word(As, wb[j][2]);
+            put_word(As, wb[j][3]);
         }
     }
 }
@@ -363,9 +390,9 @@ struct BWave {
 
 // Independent-wavefront variant for N <= 32.  A workgroup owns one 64-row block; its
 // wavefronts split the block's k range among themselves and run with no barrier at all:
-// each keeps its own B fragments in registers (loaded straight from global memory, at the
-// same pipeline depth as its packed words) and its own LDS tile, whose writes and reads
-// the LDS executes in the wavefront's program order.  At the end the wavefronts' fp32
+// each stages its own B tile (coalesced loads at the same pipeline depth as its packed
+// words, then a private LDS area) next to its own LDS A tile, and the LDS executes one
+// wavefront's writes and reads in program order.  At the end the wavefronts' fp32
 // sums are added through LDS in a fixed wavefront order, so no cross-workgroup partial
 // sums are needed unless the K range is also split across workgroups.
 template <int NPAD, int R, int P, bool VEC, int WK>
@@ -487,6 +514,149 @@ __global__ __launch_bounds__(WK * 64) void spmm_indep_kernel(SpmmArgs a) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
                     if (m + e < a.M) dst[e] = sum[e];
+            }
+        }
+    }
+}
+
+// Wide-N variant (64 < N <= 256 per launch).  Above N = 64 one A tile feeds enough MFMA
+// work to keep a whole workgroup busy, so the four wavefronts decode each tile together
+// (each loads, and scatters, a quarter of its words) and wavefront w multiplies it with
+// columns 64w .. 64w + 63 of B.  Three LDS A buffers rotate so that one barrier per k step
+// orders everything: at step k the workgroup zero-fills buffer (k+1) % 3, whose last
+// readers were the MFMAs of step k-2 (all past the barrier of step k-1), and scatters
+// into buffer k % 3, whose zero-fill was done before the barrier of step k-1.
+template <int NW, int R, bool VEC>
+__global__ __launch_bounds__(kThreads) void spmm_wide_kernel(SpmmArgs a) {
+    static_assert(kThreads == 256, "four wavefronts of 64 columns each");
+    constexpr int NPAD = NW * 64;
+    constexpr int P = 2;
+    constexpr int kBBytes = NPAD * kRowBytes;
+    __shared__ __attribute__((aligned(16))) unsigned char smem[3 * kTileBytes + 2 * kBBytes];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    unsigned char* Bs0 = smem + 3 * kTileBytes;
+
+    const int bid = blockIdx.x;
+    const int item = (bid & 7) * a.per_xcd + (bid >> 3);
+    if (item >= a.items) return;
+    const int s = item / a.G;  // G = row blocks
+    const int rb = item - s * a.G;
+    const int kt0 = (int)(((int64_t)s * a.KT) / a.S);
+    const int kt1 = (int)(((int64_t)(s + 1) * a.KT) / a.S);
+    const kconst_u32* toff = (const kconst_u32*)(a.offs) + (int64_t)rb * a.KT;
+    const __amdgpu_buffer_rsrc_t bsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)a.B, (short)0, a.N * a.K * 2, kBufWord3);
+    auto off_at = [&](int i) -> uint32_t { return i <= kt1 ? toff[i] : 0u; };
+
+    // B rows n >= N stay zero in both buffers; A buffer 0 starts zeroed.
+    for (int ch = tid; ch < 2 * NPAD * 8; ch += kThreads) {
+        const int row = ch >> 3;
+        if (row % NPAD >= a.N) {
+            const u32x4 z = {0u, 0u, 0u, 0u};
+            *reinterpret_cast<u32x4*>(Bs0 + row * kRowBytes + (ch & 7) * 16) = z;
+        }
+    }
+    {
+        const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int j = 0; j < kTileBytes / (16 * kThreads); ++j)
+            *reinterpret_cast<u32x4*>(smem + (j * kThreads + tid) * 16) = z;
+    }
+
+    u32x4 wb[P][R];
+    BStage<NPAD, VEC> bst[P];
+    int nv[P];
+#pragma unroll
+    for (int q = 0; q < P; ++q) {
+        const int k = kt0 + q;
+        uint32_t o0 = 0, o1 = 0;
+        if (k < kt1) {
+            o0 = toff[k];
+            o1 = toff[k + 1];
+        }
+        nv[q] = (int)((o1 - o0) >> 2);
+        bst[q].load(bsrc, a.B, a.N, a.K, k, tid, k < kt1);
+        load_tile_wg<R>(wb[q], a.words, o0, nv[q], tid);
+    }
+    uint32_t o_next = off_at(kt0 + P);
+    uint32_t o_pf = off_at(kt0 + P + 1);
+    __syncthreads();
+
+    f32x4 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    int ab = 0;  // A buffer of the current k step
+    for (int kt = kt0; kt < kt1; kt += P) {
+#pragma unroll
+        for (int q = 0; q < P; ++q) {
+            const int k = kt + q;
+            const int kn = k + P;
+            const int an = ab == 2 ? 0 : ab + 1;
+            unsigned char* As = smem + ab * kTileBytes;
+            unsigned char* Bs = Bs0 + (k & 1) * kBBytes;
+            const uint32_t o_pf2 = off_at(kn + 2);
+            {
+                const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+                for (int j = 0; j < kTileBytes / (16 * kThreads); ++j)
+                    *reinterpret_cast<u32x4*>(smem + an * kTileBytes + (j * kThreads + tid) * 16) = z;
+            }
+            bst[q].store(Bs, a.N, tid);
+            const int n = nv[q];
+            scatter_tile_wg<R>(wb[q], n, As, tid);
+            uint32_t o0 = 0, o1 = 0;
+            if (kn < kt1) {
+                o0 = o_next;
+                o1 = o_pf;
+            }
+            o_next = o_pf;
+            o_pf = o_pf2;
+            nv[q] = (int)((o1 - o0) >> 2);
+            bst[q].load(bsrc, a.B, a.N, a.K, kn, tid, kn < kt1);
+            load_tile_wg<R>(wb[q], a.words, o0, nv[q], tid);
+            __syncthreads();
+            if (n > 0 && wave < NW) mma_tile<64>(acc, As, Bs + wave * 64 * kRowBytes, lane);
+            ab = an;
+        }
+    }
+    if (wave >= NW) return;
+    const int ncol = lane & 15;
+    const int mrow = rb * kTileM + (lane >> 4) * 4;
+    const bool vec_m = (a.M & 3) == 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int n = wave * 64 + j * 16 + ncol;
+            const int m = mrow + i * 16;
+            if (n >= a.N || m >= a.M) continue;
+            const f32x4 v = acc[i][j];
+            if (a.S == 1) {
+                uint16_t* dst = a.C + (int64_t)n * a.M + m;
+                if (vec_m && m + 3 < a.M) {
+                    uint2 pk;
+                    pk.x = (uint32_t)f16_bits(v[0]) | ((uint32_t)f16_bits(v[1]) << 16);
+                    pk.y = (uint32_t)f16_bits(v[2]) | ((uint32_t)f16_bits(v[3]) << 16);
+                    *reinterpret_cast<uint2*>(dst) = pk;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (m + e < a.M) dst[e] = f16_bits(v[e]);
+                }
+            } else {
+                float* dst = a.part + ((int64_t)s * a.N + n) * a.M + m;
+                if (vec_m && m + 3 < a.M) {
+                    *reinterpret_cast<f32x4*>(dst) = v;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (m + e < a.M) dst[e] = v[e];
+                }
             }
         }
     }
@@ -622,6 +792,26 @@ hipError_t launch_spmm_n(int kind, int R, const SpmmArgs& a, int grid, hipStream
     }
 }
 
+template <int NW>
+hipError_t launch_wide_nw(int R, const SpmmArgs& a, int grid, hipStream_t st, int* occ) {
+    if ((a.K & 7) != 0) return run(spmm_wide_kernel<NW, 4, false>, a, grid, st, occ);
+    switch (R) {
+        case 1: return run(spmm_wide_kernel<NW, 1, true>, a, grid, st, occ);
+        case 2: return run(spmm_wide_kernel<NW, 2, true>, a, grid, st, occ);
+        case 4: return run(spmm_wide_kernel<NW, 4, true>, a, grid, st, occ);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_wide_any(int npad, int R, const SpmmArgs& a, int grid, hipStream_t st, int* occ) {
+    switch (npad) {
+        case 128: return launch_wide_nw<2>(R, a, grid, st, occ);
+        case 192: return launch_wide_nw<3>(R, a, grid, st, occ);
+        case 256: return launch_wide_nw<4>(R, a, grid, st, occ);
+        default: return hipErrorInvalidValue;
+    }
+}
+
 template <int R>
 hipError_t launch_decode_r(const DecodeArgs& a, int grid, hipStream_t st) {
     hipLaunchKernelGGL((decode_kernel<R>), dim3(grid), dim3(kThreads), 0, st, a);
@@ -645,7 +835,13 @@ int pick_reg_vectors(int32_t max_tile_words) {
     return best;
 }
 
+int pick_reg_vectors_wide(int32_t max_tile_words) {
+    const int need = ((max_tile_words / 4) + kThreads - 1) / kThreads;
+    return need <= 1 ? 1 : (need <= 2 ? 2 : 4);
+}
+
 hipError_t launch_spmm(int kind, int npad, int R, const SpmmArgs& a, int grid, hipStream_t st) {
+    if (kind == kKernelWide) return launch_wide_any(npad, R, a, grid, st, nullptr);
     switch (npad) {
         case 16: return launch_spmm_n<16>(kind, R, a, grid, st, nullptr);
         case 32: return launch_spmm_n<32>(kind, R, a, grid, st, nullptr);
@@ -659,6 +855,7 @@ int spmm_blocks_per_cu(int kind, int npad, int R, int K) {
     SpmmArgs dummy{};
     dummy.K = K;
     hipError_t e = hipErrorInvalidValue;
+    if (kind == kKernelWide) return (launch_wide_any(npad, R, dummy, 0, nullptr, &occ) == hipSuccess && occ > 0) ? occ : 1;
     switch (npad) {
         case 16: e = launch_spmm_n<16>(kind, R, dummy, 0, nullptr, &occ); break;
         case 32: e = launch_spmm_n<32>(kind, R, dummy, 0, nullptr, &occ); break;
