@@ -52,6 +52,9 @@ def parse():
     ap.add_argument("--sweep-n", default=None, metavar="N1,N2,...",
                     help="instead of the benchmark line: time the sparse product, the dense GEMM and "
                          "lscd_linear (cost-model choice) for each N on the config's matrix, one JSON line each")
+    ap.add_argument("--encode", action="store_true",
+                    help="instead of the benchmark line: time the device encoder (lscd_encode_device) and "
+                         "the host encoder (lscd_pack) on the config's matrix, one JSON line")
     ap.add_argument("--calibrate", action="store_true",
                     help="only run a plain 1 GiB device copy (scale for the HBM byte counters)")
     return ap.parse_args()
@@ -196,6 +199,31 @@ def sweep_n(args, case, L, torch, np):
     print(json.dumps({"sweep": "n", "workload": case.name, "largest_n_sparse_wins": last_sparse_win}), flush=True)
 
 
+def bench_encode(args, case, L, torch, np):
+    """Device encoder vs host encoder on the same matrix (dense fp16 + mask in, format out)."""
+    M, K = case.M, case.K
+    Ad = torch.from_numpy(case.A16.view(np.float16)).to("cuda")
+    md = torch.from_numpy(case.mask.astype(np.uint8)).to("cuda")
+    in_bytes = 3 * M * K                                   # fp16 values + mask bytes
+    L.lscd_encode_device(Ad, md).close()                   # warm-up (module load, first allocations)
+    torch.cuda.synchronize()
+    reps = max(3, args.steps // 20)
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        h = L.lscd_encode_device(Ad, md)
+        h.close()
+    t_dev = (time.perf_counter() - t0) / reps
+    t0 = time.perf_counter()
+    words, offs = L.lscd_pack(case.A16, case.mask)
+    t_host = time.perf_counter() - t0
+    print(json.dumps({"encode": "tiled-csl 64x64", "workload": case.name, "M": M, "K": K,
+                      "nnz_padded": int(words.size), "device_ms": round(t_dev * 1e3, 3),
+                      "device_input_gbs": round(in_bytes / t_dev / 1e9, 1), "device_reps": reps,
+                      "host_ms": round(t_host * 1e3, 1), "host_threads": os.cpu_count(),
+                      "speedup": round(t_host / t_dev, 1),
+                      "note": "wall time per synchronous call, allocations included"}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -221,6 +249,9 @@ def main():
         f"(generated in {time.perf_counter() - t_gen:.1f}s)")
     if args.sweep_n:
         sweep_n(args, case, L, torch, np)
+        return
+    if args.encode:
+        bench_encode(args, case, L, torch, np)
         return
 
     t_enc = time.perf_counter()

@@ -116,6 +116,22 @@ lscd_status_t lscd_encode_tiled(const uint16_t* A, const uint8_t* mask, int64_t 
                                 int32_t tile_m, int32_t tile_k, lscd_handle_t* out);
 
 /*
+ * lscd_encode_device -- lscd_encode for a matrix already in device memory: the encoding of
+ * the default 64 x 64 tiles is built by GPU kernels (per-tile counts, a prefix sum of the
+ * padded counts, then a fill that writes every kept entry straight to its slot) and is
+ * word for word the one lscd_encode produces for the same inputs (same bank-aware order
+ * inside each tile).  The pages build the format ahead of time on the host (Flash-LLM
+ * review, section 3); this serves weights that are loaded or re-pruned on the GPU.
+ *   A      device, M*K fp16 row-major, 2-byte aligned; read only.
+ *   mask   device, M*K bytes (nonzero = keep), or NULL (keep (bits & 0x7FFF) != 0).
+ *   stream the kernels run on it; the call returns when the handle is complete.
+ * Allocates the handle's buffers plus O(num_tiles) temporary device memory.  Errors as
+ * lscd_encode (INVALID_VALUE for a misaligned A, NOT_SUPPORTED for 2^32 words or more).
+ */
+lscd_status_t lscd_encode_device(const void* A, const void* mask, int64_t M, int64_t K, void* stream,
+                                 lscd_handle_t* out);
+
+/*
  * lscd_import -- validate a caller-built encoding (host arrays, as described above) and
  * upload it to the current device.  Returns INVALID_FORMAT when tile_offsets is not
  * non-decreasing from 0, a tile's word count is not a multiple of 4, the last offset is

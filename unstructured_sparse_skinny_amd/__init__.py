@@ -32,7 +32,8 @@ LSCD_NARROW_MAX_N = 64
 LSCD_MAX_N = 65535
 
 #: Every entry point include/lscd.h declares.
-EXPORTS = ("lscd_pack_size", "lscd_pack", "lscd_encode", "lscd_encode_tiled", "lscd_import", "lscd_export",
+EXPORTS = ("lscd_pack_size", "lscd_pack", "lscd_encode", "lscd_encode_tiled", "lscd_encode_device",
+           "lscd_import", "lscd_export",
            "lscd_get_info", "lscd_spmm", "lscd_debug_decode", "lscd_attach_dense", "lscd_linear",
            "lscd_linear_path", "lscd_set_linear_crossover", "lscd_linear_model", "lscd_destroy",
            "lscd_status_string")
@@ -65,6 +66,7 @@ def _load():
         "lscd_pack": [VP, VP, I64, I64, I32, I32, VP, I64, VP, I64],
         "lscd_encode": [VP, VP, I64, I64, P(VP)],
         "lscd_encode_tiled": [VP, VP, I64, I64, I32, I32, P(VP)],
+        "lscd_encode_device": [VP, VP, I64, I64, VP, P(VP)],
         "lscd_import": [VP, I64, VP, I64, I64, I32, I32, P(VP)],
         "lscd_export": [VP, VP, VP],
         "lscd_get_info": [VP, P(lscd_info_t)],
@@ -174,6 +176,23 @@ def lscd_encode_tiled(A16, mask, tile_m, tile_k) -> Handle:
     h = ctypes.c_void_p()
     _check(_lib.lscd_encode_tiled(pa, pm, A16.shape[0], A16.shape[1], tile_m, tile_k, ctypes.byref(h)),
            "lscd_encode_tiled")
+    return Handle(h.value)
+
+
+def lscd_encode_device(A, mask=None, stream=None) -> Handle:
+    """Encode a matrix already on the GPU: A float16 [M][K], mask uint8/bool [M][K] or None."""
+    if not isinstance(A, torch.Tensor) or not A.is_cuda or A.dim() != 2 or not A.is_contiguous() or \
+            A.dtype not in (torch.float16, torch.int16, torch.uint16):
+        raise ValueError("A must be a contiguous 2-D CUDA tensor of fp16 (or 16-bit patterns)")
+    pm = None
+    if mask is not None:
+        if not isinstance(mask, torch.Tensor) or not mask.is_cuda or tuple(mask.shape) != tuple(A.shape) or \
+                not mask.is_contiguous() or mask.dtype not in (torch.uint8, torch.bool):
+            raise ValueError("mask must be a contiguous uint8/bool CUDA tensor of A's shape")
+        pm = ctypes.c_void_p(mask.data_ptr())
+    h = ctypes.c_void_p()
+    _check(_lib.lscd_encode_device(ctypes.c_void_p(A.data_ptr()), pm, A.shape[0], A.shape[1], _stream(stream),
+                                   ctypes.byref(h)), "lscd_encode_device")
     return Handle(h.value)
 
 

@@ -19,7 +19,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "liblscd.so")
 BUILD_DIR = os.path.join(HERE, "_build")
-SOURCES = ["csrc/lscd_api.cpp", "csrc/lscd_linear.cpp", "csrc/lscd_pack.cpp", "csrc/lscd_kernels.hip"]
+SOURCES = ["csrc/lscd_api.cpp", "csrc/lscd_linear.cpp", "csrc/lscd_pack.cpp", "csrc/lscd_kernels.hip",
+           "csrc/lscd_encode_dev.hip"]
 ARCH = os.environ.get("LSCD_OFFLOAD_ARCH", "gfx950")
 
 

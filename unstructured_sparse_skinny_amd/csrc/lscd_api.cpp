@@ -68,9 +68,13 @@ int pick_kind(int npad) {
 
 int npad_index(int N) { return N <= 16 ? 0 : (N <= 32 ? 1 : 2); }
 
-// Upload an encoding and size the workspace.  Takes ownership of nothing.
-lscd_status_t make_handle(const uint32_t* words, int64_t nwords, const uint32_t* offs, const Grid& g,
-                          int64_t nnz, int32_t maxw, lscd_handle_t* out) {
+}  // namespace
+
+namespace lscd {
+
+// A handle for grid g with its kernel plan (variants, K splits) and split-K workspace; the
+// caller supplies the encoding buffers.
+lscd_status_t new_handle(const Grid& g, int64_t nnz, int64_t nwords, int32_t maxw, lscd_handle_s** out) {
     lscd_handle_s* h = new (std::nothrow) lscd_handle_s();
     if (!h) return LSCD_ERROR_OUT_OF_MEMORY;
     h->g = g;
@@ -85,21 +89,20 @@ lscd_status_t make_handle(const uint32_t* words, int64_t nwords, const uint32_t*
     int cus = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, h->device) == hipSuccess && cus > 0)
         h->cus = cus;
-    h->R = lscd::pick_reg_vectors(maxw);
-    const bool kernel_tile = g.tm == lscd::kTileM && g.tk == lscd::kTileK;
+    h->R = pick_reg_vectors(maxw);
+    const bool kernel_tile = g.tm == kTileM && g.tk == kTileK;
     int64_t part = 0;
     for (int i = 0; i < 3 && kernel_tile; ++i) {
         h->kind[i] = pick_kind(16 << i);
-        const int occ = lscd::spmm_blocks_per_cu(h->kind[i], 16 << i, h->R, (int)std::min<int64_t>(g.K, 1 << 30));
-        const int min_tiles = h->kind[i] == lscd::kKernelIndep ? 8 : (h->kind[i] == lscd::kKernelIndep8 ? 16 : 2);
-        h->S[i] = plan_splits(g, h->cus, occ, row_groups(g, h->kind[i]), min_tiles,
-                              h->kind[i] != lscd::kKernelShared);
+        const int occ = spmm_blocks_per_cu(h->kind[i], 16 << i, h->R, (int)std::min<int64_t>(g.K, 1 << 30));
+        const int min_tiles = h->kind[i] == kKernelIndep ? 8 : (h->kind[i] == kKernelIndep8 ? 16 : 2);
+        h->S[i] = plan_splits(g, h->cus, occ, row_groups(g, h->kind[i]), min_tiles, h->kind[i] != kKernelShared);
         if (h->S[i] > 1) part = std::max<int64_t>(part, (int64_t)h->S[i] * g.M * (16 << i) * 4);
     }
-    h->Rw = lscd::pick_reg_vectors_wide(maxw);
+    h->Rw = pick_reg_vectors_wide(maxw);
     for (int i = 0; i < 3 && kernel_tile; ++i) {
         const int npad = 128 + 64 * i;
-        const int occ = lscd::spmm_blocks_per_cu(lscd::kKernelWide, npad, h->Rw, (int)std::min<int64_t>(g.K, 1 << 30));
+        const int occ = spmm_blocks_per_cu(kKernelWide, npad, h->Rw, (int)std::min<int64_t>(g.K, 1 << 30));
         h->Sw[i] = plan_splits(g, h->cus, occ, g.MB, 4, false);
         if (h->Sw[i] > 1) part = std::max<int64_t>(part, (int64_t)h->Sw[i] * g.M * npad * 4);
     }
@@ -107,18 +110,36 @@ lscd_status_t make_handle(const uint32_t* words, int64_t nwords, const uint32_t*
         free_handle(h);
         return LSCD_ERROR_OUT_OF_MEMORY;
     }
+    if (part > 0) {
+        h->part_bytes = part;
+        if ((e = hipMalloc((void**)&h->d_part, (size_t)h->part_bytes)) != hipSuccess) {
+            h->d_part = nullptr;
+            free_handle(h);
+            return hip_status(e);
+        }
+    }
+    *out = h;
+    return LSCD_SUCCESS;
+}
+
+void delete_handle(lscd_handle_s* h) { free_handle(h); }
+
+}  // namespace lscd
+
+namespace {
+
+// Upload a host encoding into a new handle.
+lscd_status_t make_handle(const uint32_t* words, int64_t nwords, const uint32_t* offs, const Grid& g,
+                          int64_t nnz, int32_t maxw, lscd_handle_t* out) {
+    lscd_handle_s* h = nullptr;
+    lscd_status_t st = lscd::new_handle(g, nnz, nwords, maxw, &h);
+    if (st != LSCD_SUCCESS) return st;
+    hipError_t e;
     const size_t wbytes = (size_t)std::max<int64_t>(nwords, 4) * 4;
     if ((e = hipMalloc((void**)&h->d_words, wbytes)) != hipSuccess ||
         (e = hipMalloc((void**)&h->d_offs, (size_t)(g.T + 1) * 4)) != hipSuccess) {
         free_handle(h);
         return hip_status(e);
-    }
-    if (part > 0) {
-        h->part_bytes = part;
-        if ((e = hipMalloc((void**)&h->d_part, (size_t)h->part_bytes)) != hipSuccess) {
-            free_handle(h);
-            return hip_status(e);
-        }
     }
     if (nwords > 0 && (e = hipMemcpy(h->d_words, words, (size_t)nwords * 4, hipMemcpyHostToDevice)) != hipSuccess) {
         free_handle(h);
@@ -223,6 +244,60 @@ lscd_status_t lscd_encode_tiled(const uint16_t* A, const uint8_t* mask, int64_t 
 
 lscd_status_t lscd_encode(const uint16_t* A, const uint8_t* mask, int64_t M, int64_t K, lscd_handle_t* out) {
     return lscd_encode_tiled(A, mask, M, K, LSCD_DEFAULT_TILE_M, LSCD_DEFAULT_TILE_K, out);
+}
+
+lscd_status_t lscd_encode_device(const void* A, const void* mask, int64_t M, int64_t K, void* stream,
+                                 lscd_handle_t* out) {
+    Grid g;
+    if (!A || !out || ((uintptr_t)A & 1u) || !lscd::make_grid(M, K, lscd::kTileM, lscd::kTileK, &g))
+        return LSCD_ERROR_INVALID_VALUE;
+    *out = nullptr;
+    hipStream_t s = (hipStream_t)stream;
+    uint32_t* counts = nullptr;
+    uint32_t* offs = nullptr;
+    uint32_t* words = nullptr;
+    unsigned long long* stats = nullptr;
+    unsigned long long hs[4] = {0, 0, 0, 0};
+    lscd_handle_s* h = nullptr;
+    lscd_status_t st = LSCD_SUCCESS;
+    hipError_t e;
+    if ((e = hipMalloc((void**)&counts, (size_t)g.T * 4)) != hipSuccess ||
+        (e = hipMalloc((void**)&offs, (size_t)(g.T + 1) * 4)) != hipSuccess ||
+        (e = hipMalloc((void**)&stats, sizeof(hs))) != hipSuccess) {
+        st = hip_status(e);
+        goto done;
+    }
+    if ((e = lscd::encode_device((const uint16_t*)A, (const uint8_t*)mask, g, counts, offs, stats, s)) != hipSuccess ||
+        (e = hipMemcpyAsync(hs, stats, sizeof(hs), hipMemcpyDeviceToHost, s)) != hipSuccess ||
+        (e = hipStreamSynchronize(s)) != hipSuccess) {
+        st = hip_status(e);
+        goto done;
+    }
+    if (hs[3]) {
+        st = LSCD_ERROR_NOT_SUPPORTED;  // 2^32 words or more
+        goto done;
+    }
+    if ((st = lscd::new_handle(g, (int64_t)hs[0], (int64_t)hs[1], (int32_t)hs[2], &h)) != LSCD_SUCCESS) goto done;
+    if ((e = hipMalloc((void**)&words, (size_t)std::max<unsigned long long>(hs[1], 4) * 4)) != hipSuccess ||
+        (e = lscd::encode_device_fill((const uint16_t*)A, (const uint8_t*)mask, g, offs, words,
+                                      lscd::reorder_enabled(), s)) != hipSuccess ||
+        (e = hipStreamSynchronize(s)) != hipSuccess) {
+        st = hip_status(e);
+        goto done;
+    }
+    h->d_words = words;
+    h->d_offs = offs;
+    words = nullptr;
+    offs = nullptr;
+    *out = h;
+    h = nullptr;
+done:
+    if (h) free_handle(h);
+    if (words) (void)hipFree(words);
+    if (offs) (void)hipFree(offs);
+    if (counts) (void)hipFree(counts);
+    if (stats) (void)hipFree(stats);
+    return st;
 }
 
 lscd_status_t lscd_import(const uint32_t* nonzeros, int64_t nnz_padded, const uint32_t* tile_offsets, int64_t M,

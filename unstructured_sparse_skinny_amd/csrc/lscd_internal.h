@@ -92,6 +92,16 @@ int spmm_blocks_per_cu(int kind, int npad, int R, int K);
 hipError_t launch_reduce(const float* part, uint16_t* C, int S, int64_t NM, hipStream_t s);
 hipError_t launch_decode(int R, const DecodeArgs& a, int grid, hipStream_t s);
 
+// A new handle for grid g: kernel plan, split-K workspace; d_words / d_offs left null for
+// the caller to fill.  delete_handle frees a handle and every buffer it holds.
+lscd_status_t new_handle(const Grid& g, int64_t nnz, int64_t nwords, int32_t maxw, struct ::lscd_handle_s** out);
+void delete_handle(struct ::lscd_handle_s* h);
+// Device encoder (64 x 64 tiles): count + scan into counts[T], offs[T+1] and stats
+// {nnz, words, largest tile, overflow flag}; then the bank-ordered fill into words.
+hipError_t encode_device(const uint16_t* A, const uint8_t* mask, const Grid& g, uint32_t* counts, uint32_t* offs,
+                         unsigned long long* stats, hipStream_t s);
+hipError_t encode_device_fill(const uint16_t* A, const uint8_t* mask, const Grid& g, const uint32_t* offs,
+                              uint32_t* words, bool reorder, hipStream_t s);
 // Frees the dense copy and the GEMM library handle of lscd_linear, if any.
 void release_dense(struct ::lscd_handle_s* h);
 
