@@ -106,6 +106,54 @@ __device__ __forceinline__ void scatter_tile(const u32x4 (&wb)[R], int nvec, uns
     }
 }
 
+// Scatter the register stage and keep, in place of each stored word, its LDS byte offset:
+// once the tile has been multiplied, unscatter() writes zeros at exactly those offsets, which
+// returns the tile to all zeros for a fraction of the cost of clearing all 8 KB.  Words past
+// the register stage (tiles of more than R * 64 vectors) are placed by scatter_rest(); such
+// a tile is cleared whole afterwards.
+__device__ __forceinline__ uint32_t lds_offset(uint32_t w) {
+    uint32_t b = (w >> 15) & 0x1FFEu;
+    return b ^ ((b >> 3) & 0x70u);
+}
+
+template <int R>
+__device__ __forceinline__ void scatter_keep(u32x4 (&wb)[R], int nvec, unsigned char* As, int lane) {
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+        if (j * 64 + lane < nvec) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t w = wb[j][e];
+                const uint32_t b = lds_offset(w);
+                *reinterpret_cast<uint16_t*>(As + b) = (uint16_t)w;
+                wb[j][e] = b;
+            }
+        }
+    }
+}
+
+template <int R>
+__device__ __forceinline__ void scatter_rest(int nvec, unsigned char* As, const uint32_t* tile_words, int lane) {
+    for (int v = R * 64 + lane; v < nvec; v += 64) {
+        const u32x4 x = *reinterpret_cast<const u32x4*>(tile_words + 4 * (size_t)v);
+        put_word(As, x[0]);
+        put_word(As, x[1]);
+        put_word(As, x[2]);
+        put_word(As, x[3]);
+    }
+}
+
+template <int R>
+__device__ __forceinline__ void unscatter(const u32x4 (&wb)[R], int nvec, unsigned char* As, int lane) {
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+        if (j * 64 + lane < nvec) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) *reinterpret_cast<uint16_t*>(As + wb[j][e]) = (uint16_t)0;
+        }
+    }
+}
+
 // Workgroup-cooperative forms: thread t of the workgroup takes vectors t, t + 256, ...
 // R * 256 vectors cover the largest 64 x 64 tile (1024 vectors) for R = 4.
 template <int R>
@@ -420,6 +468,7 @@ __global__ __launch_bounds__(WK * 64) void spmm_indep_kernel(SpmmArgs a) {
         __builtin_amdgcn_make_buffer_rsrc((void*)a.B, (short)0, a.N * a.K * 2, kBufWord3);
     auto off_at = [&](int i) -> uint32_t { return i <= kt1 ? toff[i] : 0u; };
 
+    zero_tile(As, lane);  // kept all-zero between tiles by unscatter()
     u32x4 wb[P][R];
     BWave<NPAD, VEC> bf[P];
     int nv[P];
@@ -454,10 +503,14 @@ __global__ __launch_bounds__(WK * 64) void spmm_indep_kernel(SpmmArgs a) {
             const uint32_t o_pf2 = off_at(kn + 2);
             const int n = nv[q];
             if (n > 0) {
-                zero_tile(As, lane);
-                scatter_tile<R>(wb[q], n, As, a.words + first[q], lane);
+                scatter_keep<R>(wb[q], n, As, lane);
+                if (n > R * 64) scatter_rest<R>(n, As, a.words + first[q], lane);
                 bf[q].store(Bw, lane);
                 mma_tile<NPAD>(acc, As, Bw, lane);
+                if (n > R * 64)
+                    zero_tile(As, lane);
+                else
+                    unscatter<R>(wb[q], n, As, lane);
             }
             uint32_t o0 = 0, o1 = 0;
             if (kn < kt1) {
