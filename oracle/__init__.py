@@ -20,10 +20,13 @@ What it computes, from the Flash-LLM pages:
   "solution" and section 3 "core formulas": C = A x B with the sparse A
   decoded to dense); so the oracle is the plain definition
   C[n][i] = sum_k A[i][k] * B[n][k], accumulated in fp64.
+* `bitmap` -- the bitmap-tile variant of the format (the pages' follow-up summary,
+  section "Problematica": one bit per position instead of per-entry positions): per
+  tile, 64-bit row masks followed by the kept values in row-major order.
 * `accounting` -- the compute-intensity formula and the byte/flop counts used
   for effective bandwidth (same review, section 3 "core formulas").
 
 Readings of points the pages leave open (bit order of a word, offset units,
 padding, output rounding) are stated in the module that takes them.
 """
-from . import accounting, spmm, tiled_csl  # noqa: F401
+from . import accounting, bitmap, spmm, tiled_csl  # noqa: F401
