@@ -43,6 +43,8 @@ def parse():
     ap.add_argument("--shape", type=int, default=0, help="config 5 only: 0 QKV, 1 OutProj, 2 MLP1, 3 MLP2")
     ap.add_argument("--n", type=int, default=None, help="batch width N (default: the config's)")
     ap.add_argument("--sparsity", type=float, default=None, help="override the config's sparsity")
+    ap.add_argument("--format", choices=("tiled-csl", "bitmap"), default="tiled-csl",
+                    help="sparse format of A: Tiled-CSL (the method's, default) or the bitmap-tile variant")
     ap.add_argument("--copies", type=int, default=0, help="encoded copies rotated in the timed loop (0: auto)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense hipBLASLt baseline")
@@ -255,12 +257,19 @@ def main():
         return
 
     t_enc = time.perf_counter()
-    words, offs = L.lscd_pack(case.A16, case.mask)
-    h0 = L.lscd_import(words, offs, M, K)
+    if args.format == "bitmap":
+        words, offs = L.lscd_pack_bitmap(case.A16, case.mask)
+        h0 = L.lscd_encode_bitmap(case.A16, case.mask)
+    else:
+        words, offs = L.lscd_pack(case.A16, case.mask)
+        h0 = L.lscd_import(words, offs, M, K)
     info = h0.info
     fmt_bytes = info["format_bytes"]
     copies = args.copies or max(2, min(32, math.ceil(3 * MALL_BYTES / fmt_bytes) + 1))
-    handles = [h0] + [L.lscd_import(words, offs, M, K) for _ in range(copies - 1)]
+    if args.format == "bitmap":
+        handles = [h0] + [L.lscd_encode_bitmap(case.A16, case.mask) for _ in range(copies - 1)]
+    else:
+        handles = [h0] + [L.lscd_import(words, offs, M, K) for _ in range(copies - 1)]
     del words, offs
     log(f"[bench] encoded {copies} copies of {fmt_bytes / 1e6:.1f} MB in {time.perf_counter() - t_enc:.1f}s; "
         f"splits={info['splits']} variants={info['variant']} reg_vectors={info['reg_vectors']} "
@@ -268,7 +277,9 @@ def main():
 
     nnz, tiles = info["nnz"], info["num_tiles"]
     split = info["splits"][L.npad_index(N)]
-    alg_bytes = 4 * nnz + 4 * (tiles + 1) + 2 * K * N + 2 * M * N
+    # Tiled-CSL: one 4-byte word per nonzero; bitmap tiles: the blob as stored (masks + values)
+    stored = 4 * info["nnz_padded"] if args.format == "bitmap" else 4 * nnz
+    alg_bytes = stored + 4 * (tiles + 1) + 2 * K * N + 2 * M * N
     flops = 2 * M * N * K
 
     B = torch.from_numpy(case.B16.view(np.float16)).to("cuda")
@@ -329,7 +340,7 @@ def main():
         with open(tpath) as f:
             t = json.load(f)
         launch = t.get("launch", {})
-        if (t.get("kernel_source_hash") == kernel_source_hash() and launch.get("splits") == split
+        if (args.format == "tiled-csl" and t.get("kernel_source_hash") == kernel_source_hash() and launch.get("splits") == split
                 and launch.get("reg_vectors") == info["reg_vectors"]):
             traffic = t.get("hbm_bytes_per_launch")
 
@@ -337,9 +348,10 @@ def main():
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f16", "data": "synthetic",
-        "config": {"workload": case.name, "M": M, "K": K, "N": N, "sparsity": round(case.sparsity, 4),
+        "config": {"workload": case.name, "format": args.format, "M": M, "K": K, "N": N,
+                   "sparsity": round(case.sparsity, 4),
                    "nnz": nnz, "tile": f"{info['tile_m']}x{info['tile_k']}", "splits": split,
-                   "variant": ["shared-B", "independent-4", "independent-8"][info["variant"][L.npad_index(N)]],
+                   "variant": ["shared-B", "independent-4", "independent-8", "wide", "bitmap"][info["variant"][L.npad_index(N)]],
                    "copies_rotated": copies, "gpu": props.name, "cus": props.multi_processor_count},
         "tflops": round(flops / (ms_step * 1e-3) / 1e12, 2),
         "pct_roofline": round(100 * value / HBM_PEAK_GBS, 1),

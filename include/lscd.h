@@ -70,6 +70,8 @@ typedef struct {
     int32_t splits_wide[3];     /* K-splits for N > 64, per launch of N padded to 128, 192,
                                    256 (N > 256 runs one launch per 256 columns)            */
     int32_t reg_vectors_wide;   /* 128-bit staging registers per thread, N > 64 kernel      */
+    int32_t format;             /* 0 Tiled-CSL, 1 bitmap tiles (lscd_encode_bitmap); for
+                                   bitmap handles nnz_padded counts the blob's 32-bit words */
 } lscd_info_t;
 
 #define LSCD_DEFAULT_TILE_M 64
@@ -114,6 +116,30 @@ lscd_status_t lscd_encode(const uint16_t* A, const uint8_t* mask, int64_t M, int
 /* lscd_encode_tiled -- lscd_encode with an explicit tile shape. */
 lscd_status_t lscd_encode_tiled(const uint16_t* A, const uint8_t* mask, int64_t M, int64_t K,
                                 int32_t tile_m, int32_t tile_k, lscd_handle_t* out);
+
+/*
+ * Bitmap-tile variant of the format (the pages' follow-up summary, section "Problematica":
+ * per-entry position metadata is as large as the values near 50% sparsity, one bit per
+ * position is not).  Same 64 x 64 tiles and tile order as above; a tile with k kept
+ * entries stores 64 row masks (uint64, little-endian, bit c of mask r = entry (r, c)
+ * kept), then its k fp16 values in row-major order padded with 0x0000 to a multiple of 8
+ * values; an empty tile stores nothing.  tile_offsets (num_tiles + 1 entries) count
+ * 16-byte units.  Bytes: 512 + 16*ceil(k/8) per non-empty tile, against 16*ceil(k/4) for
+ * Tiled-CSL.
+ *
+ * lscd_pack_bitmap_size / lscd_pack_bitmap -- host only.  The encoding of (A, mask) (same
+ *   argument rules as lscd_pack; tiles are always 64 x 64) into caller arrays of nwords
+ *   32-bit words and num_tiles + 1 offsets.
+ * lscd_encode_bitmap -- pack and upload, like lscd_encode.  The handle works with every
+ *   entry point taking a handle: lscd_spmm runs the bitmap kernel in launches of up to 32
+ *   columns; lscd_export returns the blob and its offsets; lscd_debug_decode and
+ *   lscd_attach_dense decode it.
+ */
+lscd_status_t lscd_pack_bitmap_size(const uint16_t* A, const uint8_t* mask, int64_t M, int64_t K,
+                                    int64_t* nwords, int64_t* num_tiles);
+lscd_status_t lscd_pack_bitmap(const uint16_t* A, const uint8_t* mask, int64_t M, int64_t K, uint32_t* words,
+                               int64_t words_len, uint32_t* tile_offsets, int64_t tile_offsets_len);
+lscd_status_t lscd_encode_bitmap(const uint16_t* A, const uint8_t* mask, int64_t M, int64_t K, lscd_handle_t* out);
 
 /*
  * lscd_encode_device -- lscd_encode for a matrix already in device memory: the encoding of

@@ -175,3 +175,23 @@ def test_linear_cost_model():
     for bad in ((0, K, 0, T, 8), (M, K, -1, T, 8), (M, K, 0, T, 0)):
         with pytest.raises(L.LSCDError):
             L.lscd_linear_model(*bad)
+
+
+@pytest.mark.parametrize("M,K,keep", [(64, 64, 0.2), (130, 200, 0.5), (1, 1, 1.0), (65, 129, 0.9), (100, 300, 0.0),
+                                      (257, 700, 0.3)])
+def test_pack_bitmap_matches_oracle(M, K, keep):
+    """The bitmap layout is fully determined (no free order), so the host encoder must equal
+    the oracle's encoding word for word."""
+    from oracle import bitmap as ob
+    case = syn.random_case(M, K, 1, keep, seed=M + 2 * K)
+    words, offs = L.lscd_pack_bitmap(case.A16, case.mask)
+    ow, oo = ob.encode(case.A16, case.mask)
+    assert np.array_equal(offs, oo)
+    assert np.array_equal(words, ow)
+    A = case.A16.copy()
+    A[case.mask == 0] = 0
+    A[0, 0] = 0x8000                                         # -0 is dropped without a mask
+    w2, o2 = L.lscd_pack_bitmap(A, None)
+    m2 = ((A & 0x7FFF) != 0).astype(np.uint8)
+    ow2, oo2 = ob.encode(A, m2)
+    assert np.array_equal(w2, ow2) and np.array_equal(o2, oo2)

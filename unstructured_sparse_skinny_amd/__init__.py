@@ -33,6 +33,7 @@ LSCD_MAX_N = 65535
 
 #: Every entry point include/lscd.h declares.
 EXPORTS = ("lscd_pack_size", "lscd_pack", "lscd_encode", "lscd_encode_tiled", "lscd_encode_device",
+           "lscd_pack_bitmap_size", "lscd_pack_bitmap", "lscd_encode_bitmap",
            "lscd_import", "lscd_export",
            "lscd_get_info", "lscd_spmm", "lscd_debug_decode", "lscd_attach_dense", "lscd_linear",
            "lscd_linear_path", "lscd_set_linear_crossover", "lscd_linear_model", "lscd_destroy",
@@ -46,7 +47,8 @@ class lscd_info_t(ctypes.Structure):
                 ("max_tile_words", ctypes.c_int32), ("device", ctypes.c_int32),
                 ("workspace_bytes", ctypes.c_int64), ("reg_vectors", ctypes.c_int32),
                 ("splits", ctypes.c_int32 * 3), ("variant", ctypes.c_int32 * 3),
-                ("splits_wide", ctypes.c_int32 * 3), ("reg_vectors_wide", ctypes.c_int32)]
+                ("splits_wide", ctypes.c_int32 * 3), ("reg_vectors_wide", ctypes.c_int32),
+                ("format", ctypes.c_int32)]
 
 
 class LSCDError(RuntimeError):
@@ -67,6 +69,9 @@ def _load():
         "lscd_encode": [VP, VP, I64, I64, P(VP)],
         "lscd_encode_tiled": [VP, VP, I64, I64, I32, I32, P(VP)],
         "lscd_encode_device": [VP, VP, I64, I64, VP, P(VP)],
+        "lscd_pack_bitmap_size": [VP, VP, I64, I64, P(I64), P(I64)],
+        "lscd_pack_bitmap": [VP, VP, I64, I64, VP, I64, VP, I64],
+        "lscd_encode_bitmap": [VP, VP, I64, I64, P(VP)],
         "lscd_import": [VP, I64, VP, I64, I64, I32, I32, P(VP)],
         "lscd_export": [VP, VP, VP],
         "lscd_get_info": [VP, P(lscd_info_t)],
@@ -176,6 +181,26 @@ def lscd_encode_tiled(A16, mask, tile_m, tile_k) -> Handle:
     h = ctypes.c_void_p()
     _check(_lib.lscd_encode_tiled(pa, pm, A16.shape[0], A16.shape[1], tile_m, tile_k, ctypes.byref(h)),
            "lscd_encode_tiled")
+    return Handle(h.value)
+
+
+def lscd_pack_bitmap(A16, mask=None):
+    """Host-only bitmap-tile encoding: (words uint32[nwords], tile_offsets uint32[T+1] in 16-byte units)."""
+    A16, m, pa, pm = _host_A(A16, mask)
+    nw, nt = ctypes.c_int64(), ctypes.c_int64()
+    _check(_lib.lscd_pack_bitmap_size(pa, pm, A16.shape[0], A16.shape[1], ctypes.byref(nw), ctypes.byref(nt)),
+           "lscd_pack_bitmap_size")
+    words = np.empty(max(nw.value, 1), dtype=np.uint32)
+    offs = np.empty(nt.value + 1, dtype=np.uint32)
+    _check(_lib.lscd_pack_bitmap(pa, pm, A16.shape[0], A16.shape[1], words.ctypes.data, nw.value, offs.ctypes.data,
+                                 nt.value + 1), "lscd_pack_bitmap")
+    return words[:nw.value], offs
+
+
+def lscd_encode_bitmap(A16, mask=None) -> Handle:
+    A16, m, pa, pm = _host_A(A16, mask)
+    h = ctypes.c_void_p()
+    _check(_lib.lscd_encode_bitmap(pa, pm, A16.shape[0], A16.shape[1], ctypes.byref(h)), "lscd_encode_bitmap")
     return Handle(h.value)
 
 

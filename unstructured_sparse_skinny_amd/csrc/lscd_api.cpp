@@ -74,13 +74,14 @@ namespace lscd {
 
 // A handle for grid g with its kernel plan (variants, K splits) and split-K workspace; the
 // caller supplies the encoding buffers.
-lscd_status_t new_handle(const Grid& g, int64_t nnz, int64_t nwords, int32_t maxw, lscd_handle_s** out) {
+lscd_status_t new_handle(const Grid& g, int64_t nnz, int64_t nwords, int32_t maxw, lscd_handle_s** out, int format) {
     lscd_handle_s* h = new (std::nothrow) lscd_handle_s();
     if (!h) return LSCD_ERROR_OUT_OF_MEMORY;
     h->g = g;
     h->nnz = nnz;
     h->nnz_padded = nwords;
     h->max_tile_words = maxw;
+    h->format = format;
     hipError_t e = hipGetDevice(&h->device);
     if (e != hipSuccess) {
         free_handle(h);
@@ -89,10 +90,21 @@ lscd_status_t new_handle(const Grid& g, int64_t nnz, int64_t nwords, int32_t max
     int cus = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, h->device) == hipSuccess && cus > 0)
         h->cus = cus;
-    h->R = pick_reg_vectors(maxw);
     const bool kernel_tile = g.tm == kTileM && g.tk == kTileK;
     int64_t part = 0;
-    for (int i = 0; i < 3 && kernel_tile; ++i) {
+    if (format == 1) {
+        // bitmap tiles: one kernel, launches of <= 32 columns
+        h->R = pick_reg_vectors_bitmap(maxw);
+        for (int i = 0; i < 3 && kernel_tile; ++i) {
+            const int npad = i == 0 ? 16 : 32;
+            h->kind[i] = kKernelBitmap;
+            const int occ = spmm_blocks_per_cu(kKernelBitmap, npad, h->R, (int)std::min<int64_t>(g.K, 1 << 30));
+            h->S[i] = plan_splits(g, h->cus, occ, g.MB, 8, false);  // decode-bound: fill every slot
+            if (h->S[i] > 1) part = std::max<int64_t>(part, (int64_t)h->S[i] * g.M * npad * 4);
+        }
+    }
+    if (format == 0) h->R = pick_reg_vectors(maxw);
+    for (int i = 0; i < 3 && kernel_tile && format == 0; ++i) {
         h->kind[i] = pick_kind(16 << i);
         const int occ = spmm_blocks_per_cu(h->kind[i], 16 << i, h->R, (int)std::min<int64_t>(g.K, 1 << 30));
         const int min_tiles = h->kind[i] == kKernelIndep ? 8 : (h->kind[i] == kKernelIndep8 ? 16 : 2);
@@ -100,7 +112,7 @@ lscd_status_t new_handle(const Grid& g, int64_t nnz, int64_t nwords, int32_t max
         if (h->S[i] > 1) part = std::max<int64_t>(part, (int64_t)h->S[i] * g.M * (16 << i) * 4);
     }
     h->Rw = pick_reg_vectors_wide(maxw);
-    for (int i = 0; i < 3 && kernel_tile; ++i) {
+    for (int i = 0; i < 3 && kernel_tile && format == 0; ++i) {
         const int npad = 128 + 64 * i;
         const int occ = spmm_blocks_per_cu(kKernelWide, npad, h->Rw, (int)std::min<int64_t>(g.K, 1 << 30));
         h->Sw[i] = plan_splits(g, h->cus, occ, g.MB, 4, false);
@@ -130,9 +142,9 @@ namespace {
 
 // Upload a host encoding into a new handle.
 lscd_status_t make_handle(const uint32_t* words, int64_t nwords, const uint32_t* offs, const Grid& g,
-                          int64_t nnz, int32_t maxw, lscd_handle_t* out) {
+                          int64_t nnz, int32_t maxw, lscd_handle_t* out, int format = 0) {
     lscd_handle_s* h = nullptr;
-    lscd_status_t st = lscd::new_handle(g, nnz, nwords, maxw, &h);
+    lscd_status_t st = lscd::new_handle(g, nnz, nwords, maxw, &h, format);
     if (st != LSCD_SUCCESS) return st;
     hipError_t e;
     const size_t wbytes = (size_t)std::max<int64_t>(nwords, 4) * 4;
@@ -246,6 +258,70 @@ lscd_status_t lscd_encode(const uint16_t* A, const uint8_t* mask, int64_t M, int
     return lscd_encode_tiled(A, mask, M, K, LSCD_DEFAULT_TILE_M, LSCD_DEFAULT_TILE_K, out);
 }
 
+lscd_status_t lscd_pack_bitmap_size(const uint16_t* A, const uint8_t* mask, int64_t M, int64_t K,
+                                    int64_t* nwords, int64_t* num_tiles) {
+    try {
+        Grid g;
+        if (!A || !nwords || !num_tiles || !lscd::make_grid(M, K, lscd::kTileM, lscd::kTileK, &g))
+            return LSCD_ERROR_INVALID_VALUE;
+        std::vector<uint32_t> offs;
+        int64_t nnz = 0;
+        lscd_status_t st = lscd::bitmap_offsets(A, mask, g, &offs, &nnz);
+        if (st != LSCD_SUCCESS) return st;
+        *nwords = 4 * (int64_t)offs[(size_t)g.T];
+        *num_tiles = g.T;
+        return LSCD_SUCCESS;
+    } catch (const std::bad_alloc&) {
+        return LSCD_ERROR_OUT_OF_MEMORY;
+    } catch (...) {
+        return LSCD_ERROR_INVALID_VALUE;
+    }
+}
+
+lscd_status_t lscd_pack_bitmap(const uint16_t* A, const uint8_t* mask, int64_t M, int64_t K, uint32_t* words,
+                               int64_t words_len, uint32_t* tile_offsets, int64_t tile_offsets_len) {
+    try {
+        Grid g;
+        if (!A || !tile_offsets || !lscd::make_grid(M, K, lscd::kTileM, lscd::kTileK, &g))
+            return LSCD_ERROR_INVALID_VALUE;
+        std::vector<uint32_t> offs;
+        int64_t nnz = 0;
+        lscd_status_t st = lscd::bitmap_offsets(A, mask, g, &offs, &nnz);
+        if (st != LSCD_SUCCESS) return st;
+        const int64_t nw = 4 * (int64_t)offs[(size_t)g.T];
+        if (tile_offsets_len < g.T + 1 || words_len < nw || (nw > 0 && !words)) return LSCD_ERROR_INVALID_VALUE;
+        lscd::bitmap_fill(A, mask, g, offs.data(), words);
+        memcpy(tile_offsets, offs.data(), (size_t)(g.T + 1) * 4);
+        return LSCD_SUCCESS;
+    } catch (const std::bad_alloc&) {
+        return LSCD_ERROR_OUT_OF_MEMORY;
+    } catch (...) {
+        return LSCD_ERROR_INVALID_VALUE;
+    }
+}
+
+lscd_status_t lscd_encode_bitmap(const uint16_t* A, const uint8_t* mask, int64_t M, int64_t K, lscd_handle_t* out) {
+    try {
+        Grid g;
+        if (!A || !out || !lscd::make_grid(M, K, lscd::kTileM, lscd::kTileK, &g)) return LSCD_ERROR_INVALID_VALUE;
+        *out = nullptr;
+        std::vector<uint32_t> offs;
+        int64_t nnz = 0;
+        lscd_status_t st = lscd::bitmap_offsets(A, mask, g, &offs, &nnz);
+        if (st != LSCD_SUCCESS) return st;
+        const int64_t nw = 4 * (int64_t)offs[(size_t)g.T];
+        std::vector<uint32_t> words((size_t)std::max<int64_t>(nw, 1));
+        lscd::bitmap_fill(A, mask, g, offs.data(), words.data());
+        int32_t maxw = 0;
+        for (int64_t t = 0; t < g.T; ++t) maxw = std::max<int32_t>(maxw, (int32_t)(4 * (offs[t + 1] - offs[t])));
+        return make_handle(words.data(), nw, offs.data(), g, nnz, maxw, out, 1);
+    } catch (const std::bad_alloc&) {
+        return LSCD_ERROR_OUT_OF_MEMORY;
+    } catch (...) {
+        return LSCD_ERROR_INVALID_VALUE;
+    }
+}
+
 lscd_status_t lscd_encode_device(const void* A, const void* mask, int64_t M, int64_t K, void* stream,
                                  lscd_handle_t* out) {
     Grid g;
@@ -355,6 +431,7 @@ lscd_status_t lscd_get_info(lscd_handle_t h, lscd_info_t* info) {
         info->splits_wide[i] = h->Sw[i];
     }
     info->reg_vectors_wide = h->Rw;
+    info->format = h->format;
     return LSCD_SUCCESS;
 }
 
@@ -377,6 +454,27 @@ lscd_status_t lscd_spmm(lscd_handle_t h, const void* B, void* C, int32_t N, void
     a.K = (int32_t)h->g.K;
     a.MB = (int32_t)h->g.MB;
     a.KT = (int32_t)h->g.KT;
+    if (h->format == 1) {
+        // bitmap tiles: launches of up to 32 columns (the packed tile is read once per launch)
+        for (int32_t c0 = 0; c0 < N; c0 += lscd::kBitmapMaxN) {
+            const int32_t n = std::min(N - c0, lscd::kBitmapMaxN);
+            const int npad = n <= 16 ? 16 : 32;
+            a.B = (const uint16_t*)B + (int64_t)c0 * h->g.K;
+            a.C = (uint16_t*)C + (int64_t)c0 * h->g.M;
+            a.N = n;
+            a.G = (int32_t)h->g.MB;
+            a.S = h->S[npad_index(n)];
+            a.items = a.G * a.S;
+            a.per_xcd = (a.items + 7) / 8;
+            hipError_t e = lscd::launch_spmm(lscd::kKernelBitmap, npad, h->R, a, 8 * a.per_xcd, s);
+            if (e != hipSuccess) return hip_status(e);
+            if (a.S > 1) {
+                e = lscd::launch_reduce(h->d_part, a.C, a.S, (int64_t)n * h->g.M, s);
+                if (e != hipSuccess) return hip_status(e);
+            }
+        }
+        return LSCD_SUCCESS;
+    }
     // N <= 64: one launch of a skinny kernel.  N > 64: launches of up to 256 columns of the
     // wide kernel (the packed words are read once per launch); a last slice of <= 64 columns
     // goes to the skinny kernels.
@@ -426,6 +524,7 @@ lscd_status_t lscd_debug_decode(lscd_handle_t h, void* A_dense, void* stream) {
     a.KT = (int32_t)h->g.KT;
     a.T = h->g.T;
     const int64_t grid = (h->g.T + lscd::kWaves - 1) / lscd::kWaves;
+    if (h->format == 1) return hip_status(lscd::launch_decode_bitmap(a, (int)grid, (hipStream_t)stream));
     return hip_status(lscd::launch_decode(h->R, a, (int)grid, (hipStream_t)stream));
 }
 

@@ -44,6 +44,10 @@ lscd_status_t pack_offsets(const uint16_t* A, const uint8_t* mask, const Grid& g
 // Fill pass into caller storage, offsets from pack_offsets.
 void pack_fill(const uint16_t* A, const uint8_t* mask, const Grid& g, const uint32_t* offsets,
                uint32_t* words);
+// Bitmap-tile variant: count pass -> offsets in 16-byte units; fill pass into caller storage.
+lscd_status_t bitmap_offsets(const uint16_t* A, const uint8_t* mask, const Grid& g,
+                             std::vector<uint32_t>* offsets, int64_t* nnz);
+void bitmap_fill(const uint16_t* A, const uint8_t* mask, const Grid& g, const uint32_t* offsets, uint32_t* words);
 // Validate an imported encoding; fills nnz and the largest tile.
 lscd_status_t validate_format(const uint32_t* words, int64_t nwords, const uint32_t* offsets,
                               const Grid& g, int64_t* nnz, int32_t* max_tile_words);
@@ -84,6 +88,12 @@ constexpr int kKernelIndep8 = 2;  // 8 wavefronts per row block
 // of B per wavefront (N padded to 128, 192 or 256 per launch).
 constexpr int kKernelWide = 3;
 constexpr int kWideMaxN = 256;
+// Bitmap-tile format: one row block per workgroup, four wavefronts over its k range, N
+// padded to 16 or 32 per launch (wider N runs launches of 32 columns).
+constexpr int kKernelBitmap = 4;
+constexpr int kBitmapMaxN = 32;
+int pick_reg_vectors_bitmap(int32_t max_tile_words);
+hipError_t launch_decode_bitmap(const DecodeArgs& a, int grid, hipStream_t s);
 // Staging registers per thread and tile of the wide variant (1, 2 or 4).
 int pick_reg_vectors_wide(int32_t max_tile_words);
 hipError_t launch_spmm(int kind, int npad, int R, const SpmmArgs& a, int grid, hipStream_t s);
@@ -94,7 +104,8 @@ hipError_t launch_decode(int R, const DecodeArgs& a, int grid, hipStream_t s);
 
 // A new handle for grid g: kernel plan, split-K workspace; d_words / d_offs left null for
 // the caller to fill.  delete_handle frees a handle and every buffer it holds.
-lscd_status_t new_handle(const Grid& g, int64_t nnz, int64_t nwords, int32_t maxw, struct ::lscd_handle_s** out);
+lscd_status_t new_handle(const Grid& g, int64_t nnz, int64_t nwords, int32_t maxw, struct ::lscd_handle_s** out,
+                         int format = 0);
 void delete_handle(struct ::lscd_handle_s* h);
 // Device encoder (64 x 64 tiles): count + scan into counts[T], offs[T+1] and stats
 // {nnz, words, largest tile, overflow flag}; then the bank-ordered fill into words.
@@ -118,6 +129,7 @@ struct lscd_handle_s {
     int R = 2;
     int S[3] = {1, 1, 1};     // K splits used by lscd_spmm for N padded to 16, 32, 64
     int kind[3] = {0, 0, 0};  // product kernel variant for N padded to 16, 32, 64
+    int format = 0;           // 0 Tiled-CSL, 1 bitmap tiles
     int Rw = 1;               // staging vectors per thread of the wide (N > 64) variant
     int Sw[3] = {1, 1, 1};    // K splits of the wide variant for N padded to 128, 192, 256
     uint32_t* d_words = nullptr;

@@ -715,6 +715,234 @@ __global__ __launch_bounds__(kThreads) void spmm_wide_kernel(SpmmArgs a) {
     }
 }
 
+// ---------------------------------------------------------------- bitmap tiles
+// Variant format with one bit per position (the pages' follow-up summary, section
+// "Problematica"): a non-empty tile holds 64 row masks (64-bit, little-endian) and then
+// its kept values in row-major order, padded to 16-byte vectors; offsets count 16-byte
+// units.  Decoding moves work on chip: each wavefront stages the tile's values in its own
+// LDS area, lane r takes row r, finds where its row's values start (exclusive prefix of
+// the rows' popcounts across the wavefront) and writes each value at the column of the
+// next set bit of its mask.  The dense tile then feeds the same MFMA step as Tiled-CSL.
+constexpr int kMaskUnits = kTileM * 8 / 16;  // 16-byte units of a tile's masks (32)
+
+// Place row `lane`'s values (staged at Vs from value index `first`) into the zero-filled
+// dense tile As, one 32-bit half of the mask at a time; values are read eight at a time so
+// that eight LDS reads are in flight per round trip.
+__device__ __forceinline__ void bitmap_place_half(unsigned char* As, const uint16_t* Vs, uint32_t m, uint32_t col0,
+                                                  uint32_t first, int lane) {
+    const int cnt = __popc(m);
+    const uint32_t rowb = (uint32_t)lane * kRowBytes, swz = ((uint32_t)lane & 7u) << 4;
+    for (int g = 0; g < cnt; g += 8) {
+        uint16_t v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = (g + e < cnt) ? Vs[first + g + e] : (uint16_t)0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            if (g + e < cnt) {
+                const uint32_t c = col0 + (uint32_t)__builtin_ctz(m);
+                m &= m - 1u;
+                *reinterpret_cast<uint16_t*>(As + rowb + ((c * 2u) ^ swz)) = v[e];
+            }
+        }
+    }
+}
+
+__device__ __forceinline__ void bitmap_place(unsigned char* As, const uint16_t* Vs, uint32_t mlo, uint32_t mhi,
+                                             int lane) {
+    const uint32_t cnt = (uint32_t)__popc(mlo) + (uint32_t)__popc(mhi);
+    uint32_t x = cnt;  // inclusive prefix over the wavefront's rows
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const uint32_t y = (uint32_t)__shfl_up((int)x, d, 64);
+        if (lane >= d) x += y;
+    }
+    const uint32_t first = x - cnt;
+    bitmap_place_half(As, Vs, mlo, 0u, first, lane);
+    bitmap_place_half(As, Vs, mhi, 32u, first + (uint32_t)__popc(mlo), lane);
+}
+
+// Bitmap-tile product for N <= 32 per launch, organised like the independent-wavefront
+// kernel: a workgroup owns one row block and its four wavefronts split the k range; each
+// wavefront has its own dense tile, value staging area and B tile, and needs no barrier.
+template <int NPAD, int R, bool VEC>
+__global__ __launch_bounds__(256) void spmm_bitmap_kernel(SpmmArgs a) {
+    constexpr int WK = 4, P = 2;
+    constexpr int kBBytes = NPAD * kRowBytes;
+    static_assert(NPAD * kTileM * 4 <= kTileBytes, "the reduction reuses each wavefront's tile");
+    __shared__ __attribute__((aligned(16))) unsigned char smem[WK * (2 * kTileBytes + kBBytes)];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    unsigned char* As = smem + wave * kTileBytes;
+    uint16_t* Vs = reinterpret_cast<uint16_t*>(smem + WK * kTileBytes + wave * kTileBytes);
+    unsigned char* Bw = smem + 2 * WK * kTileBytes + wave * kBBytes;
+
+    const int bid = blockIdx.x;
+    const int item = (bid & 7) * a.per_xcd + (bid >> 3);
+    if (item >= a.items) return;
+    const int s = item / a.G;
+    const int rb = item - s * a.G;
+    const int ks0 = (int)(((int64_t)s * a.KT) / a.S);
+    const int ks1 = (int)(((int64_t)(s + 1) * a.KT) / a.S);
+    const int kt0 = ks0 + (wave * (ks1 - ks0)) / WK;
+    const int kt1 = ks0 + ((wave + 1) * (ks1 - ks0)) / WK;
+    const kconst_u32* toff = (const kconst_u32*)(a.offs) + (int64_t)rb * a.KT;
+    const __amdgpu_buffer_rsrc_t bsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)a.B, (short)0, a.N * a.K * 2, kBufWord3);
+
+    u32x4 vb[P][R];
+    uint32_t mlo[P], mhi[P];
+    int nv[P];
+    uint32_t first[P];
+    BWave<NPAD, VEC> bf[P];
+    // tile k into stage q: masks (lane = row) and the first R * 64 value vectors
+    auto fetch = [&](int q, int k) {
+        uint32_t o0 = 0, o1 = 0;
+        if (k < kt1) {
+            o0 = toff[k];
+            o1 = toff[k + 1];
+        }
+        const int units = (int)(o1 - o0);
+        first[q] = o0;
+        nv[q] = units > 0 ? units - kMaskUnits : 0;
+        const uint32_t* tw = a.words + 4 * (size_t)o0;
+        __amdgpu_buffer_rsrc_t ms =
+            __builtin_amdgcn_make_buffer_rsrc((void*)tw, (short)0, units > 0 ? kTileM * 8 : 0, kBufWord3);
+        const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b32(ms, lane * 8, 0, kStreamPolicy);
+        const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b32(ms, lane * 8 + 4, 0, kStreamPolicy);
+        mlo[q] = lo;
+        mhi[q] = hi;
+        __amdgpu_buffer_rsrc_t vs = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(tw + (units > 0 ? 4 * kMaskUnits : 0)), (short)0, nv[q] * 16, kBufWord3);
+#pragma unroll
+        for (int j = 0; j < R; ++j)
+            vb[q][j] = __builtin_amdgcn_raw_buffer_load_b128(vs, (j * 64 + lane) * 16, 0, kStreamPolicy);
+        bf[q].load(bsrc, a.B, a.N, a.K, k, lane, k < kt1);
+    };
+#pragma unroll
+    for (int q = 0; q < P; ++q) fetch(q, kt0 + q);
+
+    f32x4 acc[4][NPAD / 16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < NPAD / 16; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    for (int kt = kt0; kt < kt1; kt += P) {
+#pragma unroll
+        for (int q = 0; q < P; ++q) {
+            const int k = kt + q;
+            const int n = nv[q];
+            if (n > 0) {
+                zero_tile(As, lane);
+#pragma unroll
+                for (int j = 0; j < R; ++j)
+                    if (j * 64 + lane < n) *reinterpret_cast<u32x4*>(reinterpret_cast<unsigned char*>(Vs) + (j * 64 + lane) * 16) = vb[q][j];
+                if (n > R * 64) {
+                    const uint32_t* tv = a.words + 4 * (size_t)first[q] + 4 * kMaskUnits;
+                    for (int v = R * 64 + lane; v < n; v += 64)
+                        *reinterpret_cast<u32x4*>(reinterpret_cast<unsigned char*>(Vs) + v * 16) =
+                            *reinterpret_cast<const u32x4*>(tv + 4 * (size_t)v);
+                }
+                bitmap_place(As, Vs, mlo[q], mhi[q], lane);
+                bf[q].store(Bw, lane);
+                mma_tile<NPAD>(acc, As, Bw, lane);
+            }
+            fetch(q, k + P);
+        }
+    }
+
+    // the wavefronts' sums, added in wavefront order (as in the independent-wavefront kernel)
+    float* red = reinterpret_cast<float*>(As);
+    const int ncol = lane & 15;
+    const int mq = (lane >> 4) * 4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < NPAD / 16; ++j)
+            *reinterpret_cast<f32x4*>(red + (j * 16 + ncol) * kTileM + i * 16 + mq) = acc[i][j];
+    __syncthreads();
+    const bool vec_m = (a.M & 3) == 0;
+    for (int it = tid; it < a.N * (kTileM / 4); it += WK * 64) {
+        const int nn = it / (kTileM / 4);
+        const int ml = (it - nn * (kTileM / 4)) * 4;
+        f32x4 sum = *reinterpret_cast<const f32x4*>(smem + (nn * kTileM + ml) * 4);
+#pragma unroll
+        for (int w = 1; w < WK; ++w)
+            sum += *reinterpret_cast<const f32x4*>(smem + w * kTileBytes + (nn * kTileM + ml) * 4);
+        const int m = rb * kTileM + ml;
+        if (m >= a.M) continue;
+        if (a.S == 1) {
+            uint16_t* dst = a.C + (int64_t)nn * a.M + m;
+            if (vec_m) {
+                uint2 pk;
+                pk.x = (uint32_t)f16_bits(sum[0]) | ((uint32_t)f16_bits(sum[1]) << 16);
+                pk.y = (uint32_t)f16_bits(sum[2]) | ((uint32_t)f16_bits(sum[3]) << 16);
+                *reinterpret_cast<uint2*>(dst) = pk;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (m + e < a.M) dst[e] = f16_bits(sum[e]);
+            }
+        } else {
+            float* dst = a.part + ((int64_t)s * a.N + nn) * a.M + m;
+            if (vec_m) {
+                *reinterpret_cast<f32x4*>(dst) = sum;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (m + e < a.M) dst[e] = sum[e];
+            }
+        }
+    }
+}
+
+// Dense view of a bitmap encoding through the same staging and placement code.
+__global__ __launch_bounds__(kThreads) void decode_bitmap_kernel(DecodeArgs a) {
+    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * kWaves * kTileBytes];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    unsigned char* As = smem + wave * kTileBytes;
+    uint16_t* Vs = reinterpret_cast<uint16_t*>(smem + (kWaves + wave) * kTileBytes);
+    const int64_t t = (int64_t)blockIdx.x * kWaves + wave;
+    const bool act = t < a.T;
+    uint32_t o0 = 0, o1 = 0;
+    if (act) {
+        o0 = a.offs[t];
+        o1 = a.offs[t + 1];
+    }
+    zero_tile(As, lane);
+    if (o1 > o0) {
+        const uint32_t* tw = a.words + 4 * (size_t)o0;
+        const uint32_t mlo = tw[2 * lane], mhi = tw[2 * lane + 1];
+        const int n = (int)(o1 - o0) - kMaskUnits;
+        for (int v = lane; v < n; v += 64)
+            *reinterpret_cast<u32x4*>(reinterpret_cast<unsigned char*>(Vs) + v * 16) =
+                *reinterpret_cast<const u32x4*>(tw + 4 * kMaskUnits + 4 * (size_t)v);
+        bitmap_place(As, Vs, mlo, mhi, lane);
+    }
+    __syncthreads();
+    if (!act) return;
+    const int bm = (int)(t / a.KT), bk = (int)(t % a.KT);
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+        const int ch = p * 64 + lane;
+        const int r = ch >> 3, c = ch & 7;
+        const int gi = bm * kTileM + r, gj = bk * kTileK + c * 8;
+        if (gi >= a.M || gj >= a.K) continue;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(As + lds_chunk(r, c));
+        uint16_t* dst = a.A + (int64_t)gi * a.K + gj;
+        if ((a.K & 7) == 0 && gj + 8 <= a.K) {
+            *reinterpret_cast<u32x4*>(dst) = v;
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if (gj + e < a.K) dst[e] = (uint16_t)(v[e >> 1] >> ((e & 1) * 16));
+        }
+    }
+}
+
 // Second pass of split-K: C = fp16( ((P0 + P1) + P2) + ... ), fixed ascending order.  A
 // separate launch: the kernel boundary makes every workgroup's partial sums visible to
 // every XCD without cache write-backs inside the product kernel.
@@ -845,6 +1073,26 @@ hipError_t launch_spmm_n(int kind, int R, const SpmmArgs& a, int grid, hipStream
     }
 }
 
+template <int NPAD>
+hipError_t launch_bitmap_n(int R, const SpmmArgs& a, int grid, hipStream_t st, int* occ) {
+    if ((a.K & 7) != 0) return run(spmm_bitmap_kernel<NPAD, 2, false>, a, grid, st, occ);
+    switch (R) {
+        case 1: return run(spmm_bitmap_kernel<NPAD, 1, true>, a, grid, st, occ);
+        case 2: return run(spmm_bitmap_kernel<NPAD, 2, true>, a, grid, st, occ);
+        case 4: return run(spmm_bitmap_kernel<NPAD, 4, true>, a, grid, st, occ);
+        case 8: return run(spmm_bitmap_kernel<NPAD, 8, true>, a, grid, st, occ);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_bitmap_any(int npad, int R, const SpmmArgs& a, int grid, hipStream_t st, int* occ) {
+    switch (npad) {
+        case 16: return launch_bitmap_n<16>(R, a, grid, st, occ);
+        case 32: return launch_bitmap_n<32>(R, a, grid, st, occ);
+        default: return hipErrorInvalidValue;
+    }
+}
+
 template <int NW>
 hipError_t launch_wide_nw(int R, const SpmmArgs& a, int grid, hipStream_t st, int* occ) {
     if ((a.K & 7) != 0) return run(spmm_wide_kernel<NW, 4, false>, a, grid, st, occ);
@@ -895,6 +1143,7 @@ int pick_reg_vectors_wide(int32_t max_tile_words) {
 
 hipError_t launch_spmm(int kind, int npad, int R, const SpmmArgs& a, int grid, hipStream_t st) {
     if (kind == kKernelWide) return launch_wide_any(npad, R, a, grid, st, nullptr);
+    if (kind == kKernelBitmap) return launch_bitmap_any(npad, R, a, grid, st, nullptr);
     switch (npad) {
         case 16: return launch_spmm_n<16>(kind, R, a, grid, st, nullptr);
         case 32: return launch_spmm_n<32>(kind, R, a, grid, st, nullptr);
@@ -909,6 +1158,8 @@ int spmm_blocks_per_cu(int kind, int npad, int R, int K) {
     dummy.K = K;
     hipError_t e = hipErrorInvalidValue;
     if (kind == kKernelWide) return (launch_wide_any(npad, R, dummy, 0, nullptr, &occ) == hipSuccess && occ > 0) ? occ : 1;
+    if (kind == kKernelBitmap)
+        return (launch_bitmap_any(npad, R, dummy, 0, nullptr, &occ) == hipSuccess && occ > 0) ? occ : 1;
     switch (npad) {
         case 16: e = launch_spmm_n<16>(kind, R, dummy, 0, nullptr, &occ); break;
         case 32: e = launch_spmm_n<32>(kind, R, dummy, 0, nullptr, &occ); break;
@@ -924,6 +1175,21 @@ hipError_t launch_reduce(const float* part, uint16_t* C, int S, int64_t NM, hipS
     if (blocks < 1) blocks = 1;
     hipLaunchKernelGGL(reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, st, part, C, S, NM);
     return hipGetLastError();
+}
+
+hipError_t launch_decode_bitmap(const DecodeArgs& a, int grid, hipStream_t st) {
+    hipLaunchKernelGGL(decode_bitmap_kernel, dim3(grid), dim3(kThreads), 0, st, a);
+    return hipGetLastError();
+}
+
+int pick_reg_vectors_bitmap(int32_t max_tile_words) {
+    // value vectors of the largest tile (its words minus the masks), per lane
+    const int vec = max_tile_words / 4 > kMaskUnits ? max_tile_words / 4 - kMaskUnits : 0;
+    const int need = (vec + 63) / 64;
+    int r = need <= 1 ? 1 : (need <= 2 ? 2 : (need <= 4 ? 4 : 8));
+    if (const char* e = getenv("LSCD_MAX_R"))  // tests: force the path for tiles past the stage
+        if (atoi(e) > 0 && atoi(e) < r) r = atoi(e) >= 4 ? 4 : (atoi(e) >= 2 ? 2 : 1);
+    return r;
 }
 
 hipError_t launch_decode(int R, const DecodeArgs& a, int grid, hipStream_t st) {

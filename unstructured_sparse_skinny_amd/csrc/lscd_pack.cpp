@@ -182,6 +182,76 @@ void pack_fill(const uint16_t* A, const uint8_t* mask, const Grid& g, const uint
     });
 }
 
+// ---------------------------------------------------------------- bitmap tiles
+// Layout (follow-up summary of the pages, section "Problematica": one bit per position in
+// place of per-entry positions): a tile with k kept entries stores tm 64-bit row masks,
+// little-endian (bit c of mask r = entry (r, c) kept), then the k fp16 values in row-major
+// order padded with zeros to a multiple of 8 values; an empty tile stores nothing.
+// Offsets count 16-byte units.
+
+lscd_status_t bitmap_offsets(const uint16_t* A, const uint8_t* mask, const Grid& g, std::vector<uint32_t>* offsets,
+                             int64_t* nnz_out) {
+    if (g.tk > 64) return LSCD_ERROR_INVALID_VALUE;
+    std::vector<int64_t> cnt((size_t)g.T, 0);
+    parallel_for(g.MB, [&](int64_t lo, int64_t hi) {
+        for (int64_t bm = lo; bm < hi; ++bm) {
+            int64_t* c = cnt.data() + bm * g.KT;
+            const int64_t r1 = std::min<int64_t>(g.M, (bm + 1) * g.tm);
+            for (int64_t r = bm * g.tm; r < r1; ++r) {
+                const size_t base = (size_t)r * (size_t)g.K;
+                for (int64_t bk = 0; bk < g.KT; ++bk) {
+                    const int64_t c1 = std::min<int64_t>(g.K, (bk + 1) * g.tk);
+                    int64_t n = 0;
+                    for (int64_t k = bk * g.tk; k < c1; ++k) n += kept(A, mask, base + (size_t)k);
+                    c[bk] += n;
+                }
+            }
+        }
+    });
+    offsets->assign((size_t)g.T + 1, 0);
+    uint64_t run = 0;
+    int64_t nnz = 0;
+    for (int64_t t = 0; t < g.T; ++t) {
+        const int64_t n = cnt[(size_t)t];
+        nnz += n;
+        if (n > 0) run += (uint64_t)(g.tm / 2) + (uint64_t)((n + 7) / 8);  // masks: tm * 8 bytes
+        if (run * 4 >= ((uint64_t)1 << 32)) return LSCD_ERROR_NOT_SUPPORTED;
+        (*offsets)[(size_t)t + 1] = (uint32_t)run;
+    }
+    *nnz_out = nnz;
+    return LSCD_SUCCESS;
+}
+
+void bitmap_fill(const uint16_t* A, const uint8_t* mask, const Grid& g, const uint32_t* offsets, uint32_t* words) {
+    parallel_for(g.MB, [&](int64_t lo, int64_t hi) {
+        for (int64_t bm = lo; bm < hi; ++bm) {
+            const int64_t r0 = bm * g.tm, r1 = std::min<int64_t>(g.M, r0 + g.tm);
+            for (int64_t bk = 0; bk < g.KT; ++bk) {
+                const int64_t t = bm * g.KT + bk;
+                if (offsets[t + 1] == offsets[t]) continue;
+                uint32_t* out = words + 4 * (size_t)offsets[t];
+                uint16_t* vals = reinterpret_cast<uint16_t*>(out + 2 * (size_t)g.tm);
+                const size_t nwords = 4 * (size_t)(offsets[t + 1] - offsets[t]);
+                memset(out, 0, nwords * 4);
+                const int64_t c0 = bk * g.tk, c1 = std::min<int64_t>(g.K, c0 + g.tk);
+                size_t v = 0;
+                for (int64_t r = r0; r < r1; ++r) {
+                    const size_t base = (size_t)r * (size_t)g.K;
+                    uint64_t m = 0;
+                    for (int64_t c = c0; c < c1; ++c) {
+                        if (kept(A, mask, base + (size_t)c)) {
+                            m |= (uint64_t)1 << (c - c0);
+                            vals[v++] = A[base + (size_t)c];
+                        }
+                    }
+                    out[2 * (r - r0)] = (uint32_t)m;
+                    out[2 * (r - r0) + 1] = (uint32_t)(m >> 32);
+                }
+            }
+        }
+    });
+}
+
 lscd_status_t validate_format(const uint32_t* words, int64_t nwords, const uint32_t* offsets,
                               const Grid& g, int64_t* nnz_out, int32_t* maxw_out) {
     if (offsets[0] != 0 || (int64_t)offsets[g.T] != nwords) return LSCD_ERROR_INVALID_FORMAT;
