@@ -170,11 +170,12 @@ def sweep_n(args, case, L, torch, np):
     """N sweep to the dense crossover: sparse (lscd_spmm), dense (torch.mm -> hipBLASLt) and
     lscd_linear on the attached dense copy, for every N of --sweep-n."""
     M, K = case.M, case.K
-    words, offs = L.lscd_pack(case.A16, case.mask)
-    h0 = L.lscd_import(words, offs, M, K)
+    tm = L.lscd_default_tile_m(M, K)
+    words, offs = L.lscd_pack(case.A16, case.mask, tm, 64)
+    h0 = L.lscd_import(words, offs, M, K, tm, 64)
     info = h0.info
     copies = max(1, min(8, math.ceil(3 * MALL_BYTES / info["format_bytes"])))
-    hs = [h0] + [L.lscd_import(words, offs, M, K) for _ in range(copies - 1)]
+    hs = [h0] + [L.lscd_import(words, offs, M, K, tm, 64) for _ in range(copies - 1)]
     del words, offs
     Ad = torch.from_numpy(np.where(case.mask.astype(bool), case.A16, 0).astype(np.uint16).view(np.float16))
     dcopies = max(1, min(4, math.ceil(3 * MALL_BYTES / (2 * M * K))))
@@ -216,7 +217,7 @@ def bench_encode(args, case, L, torch, np):
         h.close()
     t_dev = (time.perf_counter() - t0) / reps
     t0 = time.perf_counter()
-    words, offs = L.lscd_pack(case.A16, case.mask)
+    words, offs = L.lscd_pack(case.A16, case.mask, L.lscd_default_tile_m(M, K), 64)
     t_host = time.perf_counter() - t0
     print(json.dumps({"encode": "tiled-csl 64x64", "workload": case.name, "M": M, "K": K,
                       "nnz_padded": int(words.size), "device_ms": round(t_dev * 1e3, 3),
@@ -261,15 +262,16 @@ def main():
         words, offs = L.lscd_pack_bitmap(case.A16, case.mask)
         h0 = L.lscd_encode_bitmap(case.A16, case.mask)
     else:
-        words, offs = L.lscd_pack(case.A16, case.mask)
-        h0 = L.lscd_import(words, offs, M, K)
+        tm = L.lscd_default_tile_m(M, K)       # the tile height lscd_encode would use
+        words, offs = L.lscd_pack(case.A16, case.mask, tm, 64)
+        h0 = L.lscd_import(words, offs, M, K, tm, 64)
     info = h0.info
     fmt_bytes = info["format_bytes"]
     copies = args.copies or max(2, min(32, math.ceil(3 * MALL_BYTES / fmt_bytes) + 1))
     if args.format == "bitmap":
         handles = [h0] + [L.lscd_encode_bitmap(case.A16, case.mask) for _ in range(copies - 1)]
     else:
-        handles = [h0] + [L.lscd_import(words, offs, M, K) for _ in range(copies - 1)]
+        handles = [h0] + [L.lscd_import(words, offs, M, K, tm, 64) for _ in range(copies - 1)]
     del words, offs
     log(f"[bench] encoded {copies} copies of {fmt_bytes / 1e6:.1f} MB in {time.perf_counter() - t_enc:.1f}s; "
         f"splits={info['splits']} variants={info['variant']} reg_vectors={info['reg_vectors']} "

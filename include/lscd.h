@@ -105,15 +105,27 @@ lscd_status_t lscd_pack(const uint16_t* A, const uint8_t* mask, int64_t M, int64
                         uint32_t* tile_offsets, int64_t tile_offsets_len);
 
 /*
- * lscd_encode -- pack (A, mask) with the default 64 x 64 tiles and upload it to the
- * current HIP device.  Synchronous: the upload is complete on return.  *out receives a
- * handle that owns all device buffers (format and split-K workspace) until
+ * lscd_default_tile_m -- the tile height lscd_encode and lscd_encode_device use for an M x K
+ * matrix on the current device (tiles are 64 columns wide; 64, 80, 96, 112 or 128 rows).
+ * Without a K split each row block of tiles is one workgroup, so the busiest CU handles
+ * ceil(blocks / CUs) blocks; a taller tile is chosen when it cuts that CU's rows by at least
+ * 10 %, e.g. 112 rows for M = 28672 on 256 CUs (256 blocks instead of 448).  Matrices whose
+ * 64-row blocks do not fill the GPU keep 64 (K splits balance them).  LSCD_HIP if no device.
+ */
+lscd_status_t lscd_default_tile_m(int64_t M, int64_t K, int32_t* tile_m);
+
+/*
+ * lscd_encode -- pack (A, mask) with 64-column tiles of lscd_default_tile_m rows and upload
+ * it to the current HIP device.  Synchronous: the upload is complete on return.  *out
+ * receives a handle that owns all device buffers (format and split-K workspace) until
  * lscd_destroy.  A and mask are read only during the call.
  */
 lscd_status_t lscd_encode(const uint16_t* A, const uint8_t* mask, int64_t M, int64_t K,
                           lscd_handle_t* out);
 
-/* lscd_encode_tiled -- lscd_encode with an explicit tile shape. */
+/* lscd_encode_tiled -- lscd_encode with an explicit tile shape.  Any shape with
+ * tile_m * tile_k <= 65536 encodes; lscd_spmm and lscd_debug_decode run tile_k = 64 with
+ * tile_m in {64, 80, 96, 112, 128} and return NOT_SUPPORTED for other shapes. */
 lscd_status_t lscd_encode_tiled(const uint16_t* A, const uint8_t* mask, int64_t M, int64_t K,
                                 int32_t tile_m, int32_t tile_k, lscd_handle_t* out);
 
@@ -142,8 +154,8 @@ lscd_status_t lscd_pack_bitmap(const uint16_t* A, const uint8_t* mask, int64_t M
 lscd_status_t lscd_encode_bitmap(const uint16_t* A, const uint8_t* mask, int64_t M, int64_t K, lscd_handle_t* out);
 
 /*
- * lscd_encode_device -- lscd_encode for a matrix already in device memory: the encoding of
- * the default 64 x 64 tiles is built by GPU kernels (per-tile counts, a prefix sum of the
+ * lscd_encode_device -- lscd_encode for a matrix already in device memory: the encoding
+ * (64-column tiles of lscd_default_tile_m rows) is built by GPU kernels (per-tile counts, a prefix sum of the
  * padded counts, then a fill that writes every kept entry straight to its slot) and is
  * word for word the one lscd_encode produces for the same inputs (same bank-aware order
  * inside each tile).  The pages build the format ahead of time on the host (Flash-LLM

@@ -29,15 +29,17 @@ def check_same(A16, mask):
     Ad = dev16(A16)
     md = None if mask is None else torch.from_numpy(np.ascontiguousarray(mask, dtype=np.uint8)).to("cuda")
     h = L.lscd_encode_device(Ad, md)
+    tm = L.lscd_default_tile_m(*A16.shape)
+    assert h.info["tile_m"] == tm
     words, offs = L.lscd_export(h)
-    pw, po = L.lscd_pack(A16, mask)
+    pw, po = L.lscd_pack(A16, mask, tm, 64)
     assert np.array_equal(offs, po)
     assert np.array_equal(words, pw)
     info, hh = h.info, L.lscd_encode(A16, mask).info
     for k in ("nnz", "nnz_padded", "max_tile_words", "num_tiles", "reg_vectors", "splits", "splits_wide"):
         assert info[k] == hh[k], k
     m = mask if mask is not None else ((A16 & 0x7FFF) != 0).astype(np.uint8)
-    assert np.array_equal(tc.decode(words, offs, A16.shape[0], A16.shape[1], 64, 64), tc.masked(A16, m))
+    assert np.array_equal(tc.decode(words, offs, A16.shape[0], A16.shape[1], tm, 64), tc.masked(A16, m))
     return h
 
 

@@ -32,7 +32,7 @@ LSCD_NARROW_MAX_N = 64
 LSCD_MAX_N = 65535
 
 #: Every entry point include/lscd.h declares.
-EXPORTS = ("lscd_pack_size", "lscd_pack", "lscd_encode", "lscd_encode_tiled", "lscd_encode_device",
+EXPORTS = ("lscd_pack_size", "lscd_pack", "lscd_default_tile_m", "lscd_encode", "lscd_encode_tiled", "lscd_encode_device",
            "lscd_pack_bitmap_size", "lscd_pack_bitmap", "lscd_encode_bitmap",
            "lscd_import", "lscd_export",
            "lscd_get_info", "lscd_spmm", "lscd_debug_decode", "lscd_attach_dense", "lscd_linear",
@@ -66,6 +66,7 @@ def _load():
     sig = {
         "lscd_pack_size": [VP, VP, I64, I64, I32, I32, P(I64), P(I64)],
         "lscd_pack": [VP, VP, I64, I64, I32, I32, VP, I64, VP, I64],
+        "lscd_default_tile_m": [I64, I64, P(I32)],
         "lscd_encode": [VP, VP, I64, I64, P(VP)],
         "lscd_encode_tiled": [VP, VP, I64, I64, I32, I32, P(VP)],
         "lscd_encode_device": [VP, VP, I64, I64, VP, P(VP)],
@@ -167,6 +168,13 @@ def lscd_pack(A16, mask=None, tile_m=LSCD_DEFAULT_TILE_M, tile_k=LSCD_DEFAULT_TI
     _check(_lib.lscd_pack(pa, pm, A16.shape[0], A16.shape[1], tile_m, tile_k, words.ctypes.data, nw,
                           offs.ctypes.data, nt + 1), "lscd_pack")
     return words[:nw], offs
+
+
+def lscd_default_tile_m(M: int, K: int) -> int:
+    """Tile height lscd_encode / lscd_encode_device use for an M x K matrix on the current device."""
+    tm = ctypes.c_int32()
+    _check(_lib.lscd_default_tile_m(M, K, ctypes.byref(tm)), "lscd_default_tile_m")
+    return tm.value
 
 
 def lscd_encode(A16, mask=None) -> Handle:

@@ -50,6 +50,44 @@ int plan_splits(const Grid& g, int cus, int blocks_per_cu, int64_t groups, int t
     return (int)S;
 }
 
+// Tile shapes with product kernels: 64 columns, 64 / 80 / 96 / 112 / 128 rows.
+bool kernel_shape(const Grid& g) {
+    return g.tk == lscd::kTileK && (g.tm == 64 || g.tm == 80 || g.tm == 96 || g.tm == 112 || g.tm == 128);
+}
+
+// Tile height for a matrix of M rows on a GPU of `cus` CUs.  Without a K split every row
+// block is one workgroup, so the busiest CU handles ceil(blocks / cus) blocks; a taller tile
+// is taken when it cuts that CU's rows by at least 10 % (e.g. 28672 rows: 448 blocks of 64,
+// two on most CUs = 128 rows, against 256 blocks of 112 = 112 rows).  Taller tiles also
+// serve each staged B tile to more rows.  When 64-row blocks do not fill the GPU, K splits
+// balance the work and the tile stays at 64.  LSCD_TILE_M overrides (tuning only).
+int32_t choose_tile_m(int64_t M, int cus) {
+    if (const char* e = getenv("LSCD_TILE_M")) {
+        const int v = atoi(e);
+        if (v == 64 || v == 80 || v == 96 || v == 112 || v == 128) return v;
+    }
+    const int64_t mb64 = (M + 63) / 64;
+    if (mb64 <= cus) return 64;
+    int32_t best = 64;
+    int64_t best_rows = (mb64 + cus - 1) / cus * 64;
+    for (int tm : {80, 96, 112, 128}) {
+        const int64_t mb = (M + tm - 1) / tm;
+        const int64_t rows = (mb + cus - 1) / cus * tm;
+        if (rows * 10 < best_rows * 9) {
+            best = tm;
+            best_rows = rows;
+        }
+    }
+    return best;
+}
+
+int current_cus() {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return -1;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) return -1;
+    return cus;
+}
+
 int64_t row_groups(const Grid& g, int kind) {
     return kind == lscd::kKernelShared ? (g.MB + lscd::kWaves - 1) / lscd::kWaves : g.MB;
 }
@@ -90,7 +128,8 @@ lscd_status_t new_handle(const Grid& g, int64_t nnz, int64_t nwords, int32_t max
     int cus = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, h->device) == hipSuccess && cus > 0)
         h->cus = cus;
-    const bool kernel_tile = g.tm == kTileM && g.tk == kTileK;
+    const bool kernel_tile = kernel_shape(g);
+    const bool tall = g.tm != kTileM;
     int64_t part = 0;
     if (format == 1) {
         // bitmap tiles: one kernel, launches of <= 32 columns
@@ -103,10 +142,12 @@ lscd_status_t new_handle(const Grid& g, int64_t nnz, int64_t nwords, int32_t max
             if (h->S[i] > 1) part = std::max<int64_t>(part, (int64_t)h->S[i] * g.M * npad * 4);
         }
     }
-    if (format == 0) h->R = pick_reg_vectors(maxw);
+    if (format == 0) h->R = tall ? pick_reg_vectors_tall(maxw) : pick_reg_vectors(maxw);
     for (int i = 0; i < 3 && kernel_tile && format == 0; ++i) {
-        h->kind[i] = pick_kind(16 << i);
-        const int occ = spmm_blocks_per_cu(h->kind[i], 16 << i, h->R, (int)std::min<int64_t>(g.K, 1 << 30));
+        // Tiles taller than 64 rows: eight wavefronts per row block for N <= 32, the shared B
+        // tile above.
+        h->kind[i] = tall ? (i < 2 ? kKernelIndep8 : kKernelShared) : pick_kind(16 << i);
+        const int occ = spmm_blocks_per_cu(h->kind[i], 16 << i, h->R, (int)std::min<int64_t>(g.K, 1 << 30), g.tm);
         const int min_tiles = h->kind[i] == kKernelIndep ? 8 : (h->kind[i] == kKernelIndep8 ? 16 : 2);
         h->S[i] = plan_splits(g, h->cus, occ, row_groups(g, h->kind[i]), min_tiles, h->kind[i] != kKernelShared);
         if (h->S[i] > 1) part = std::max<int64_t>(part, (int64_t)h->S[i] * g.M * (16 << i) * 4);
@@ -114,7 +155,7 @@ lscd_status_t new_handle(const Grid& g, int64_t nnz, int64_t nwords, int32_t max
     h->Rw = pick_reg_vectors_wide(maxw);
     for (int i = 0; i < 3 && kernel_tile && format == 0; ++i) {
         const int npad = 128 + 64 * i;
-        const int occ = spmm_blocks_per_cu(kKernelWide, npad, h->Rw, (int)std::min<int64_t>(g.K, 1 << 30));
+        const int occ = spmm_blocks_per_cu(kKernelWide, npad, h->Rw, (int)std::min<int64_t>(g.K, 1 << 30), g.tm);
         h->Sw[i] = plan_splits(g, h->cus, occ, g.MB, 4, false);
         if (h->Sw[i] > 1) part = std::max<int64_t>(part, (int64_t)h->Sw[i] * g.M * npad * 4);
     }
@@ -254,8 +295,21 @@ lscd_status_t lscd_encode_tiled(const uint16_t* A, const uint8_t* mask, int64_t 
     }
 }
 
+lscd_status_t lscd_default_tile_m(int64_t M, int64_t K, int32_t* tile_m) {
+    if (!tile_m || M < 1 || K < 1) return LSCD_ERROR_INVALID_VALUE;
+    const int cus = current_cus();
+    if (cus < 0) return LSCD_ERROR_HIP;
+    *tile_m = choose_tile_m(M, cus);
+    return LSCD_SUCCESS;
+}
+
 lscd_status_t lscd_encode(const uint16_t* A, const uint8_t* mask, int64_t M, int64_t K, lscd_handle_t* out) {
-    return lscd_encode_tiled(A, mask, M, K, LSCD_DEFAULT_TILE_M, LSCD_DEFAULT_TILE_K, out);
+    int32_t tm = LSCD_DEFAULT_TILE_M;
+    if (M >= 1 && K >= 1) {
+        lscd_status_t st = lscd_default_tile_m(M, K, &tm);
+        if (st != LSCD_SUCCESS) return st;
+    }
+    return lscd_encode_tiled(A, mask, M, K, tm, LSCD_DEFAULT_TILE_K, out);
 }
 
 lscd_status_t lscd_pack_bitmap_size(const uint16_t* A, const uint8_t* mask, int64_t M, int64_t K,
@@ -325,9 +379,11 @@ lscd_status_t lscd_encode_bitmap(const uint16_t* A, const uint8_t* mask, int64_t
 lscd_status_t lscd_encode_device(const void* A, const void* mask, int64_t M, int64_t K, void* stream,
                                  lscd_handle_t* out) {
     Grid g;
-    if (!A || !out || ((uintptr_t)A & 1u) || !lscd::make_grid(M, K, lscd::kTileM, lscd::kTileK, &g))
-        return LSCD_ERROR_INVALID_VALUE;
+    if (!A || !out || ((uintptr_t)A & 1u) || M < 1 || K < 1) return LSCD_ERROR_INVALID_VALUE;
     *out = nullptr;
+    const int cus = current_cus();
+    if (cus < 0) return LSCD_ERROR_HIP;
+    if (!lscd::make_grid(M, K, choose_tile_m(M, cus), lscd::kTileK, &g)) return LSCD_ERROR_INVALID_VALUE;
     hipStream_t s = (hipStream_t)stream;
     uint32_t* counts = nullptr;
     uint32_t* offs = nullptr;
@@ -440,7 +496,7 @@ lscd_status_t lscd_spmm(lscd_handle_t h, const void* B, void* C, int32_t N, void
     if (N == 0) return LSCD_SUCCESS;
     if (!B || !C || !aligned16(B) || !aligned16(C)) return LSCD_ERROR_INVALID_VALUE;
     if (N > LSCD_MAX_N) return LSCD_ERROR_NOT_SUPPORTED;
-    if (h->g.tm != lscd::kTileM || h->g.tk != lscd::kTileK) return LSCD_ERROR_NOT_SUPPORTED;
+    if (!kernel_shape(h->g) || (h->format == 1 && h->g.tm != lscd::kTileM)) return LSCD_ERROR_NOT_SUPPORTED;
     const int nb = std::min(N, lscd::kWideMaxN);  // columns of B read by one launch
     if ((int64_t)nb * h->g.K * 2 >= ((int64_t)1 << 31)) return LSCD_ERROR_NOT_SUPPORTED;  // B as one buffer
     lscd_status_t st = check_device(h);
@@ -454,6 +510,7 @@ lscd_status_t lscd_spmm(lscd_handle_t h, const void* B, void* C, int32_t N, void
     a.K = (int32_t)h->g.K;
     a.MB = (int32_t)h->g.MB;
     a.KT = (int32_t)h->g.KT;
+    a.TM = h->g.tm;
     if (h->format == 1) {
         // bitmap tiles: launches of up to 32 columns (the packed tile is read once per launch)
         for (int32_t c0 = 0; c0 < N; c0 += lscd::kBitmapMaxN) {
@@ -511,7 +568,7 @@ lscd_status_t lscd_spmm(lscd_handle_t h, const void* B, void* C, int32_t N, void
 
 lscd_status_t lscd_debug_decode(lscd_handle_t h, void* A_dense, void* stream) {
     if (!h || !A_dense || !aligned16(A_dense)) return LSCD_ERROR_INVALID_VALUE;
-    if (h->g.tm != lscd::kTileM || h->g.tk != lscd::kTileK) return LSCD_ERROR_NOT_SUPPORTED;
+    if (!kernel_shape(h->g) || (h->format == 1 && h->g.tm != lscd::kTileM)) return LSCD_ERROR_NOT_SUPPORTED;
     lscd_status_t st = check_device(h);
     if (st != LSCD_SUCCESS) return st;
     lscd::DecodeArgs a;
@@ -523,6 +580,7 @@ lscd_status_t lscd_debug_decode(lscd_handle_t h, void* A_dense, void* stream) {
     a.MB = (int32_t)h->g.MB;
     a.KT = (int32_t)h->g.KT;
     a.T = h->g.T;
+    a.TM = h->g.tm;
     const int64_t grid = (h->g.T + lscd::kWaves - 1) / lscd::kWaves;
     if (h->format == 1) return hip_status(lscd::launch_decode_bitmap(a, (int)grid, (hipStream_t)stream));
     return hip_status(lscd::launch_decode(h->R, a, (int)grid, (hipStream_t)stream));

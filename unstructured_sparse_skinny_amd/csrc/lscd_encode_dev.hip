@@ -1,10 +1,10 @@
 // Device-side encoder: a dense fp16 matrix (and mask) already in HBM -> the Tiled-CSL
-// encoding of the default 64 x 64 tiles, built by GPU kernels.  The pages build the format
+// encoding (64-column tiles of 64 to 128 rows), built by GPU kernels.  The pages build the format
 // ahead of time on the host (Flash-LLM paper review, xllm-io, section 3 "Tiled-CSL" and
 // "ahead-of-time data reordering"); this is the same encoding, word for word, for callers
 // whose weights are already on the GPU (loading or re-pruning a model).
 //
-//   1. count:  one wavefront per tile counts its kept entries (lane = column, 64 rows);
+//   1. count:  one wavefront per tile counts its kept entries (lane = column, one row at a time);
 //   2. scan:   one workgroup turns the per-tile counts into padded word offsets (64-bit
 //              running sum, so an encoding of 2^32 words or more is reported, not wrapped),
 //              plus the totals the host needs to size the word array;
@@ -28,12 +28,14 @@ namespace lscd {
 namespace {
 
 constexpr int kEncWaves = 4;
+constexpr int kEncMaxRows = 128;  // tallest tile
 
 struct EncArgs {
     const uint16_t* A;      // [M][K] fp16 bits
     const uint8_t* mask;    // [M][K] or null: keep (bits & 0x7FFF) != 0
     int64_t M, K;
     int64_t MB, KT, T;
+    int32_t tm;             // tile rows
     uint32_t* counts;       // [T] kept entries per tile
     uint32_t* offs;         // [T + 1] padded word offsets
     uint32_t* words;        // [offs[T]]
@@ -58,8 +60,8 @@ __global__ __launch_bounds__(kEncWaves * 64) void enc_count_kernel(EncArgs a) {
     const int64_t t = (int64_t)blockIdx.x * kEncWaves + (threadIdx.x >> 6);
     if (t >= a.T) return;
     const int64_t bm = t / a.KT, bk = t - bm * a.KT;
-    const int64_t r0 = bm * kTileM, c = bk * kTileK + lane;
-    const int rows = (int)min<int64_t>(kTileM, a.M - r0);
+    const int64_t r0 = bm * a.tm, c = bk * kTileK + lane;
+    const int rows = (int)min<int64_t>(a.tm, a.M - r0);
     uint32_t n = 0;
     if (c < a.K)
         for (int r = 0; r < rows; ++r) n += kept_at(a, (r0 + r) * a.K + c) ? 1u : 0u;
@@ -125,9 +127,9 @@ __device__ __forceinline__ uint32_t slot_of(uint32_t q, uint32_t nvec) {
 __global__ __launch_bounds__(kEncWaves * 64) void enc_fill_kernel(EncArgs a) {
     // per wavefront: bucket counters, each entry's rank in its bucket, round masks / offsets
     __shared__ uint32_t cntb[kEncWaves][64];
-    __shared__ uint8_t rank[kEncWaves][kTileM * kTileK];
-    __shared__ unsigned long long rmask[kEncWaves][2 * kTileM];
-    __shared__ uint32_t roff[kEncWaves][2 * kTileM];
+    __shared__ uint8_t rank[kEncWaves][kEncMaxRows * kTileK];           // a bucket holds <= 2 * rows entries
+    __shared__ unsigned long long rmask[kEncWaves][2 * kEncMaxRows];
+    __shared__ uint32_t roff[kEncWaves][2 * kEncMaxRows];
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
     const int64_t t = (int64_t)blockIdx.x * kEncWaves + wave;
@@ -137,8 +139,8 @@ __global__ __launch_bounds__(kEncWaves * 64) void enc_fill_kernel(EncArgs a) {
     const uint32_t nvec = (o1 - o0) >> 2;
     uint32_t* out = a.words + o0;
     const int64_t bm = t / a.KT, bk = t - bm * a.KT;
-    const int64_t r0 = bm * kTileM, c = bk * kTileK + lane;
-    const int rows = (int)min<int64_t>(kTileM, a.M - r0);
+    const int64_t r0 = bm * a.tm, c = bk * kTileK + lane;
+    const int rows = (int)min<int64_t>(a.tm, a.M - r0);
     const bool col_ok = c < a.K;
     const unsigned long long below = (1ull << lane) - 1ull;
 
@@ -218,6 +220,7 @@ hipError_t encode_device(const uint16_t* A, const uint8_t* mask, const Grid& g, 
     a.MB = g.MB;
     a.KT = g.KT;
     a.T = g.T;
+    a.tm = g.tm;
     a.counts = counts;
     a.offs = offs;
     a.stats = stats;
@@ -237,6 +240,7 @@ hipError_t encode_device_fill(const uint16_t* A, const uint8_t* mask, const Grid
     a.MB = g.MB;
     a.KT = g.KT;
     a.T = g.T;
+    a.tm = g.tm;
     a.offs = const_cast<uint32_t*>(offs);
     a.words = words;
     a.reorder = reorder ? 1 : 0;

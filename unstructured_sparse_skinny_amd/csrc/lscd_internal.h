@@ -66,6 +66,7 @@ struct SpmmArgs {
     int32_t MB, KT;            // row blocks, k tiles
     int32_t G, S;              // row groups (kWaves row blocks each), K splits
     int32_t items, per_xcd;    // G * S work items, items per XCD slot range
+    int32_t TM;                // rows of the format's tiles: 64, 80, 96, 112 or 128
 };
 
 struct DecodeArgs {
@@ -74,10 +75,13 @@ struct DecodeArgs {
     uint16_t* A;               // [M][K] fp16 out
     int32_t M, K, MB, KT;
     int64_t T;
+    int32_t TM;                // rows of the format's tiles
 };
 
 // Staging registers per lane and tile that have kernel instantiations.
 int pick_reg_vectors(int32_t max_tile_words);
+// The same for tiles taller than 64 rows (their kernels exist for R in {4, 6, 8, 10, 12}).
+int pick_reg_vectors_tall(int32_t max_tile_words);
 // Product kernel variants: kKernelShared -- four row blocks per workgroup sharing a B tile
 // in LDS (any N); kKernelIndep -- one row block per workgroup, its k range split over the
 // wavefronts, B in registers (N <= 32).
@@ -98,7 +102,7 @@ hipError_t launch_decode_bitmap(const DecodeArgs& a, int grid, hipStream_t s);
 int pick_reg_vectors_wide(int32_t max_tile_words);
 hipError_t launch_spmm(int kind, int npad, int R, const SpmmArgs& a, int grid, hipStream_t s);
 // Workgroups of a product kernel (variant, N padding, stage size) resident per CU.
-int spmm_blocks_per_cu(int kind, int npad, int R, int K);
+int spmm_blocks_per_cu(int kind, int npad, int R, int K, int TM = kTileM);
 hipError_t launch_reduce(const float* part, uint16_t* C, int S, int64_t NM, hipStream_t s);
 hipError_t launch_decode(int R, const DecodeArgs& a, int grid, hipStream_t s);
 

@@ -82,6 +82,14 @@ __device__ __forceinline__ void zero_tile(unsigned char* As, int lane) {
     for (int j = 0; j < kTileBytes / 1024; ++j) *reinterpret_cast<u32x4*>(As + (j * 64 + lane) * 16) = z;
 }
 
+// Tile of TM rows (a multiple of 16, at most 128): TM * 128 bytes, cleared 1 KB per store.
+template <int TM>
+__device__ __forceinline__ void zero_rows(unsigned char* As, int lane) {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int j = 0; j < TM * kRowBytes / 1024; ++j) *reinterpret_cast<u32x4*>(As + (j * 64 + lane) * 16) = z;
+}
+
 template <int R>
 __device__ __forceinline__ void scatter_tile(const u32x4 (&wb)[R], int nvec, unsigned char* As,
                                              const uint32_t* tile_words, int lane) {
@@ -112,7 +120,7 @@ __device__ __forceinline__ void scatter_tile(const u32x4 (&wb)[R], int nvec, uns
 // the register stage (tiles of more than R * 64 vectors) are placed by scatter_rest(); such
 // a tile is cleared whole afterwards.
 __device__ __forceinline__ uint32_t lds_offset(uint32_t w) {
-    uint32_t b = (w >> 15) & 0x1FFEu;
+    uint32_t b = (w >> 15) & 0x3FFEu;  // up to 128 rows of 64
     return b ^ ((b >> 3) & 0x70u);
 }
 
@@ -136,10 +144,8 @@ template <int R>
 __device__ __forceinline__ void scatter_rest(int nvec, unsigned char* As, const uint32_t* tile_words, int lane) {
     for (int v = R * 64 + lane; v < nvec; v += 64) {
         const u32x4 x = *reinterpret_cast<const u32x4*>(tile_words + 4 * (size_t)v);
-        put_word(As, x[0]);
-        put_word(As, x[1]);
-        put_word(As, x[2]);
-        put_word(As, x[3]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) *reinterpret_cast<uint16_t*>(As + lds_offset(x[e])) = (uint16_t)x[e];
     }
 }
 
@@ -166,15 +172,25 @@ __device__ __forceinline__ void load_tile_wg(u32x4 (&wb)[R], const uint32_t* wor
         wb[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, (j * kThreads + tid) * 16, 0, kStreamPolicy);
 }
 
+// Clear BYTES (a multiple of 16) of LDS with the workgroup's threads, 16 bytes per store.
+template <int BYTES>
+__device__ __forceinline__ void zero_buf_wg(unsigned char* buf, int tid) {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    constexpr int kChunks = BYTES / 16;
+#pragma unroll
+    for (int j = 0; j < (kChunks + kThreads - 1) / kThreads; ++j) {
+        const int c = j * kThreads + tid;
+        if (kChunks % kThreads == 0 || c < kChunks) *reinterpret_cast<u32x4*>(buf + c * 16) = z;
+    }
+}
+
 template <int R>
 __device__ __forceinline__ void scatter_tile_wg(const u32x4 (&wb)[R], int nvec, unsigned char* As, int tid) {
 #pragma unroll
     for (int j = 0; j < R; ++j) {
         if (j * kThreads + tid < nvec) {
-            put_word(As, wb[j][0]);
-            put_word(As, wb[j][1]);
-            put_word(As, wb[j][2]);
-            put_word(As, wb[j][3]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) *reinterpret_cast<uint16_t*>(As + lds_offset(wb[j][e])) = (uint16_t)wb[j][e];
         }
     }
 }
@@ -229,6 +245,27 @@ struct BStage {
     }
 };
 
+// acc[i][j] += A rows 16i..16i+15 (x 64 k) times B columns 16j..16j+15, i < RG.
+template <int NPAD, int RG>
+__device__ __forceinline__ void mma_rows(f32x4 (&acc)[RG][NPAD / 16], const unsigned char* As,
+                                         const unsigned char* Bs, int lane) {
+    const uint32_t rl = lane & 15, kq = lane >> 4;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+        half8 bf[NPAD / 16];
+#pragma unroll
+        for (int j = 0; j < NPAD / 16; ++j)
+            bf[j] = *reinterpret_cast<const half8*>(Bs + lds_chunk(j * 16 + rl, ks * 4 + kq));
+#pragma unroll
+        for (int i = 0; i < RG; ++i) {
+            const half8 af = *reinterpret_cast<const half8*>(As + lds_chunk(i * 16 + rl, ks * 4 + kq));
+#pragma unroll
+            for (int j = 0; j < NPAD / 16; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf[j], acc[i][j], 0, 0, 0);
+        }
+    }
+}
+
 // acc[i][j] += A rows 16i..16i+15 (x 64 k) times B columns 16j..16j+15.
 template <int NPAD>
 __device__ __forceinline__ void mma_tile(f32x4 (&acc)[4][NPAD / 16], const unsigned char* As,
@@ -250,14 +287,16 @@ __device__ __forceinline__ void mma_tile(f32x4 (&acc)[4][NPAD / 16], const unsig
     }
 }
 
-template <int NPAD, int R, int P, bool VEC>
+template <int NPAD, int R, int P, bool VEC, int RG>
 __global__ __launch_bounds__(kThreads) void spmm_kernel(SpmmArgs a) {
-    __shared__ __attribute__((aligned(16))) unsigned char smem[kWaves * kTileBytes + 2 * NPAD * kRowBytes];
+    constexpr int TM = 16 * RG;          // rows of the format's tiles
+    constexpr int kTB = TM * kRowBytes;  // one wavefront's LDS tile
+    __shared__ __attribute__((aligned(16))) unsigned char smem[kWaves * kTB + 2 * NPAD * kRowBytes];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    unsigned char* As = smem + wave * kTileBytes;
-    unsigned char* Bs0 = smem + kWaves * kTileBytes;
+    unsigned char* As = smem + wave * kTB;
+    unsigned char* Bs0 = smem + kWaves * kTB;
 
     // XCD-aware work mapping: hardware places workgroup b on XCD b % 8; give each XCD a
     // contiguous run of work items (items are split-major, so a run shares a B slice).
@@ -311,9 +350,9 @@ __global__ __launch_bounds__(kThreads) void spmm_kernel(SpmmArgs a) {
     uint32_t o_next = off_at(kt0 + P);      // start of the next tile to fetch
     uint32_t o_pf = off_at(kt0 + P + 1);    // its end, prefetched
 
-    f32x4 acc[4][NPAD / 16];
+    f32x4 acc[RG][NPAD / 16];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < RG; ++i)
 #pragma unroll
         for (int j = 0; j < NPAD / 16; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
@@ -332,8 +371,9 @@ __global__ __launch_bounds__(kThreads) void spmm_kernel(SpmmArgs a) {
                 bst[q].store(Bs, a.N, tid);
                 const int n = nv[q];
                 if (n > 0) {
-                    zero_tile(As, lane);
-                    scatter_tile<R>(wb[q], n, As, a.words + first[q], lane);
+                    zero_rows<TM>(As, lane);
+                    scatter_keep<R>(wb[q], n, As, lane);
+                    if (n > R * 64) scatter_rest<R>(n, As, a.words + first[q], lane);
                 }
                 // refill this register stage with tile k + P
                 uint32_t o0 = 0, o1 = 0;
@@ -348,17 +388,17 @@ __global__ __launch_bounds__(kThreads) void spmm_kernel(SpmmArgs a) {
                 bst[q].load(bsrc, a.B, a.N, a.K, kn, tid, kn < kt1);
                 load_tile<R>(wb[q], a.words, o0, nv[q], lane);
                 __syncthreads();
-                if (n > 0) mma_tile<NPAD>(acc, As, Bs, lane);
+                if (n > 0) mma_rows<NPAD, RG>(acc, As, Bs, lane);
             }
         }
     }
     // MFMA 16x16 result layout: lane holds column (lane & 15), rows 4*(lane >> 4) + 0..3.
     const int ncol = lane & 15;
-    const int mrow = rb * kTileM + (lane >> 4) * 4;
+    const int mrow = rb * TM + (lane >> 4) * 4;
     const bool vec_m = (a.M & 3) == 0;
     if (active) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < RG; ++i) {
 #pragma unroll
             for (int j = 0; j < NPAD / 16; ++j) {
                 const int n = j * 16 + ncol;
@@ -443,16 +483,19 @@ struct BWave {
 // wavefront's writes and reads in program order.  At the end the wavefronts' fp32
 // sums are added through LDS in a fixed wavefront order, so no cross-workgroup partial
 // sums are needed unless the K range is also split across workgroups.
-template <int NPAD, int R, int P, bool VEC, int WK>
+template <int NPAD, int R, int P, bool VEC, int WK, int RG>
 __global__ __launch_bounds__(WK * 64) void spmm_indep_kernel(SpmmArgs a) {
-    static_assert(NPAD * kTileM * 4 <= kTileBytes, "the reduction reuses each wavefront's tile");
+    constexpr int TM = 16 * RG;             // rows of the format's tiles
+    constexpr int kTB = TM * kRowBytes;     // the wavefront's LDS tile
+    constexpr int kUnscatterMaxWords = TM * kTileK / 4;
+    static_assert(NPAD * TM * 4 <= kTB, "the reduction reuses each wavefront's tile");
     constexpr int kBBytes = NPAD * kRowBytes;  // the wavefront's B tile
-    __shared__ __attribute__((aligned(16))) unsigned char smem[WK * (kTileBytes + kBBytes)];
+    __shared__ __attribute__((aligned(16))) unsigned char smem[WK * (kTB + kBBytes)];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    unsigned char* As = smem + wave * kTileBytes;
-    unsigned char* Bw = smem + WK * kTileBytes + wave * kBBytes;
+    unsigned char* As = smem + wave * kTB;
+    unsigned char* Bw = smem + WK * kTB + wave * kBBytes;
 
     const int bid = blockIdx.x;
     const int item = (bid & 7) * a.per_xcd + (bid >> 3);
@@ -468,7 +511,7 @@ __global__ __launch_bounds__(WK * 64) void spmm_indep_kernel(SpmmArgs a) {
         __builtin_amdgcn_make_buffer_rsrc((void*)a.B, (short)0, a.N * a.K * 2, kBufWord3);
     auto off_at = [&](int i) -> uint32_t { return i <= kt1 ? toff[i] : 0u; };
 
-    zero_tile(As, lane);  // kept all-zero between tiles by unscatter()
+    zero_rows<TM>(As, lane);  // kept all-zero between tiles by unscatter()
     u32x4 wb[P][R];
     BWave<NPAD, VEC> bf[P];
     int nv[P];
@@ -489,9 +532,9 @@ __global__ __launch_bounds__(WK * 64) void spmm_indep_kernel(SpmmArgs a) {
     uint32_t o_next = off_at(kt0 + P);
     uint32_t o_pf = off_at(kt0 + P + 1);
 
-    f32x4 acc[4][NPAD / 16];
+    f32x4 acc[RG][NPAD / 16];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < RG; ++i)
 #pragma unroll
         for (int j = 0; j < NPAD / 16; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
@@ -506,9 +549,12 @@ __global__ __launch_bounds__(WK * 64) void spmm_indep_kernel(SpmmArgs a) {
                 scatter_keep<R>(wb[q], n, As, lane);
                 if (n > R * 64) scatter_rest<R>(n, As, a.words + first[q], lane);
                 bf[q].store(Bw, lane);
-                mma_tile<NPAD>(acc, As, Bw, lane);
-                if (n > R * 64)
-                    zero_tile(As, lane);
+                mma_rows<NPAD, RG>(acc, As, Bw, lane);
+                // Reset: rewriting the scattered positions costs one 2-byte store per word,
+                // clearing the tile TM / 8 16-byte stores per lane; the former wins only for
+                // sparse tiles (at most a quarter of the tile's positions).
+                if (n > R * 64 || 4 * n > kUnscatterMaxWords)
+                    zero_rows<TM>(As, lane);
                 else
                     unscatter<R>(wb[q], n, As, lane);
             }
@@ -532,20 +578,20 @@ __global__ __launch_bounds__(WK * 64) void spmm_indep_kernel(SpmmArgs a) {
     const int ncol = lane & 15;
     const int mq = (lane >> 4) * 4;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < RG; ++i)
 #pragma unroll
         for (int j = 0; j < NPAD / 16; ++j)
-            *reinterpret_cast<f32x4*>(red + (j * 16 + ncol) * kTileM + i * 16 + mq) = acc[i][j];
+            *reinterpret_cast<f32x4*>(red + (j * 16 + ncol) * TM + i * 16 + mq) = acc[i][j];
     __syncthreads();
     const bool vec_m = (a.M & 3) == 0;
-    for (int it = tid; it < a.N * (kTileM / 4); it += WK * 64) {
-        const int n = it / (kTileM / 4);
-        const int ml = (it - n * (kTileM / 4)) * 4;
-        f32x4 sum = *reinterpret_cast<const f32x4*>(smem + (n * kTileM + ml) * 4);
+    for (int it = tid; it < a.N * (TM / 4); it += WK * 64) {
+        const int n = it / (TM / 4);
+        const int ml = (it - n * (TM / 4)) * 4;
+        f32x4 sum = *reinterpret_cast<const f32x4*>(smem + (n * TM + ml) * 4);
 #pragma unroll
         for (int w = 1; w < WK; ++w)
-            sum += *reinterpret_cast<const f32x4*>(smem + w * kTileBytes + (n * kTileM + ml) * 4);
-        const int m = rb * kTileM + ml;
+            sum += *reinterpret_cast<const f32x4*>(smem + w * kTB + (n * TM + ml) * 4);
+        const int m = rb * TM + ml;
         if (m >= a.M) continue;
         if (a.S == 1) {
             uint16_t* dst = a.C + (int64_t)n * a.M + m;
@@ -579,17 +625,19 @@ __global__ __launch_bounds__(WK * 64) void spmm_indep_kernel(SpmmArgs a) {
 // orders everything: at step k the workgroup zero-fills buffer (k+1) % 3, whose last
 // readers were the MFMAs of step k-2 (all past the barrier of step k-1), and scatters
 // into buffer k % 3, whose zero-fill was done before the barrier of step k-1.
-template <int NW, int R, bool VEC>
+template <int NW, int R, bool VEC, int RG>
 __global__ __launch_bounds__(kThreads) void spmm_wide_kernel(SpmmArgs a) {
+    constexpr int TM = 16 * RG;          // rows of the format's tiles
+    constexpr int kTB = TM * kRowBytes;  // one A buffer
     static_assert(kThreads == 256, "four wavefronts of 64 columns each");
     constexpr int NPAD = NW * 64;
     constexpr int P = 2;
     constexpr int kBBytes = NPAD * kRowBytes;
-    __shared__ __attribute__((aligned(16))) unsigned char smem[3 * kTileBytes + 2 * kBBytes];
+    __shared__ __attribute__((aligned(16))) unsigned char smem[3 * kTB + 2 * kBBytes];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    unsigned char* Bs0 = smem + 3 * kTileBytes;
+    unsigned char* Bs0 = smem + 3 * kTB;
 
     const int bid = blockIdx.x;
     const int item = (bid & 7) * a.per_xcd + (bid >> 3);
@@ -611,12 +659,7 @@ __global__ __launch_bounds__(kThreads) void spmm_wide_kernel(SpmmArgs a) {
             *reinterpret_cast<u32x4*>(Bs0 + row * kRowBytes + (ch & 7) * 16) = z;
         }
     }
-    {
-        const u32x4 z = {0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int j = 0; j < kTileBytes / (16 * kThreads); ++j)
-            *reinterpret_cast<u32x4*>(smem + (j * kThreads + tid) * 16) = z;
-    }
+    zero_buf_wg<kTB>(smem, tid);
 
     u32x4 wb[P][R];
     BStage<NPAD, VEC> bst[P];
@@ -637,9 +680,9 @@ __global__ __launch_bounds__(kThreads) void spmm_wide_kernel(SpmmArgs a) {
     uint32_t o_pf = off_at(kt0 + P + 1);
     __syncthreads();
 
-    f32x4 acc[4][4];
+    f32x4 acc[RG][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < RG; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
@@ -650,15 +693,10 @@ __global__ __launch_bounds__(kThreads) void spmm_wide_kernel(SpmmArgs a) {
             const int k = kt + q;
             const int kn = k + P;
             const int an = ab == 2 ? 0 : ab + 1;
-            unsigned char* As = smem + ab * kTileBytes;
+            unsigned char* As = smem + ab * kTB;
             unsigned char* Bs = Bs0 + (k & 1) * kBBytes;
             const uint32_t o_pf2 = off_at(kn + 2);
-            {
-                const u32x4 z = {0u, 0u, 0u, 0u};
-#pragma unroll
-                for (int j = 0; j < kTileBytes / (16 * kThreads); ++j)
-                    *reinterpret_cast<u32x4*>(smem + an * kTileBytes + (j * kThreads + tid) * 16) = z;
-            }
+            zero_buf_wg<kTB>(smem + an * kTB, tid);
             bst[q].store(Bs, a.N, tid);
             const int n = nv[q];
             scatter_tile_wg<R>(wb[q], n, As, tid);
@@ -673,16 +711,16 @@ __global__ __launch_bounds__(kThreads) void spmm_wide_kernel(SpmmArgs a) {
             bst[q].load(bsrc, a.B, a.N, a.K, kn, tid, kn < kt1);
             load_tile_wg<R>(wb[q], a.words, o0, nv[q], tid);
             __syncthreads();
-            if (n > 0 && wave < NW) mma_tile<64>(acc, As, Bs + wave * 64 * kRowBytes, lane);
+            if (n > 0 && wave < NW) mma_rows<64, RG>(acc, As, Bs + wave * 64 * kRowBytes, lane);
             ab = an;
         }
     }
     if (wave >= NW) return;
     const int ncol = lane & 15;
-    const int mrow = rb * kTileM + (lane >> 4) * 4;
+    const int mrow = rb * TM + (lane >> 4) * 4;
     const bool vec_m = (a.M & 3) == 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < RG; ++i) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int n = wave * 64 + j * 16 + ncol;
@@ -970,13 +1008,15 @@ __global__ __launch_bounds__(256) void reduce_kernel(const float* __restrict__ p
 
 // Dense view of the encoding through the product's own load and extract path: one
 // wavefront per tile, then the LDS tile is copied out un-swizzled.
-template <int R>
+template <int R, int RG>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
-    __shared__ __attribute__((aligned(16))) unsigned char smem[kWaves * kTileBytes];
+    constexpr int TM = 16 * RG;
+    constexpr int kTB = TM * kRowBytes;
+    __shared__ __attribute__((aligned(16))) unsigned char smem[kWaves * kTB];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    unsigned char* As = smem + wave * kTileBytes;
+    unsigned char* As = smem + wave * kTB;
     const int64_t t = (int64_t)blockIdx.x * kWaves + wave;
     const bool act = t < a.T;
     uint32_t o0 = 0, o1 = 0;
@@ -987,17 +1027,18 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     const int nvec = (int)((o1 - o0) >> 2);
     u32x4 wb[R];
     load_tile<R>(wb, a.words, o0, nvec, lane);
-    zero_tile(As, lane);
-    scatter_tile<R>(wb, nvec, As, a.words + o0, lane);
+    zero_rows<TM>(As, lane);
+    scatter_keep<R>(wb, nvec, As, lane);
+    if (nvec > R * 64) scatter_rest<R>(nvec, As, a.words + o0, lane);
     __syncthreads();
     if (!act) return;
     const int bm = (int)(t / a.KT), bk = (int)(t % a.KT);
     const bool vec_ok = (a.K & 7) == 0;
 #pragma unroll
-    for (int p = 0; p < 8; ++p) {
+    for (int p = 0; p < 2 * RG; ++p) {
         const int ch = p * 64 + lane;
         const int r = ch >> 3, c = ch & 7;
-        const int gi = bm * kTileM + r, gj = bk * kTileK + c * 8;
+        const int gi = bm * TM + r, gj = bk * kTileK + c * 8;
         if (gi >= a.M || gj >= a.K) continue;
         const u32x4 v = *reinterpret_cast<const u32x4*>(As + lds_chunk(r, c));
         uint16_t* dst = a.A + (int64_t)gi * a.K + gj;
@@ -1036,39 +1077,64 @@ hipError_t run(Kern k, const SpmmArgs& a, int grid, hipStream_t st, int* occ, in
     return hipGetLastError();
 }
 
+// Tile heights with kernel instantiations: 64 rows for every variant; 80, 96, 112 and 128
+// rows (RG = 5..8 row groups of 16) for the 8-wavefront independent variant (N <= 32), the
+// shared-B variant (N <= 64), the wide variant and the decode kernel.  Taller tiles come
+// with staging stages R in {4, 6, 8, 10, 12}; denser tiles take the path past the stage
+// (R = 16 with eight wavefronts spills registers).
+//
 // K % 8 != 0 (rows of B not 16-byte aligned) runs the element-wise B path, instantiated
 // only with the largest register stage.  occ != nullptr: report resident workgroups per CU
 // instead of launching.
-template <int NPAD, int R>
-hipError_t launch_spmm_r(int kind, const SpmmArgs& a, int grid, hipStream_t st, int* occ) {
+template <int NPAD, int R, int RG>
+hipError_t launch_spmm_rg(int kind, const SpmmArgs& a, int grid, hipStream_t st, int* occ) {
     const bool vec = (a.K & 7) == 0;
     if constexpr (NPAD <= 32) {
         if (kind == kKernelIndep) {
-            if (!vec) return run(spmm_indep_kernel<NPAD, 16, 2, false, 4>, a, grid, st, occ, 256);
-            return run(spmm_indep_kernel<NPAD, R, stages_indep<NPAD, R>(), true, 4>, a, grid, st, occ, 256);
+            if constexpr (RG != 4) return hipErrorInvalidValue;
+            if (!vec) return run(spmm_indep_kernel<NPAD, 16, 2, false, 4, RG>, a, grid, st, occ, 256);
+            return run(spmm_indep_kernel<NPAD, R, stages_indep<NPAD, R>(), true, 4, RG>, a, grid, st, occ, 256);
         }
         if (kind == kKernelIndep8) {
-            if (!vec) return run(spmm_indep_kernel<NPAD, 16, 2, false, 8>, a, grid, st, occ, 512);
-            return run(spmm_indep_kernel<NPAD, R, stages_indep<NPAD, R>(), true, 8>, a, grid, st, occ, 512);
+            if (!vec) return run(spmm_indep_kernel<NPAD, (RG == 4 ? 16 : 12), 2, false, 8, RG>, a, grid, st, occ, 512);
+            return run(spmm_indep_kernel<NPAD, R, (RG == 4 ? stages_indep<NPAD, R>() : 2), true, 8, RG>, a, grid, st,
+                       occ, 512);
         }
     }
     if (kind != kKernelShared) return hipErrorInvalidValue;
-    if (!vec) return run(spmm_kernel<NPAD, 16, 2, false>, a, grid, st, occ);
-    return run(spmm_kernel<NPAD, R, stages<R>(), true>, a, grid, st, occ);
+    if (!vec) return run(spmm_kernel<NPAD, (RG == 4 ? 16 : 12), 2, false, RG>, a, grid, st, occ);
+    return run(spmm_kernel<NPAD, R, stages<R>(), true, RG>, a, grid, st, occ);
+}
+
+template <int NPAD, int RG>
+hipError_t launch_spmm_r(int kind, int R, const SpmmArgs& a, int grid, hipStream_t st, int* occ) {
+    if constexpr (RG == 4) {
+        switch (R) {
+            case 2: return launch_spmm_rg<NPAD, 2, RG>(kind, a, grid, st, occ);
+            case 3: return launch_spmm_rg<NPAD, 3, RG>(kind, a, grid, st, occ);
+            case 5: return launch_spmm_rg<NPAD, 5, RG>(kind, a, grid, st, occ);
+            case 16: return launch_spmm_rg<NPAD, 16, RG>(kind, a, grid, st, occ);
+            default: break;
+        }
+    }
+    switch (R) {
+        case 4: return launch_spmm_rg<NPAD, 4, RG>(kind, a, grid, st, occ);
+        case 6: return launch_spmm_rg<NPAD, 6, RG>(kind, a, grid, st, occ);
+        case 8: return launch_spmm_rg<NPAD, 8, RG>(kind, a, grid, st, occ);
+        case 10: return launch_spmm_rg<NPAD, 10, RG>(kind, a, grid, st, occ);
+        case 12: return launch_spmm_rg<NPAD, 12, RG>(kind, a, grid, st, occ);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 template <int NPAD>
 hipError_t launch_spmm_n(int kind, int R, const SpmmArgs& a, int grid, hipStream_t st, int* occ) {
-    switch (R) {
-        case 2: return launch_spmm_r<NPAD, 2>(kind, a, grid, st, occ);
-        case 3: return launch_spmm_r<NPAD, 3>(kind, a, grid, st, occ);
-        case 4: return launch_spmm_r<NPAD, 4>(kind, a, grid, st, occ);
-        case 5: return launch_spmm_r<NPAD, 5>(kind, a, grid, st, occ);
-        case 6: return launch_spmm_r<NPAD, 6>(kind, a, grid, st, occ);
-        case 8: return launch_spmm_r<NPAD, 8>(kind, a, grid, st, occ);
-        case 10: return launch_spmm_r<NPAD, 10>(kind, a, grid, st, occ);
-        case 12: return launch_spmm_r<NPAD, 12>(kind, a, grid, st, occ);
-        case 16: return launch_spmm_r<NPAD, 16>(kind, a, grid, st, occ);
+    switch (a.TM) {
+        case 64: return launch_spmm_r<NPAD, 4>(kind, R, a, grid, st, occ);
+        case 80: return launch_spmm_r<NPAD, 5>(kind, R, a, grid, st, occ);
+        case 96: return launch_spmm_r<NPAD, 6>(kind, R, a, grid, st, occ);
+        case 112: return launch_spmm_r<NPAD, 7>(kind, R, a, grid, st, occ);
+        case 128: return launch_spmm_r<NPAD, 8>(kind, R, a, grid, st, occ);
         default: return hipErrorInvalidValue;
     }
 }
@@ -1093,13 +1159,28 @@ hipError_t launch_bitmap_any(int npad, int R, const SpmmArgs& a, int grid, hipSt
     }
 }
 
+template <int NW, int RG>
+hipError_t launch_wide_rg(int R, const SpmmArgs& a, int grid, hipStream_t st, int* occ) {
+    if ((a.K & 7) != 0) return run(spmm_wide_kernel<NW, (RG == 4 ? 4 : 8), false, RG>, a, grid, st, occ);
+    switch (R) {
+        case 1: return run(spmm_wide_kernel<NW, 1, true, RG>, a, grid, st, occ);
+        case 2: return run(spmm_wide_kernel<NW, 2, true, RG>, a, grid, st, occ);
+        case 4: return run(spmm_wide_kernel<NW, 4, true, RG>, a, grid, st, occ);
+        case 8:
+            if constexpr (RG != 4) return run(spmm_wide_kernel<NW, 8, true, RG>, a, grid, st, occ);
+            return hipErrorInvalidValue;
+        default: return hipErrorInvalidValue;
+    }
+}
+
 template <int NW>
 hipError_t launch_wide_nw(int R, const SpmmArgs& a, int grid, hipStream_t st, int* occ) {
-    if ((a.K & 7) != 0) return run(spmm_wide_kernel<NW, 4, false>, a, grid, st, occ);
-    switch (R) {
-        case 1: return run(spmm_wide_kernel<NW, 1, true>, a, grid, st, occ);
-        case 2: return run(spmm_wide_kernel<NW, 2, true>, a, grid, st, occ);
-        case 4: return run(spmm_wide_kernel<NW, 4, true>, a, grid, st, occ);
+    switch (a.TM) {
+        case 64: return launch_wide_rg<NW, 4>(R, a, grid, st, occ);
+        case 80: return launch_wide_rg<NW, 5>(R, a, grid, st, occ);
+        case 96: return launch_wide_rg<NW, 6>(R, a, grid, st, occ);
+        case 112: return launch_wide_rg<NW, 7>(R, a, grid, st, occ);
+        case 128: return launch_wide_rg<NW, 8>(R, a, grid, st, occ);
         default: return hipErrorInvalidValue;
     }
 }
@@ -1113,10 +1194,29 @@ hipError_t launch_wide_any(int npad, int R, const SpmmArgs& a, int grid, hipStre
     }
 }
 
-template <int R>
-hipError_t launch_decode_r(const DecodeArgs& a, int grid, hipStream_t st) {
-    hipLaunchKernelGGL((decode_kernel<R>), dim3(grid), dim3(kThreads), 0, st, a);
-    return hipGetLastError();
+template <int RG>
+hipError_t launch_decode_rg(int R, const DecodeArgs& a, int grid, hipStream_t st) {
+    auto go = [&](auto kern) {
+        hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), 0, st, a);
+        return hipGetLastError();
+    };
+    if constexpr (RG == 4) {
+        switch (R) {
+            case 2: return go(decode_kernel<2, RG>);
+            case 3: return go(decode_kernel<3, RG>);
+            case 5: return go(decode_kernel<5, RG>);
+            case 16: return go(decode_kernel<16, RG>);
+            default: break;
+        }
+    }
+    switch (R) {
+        case 4: return go(decode_kernel<4, RG>);
+        case 6: return go(decode_kernel<6, RG>);
+        case 8: return go(decode_kernel<8, RG>);
+        case 10: return go(decode_kernel<10, RG>);
+        case 12: return go(decode_kernel<12, RG>);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace
@@ -1136,9 +1236,14 @@ int pick_reg_vectors(int32_t max_tile_words) {
     return best;
 }
 
+int pick_reg_vectors_tall(int32_t max_tile_words) {
+    const int r = pick_reg_vectors(max_tile_words);
+    return r <= 4 ? 4 : (r <= 6 ? 6 : (r >= 12 ? 12 : r));
+}
+
 int pick_reg_vectors_wide(int32_t max_tile_words) {
     const int need = ((max_tile_words / 4) + kThreads - 1) / kThreads;
-    return need <= 1 ? 1 : (need <= 2 ? 2 : 4);
+    return need <= 1 ? 1 : (need <= 2 ? 2 : (need <= 4 ? 4 : 8));
 }
 
 hipError_t launch_spmm(int kind, int npad, int R, const SpmmArgs& a, int grid, hipStream_t st) {
@@ -1152,10 +1257,11 @@ hipError_t launch_spmm(int kind, int npad, int R, const SpmmArgs& a, int grid, h
     }
 }
 
-int spmm_blocks_per_cu(int kind, int npad, int R, int K) {
+int spmm_blocks_per_cu(int kind, int npad, int R, int K, int TM) {
     int occ = 0;
     SpmmArgs dummy{};
     dummy.K = K;
+    dummy.TM = TM;
     hipError_t e = hipErrorInvalidValue;
     if (kind == kKernelWide) return (launch_wide_any(npad, R, dummy, 0, nullptr, &occ) == hipSuccess && occ > 0) ? occ : 1;
     if (kind == kKernelBitmap)
@@ -1193,16 +1299,12 @@ int pick_reg_vectors_bitmap(int32_t max_tile_words) {
 }
 
 hipError_t launch_decode(int R, const DecodeArgs& a, int grid, hipStream_t st) {
-    switch (R) {
-        case 2: return launch_decode_r<2>(a, grid, st);
-        case 3: return launch_decode_r<3>(a, grid, st);
-        case 4: return launch_decode_r<4>(a, grid, st);
-        case 5: return launch_decode_r<5>(a, grid, st);
-        case 6: return launch_decode_r<6>(a, grid, st);
-        case 8: return launch_decode_r<8>(a, grid, st);
-        case 10: return launch_decode_r<10>(a, grid, st);
-        case 12: return launch_decode_r<12>(a, grid, st);
-        case 16: return launch_decode_r<16>(a, grid, st);
+    switch (a.TM) {
+        case 64: return launch_decode_rg<4>(R, a, grid, st);
+        case 80: return launch_decode_rg<5>(R, a, grid, st);
+        case 96: return launch_decode_rg<6>(R, a, grid, st);
+        case 112: return launch_decode_rg<7>(R, a, grid, st);
+        case 128: return launch_decode_rg<8>(R, a, grid, st);
         default: return hipErrorInvalidValue;
     }
 }

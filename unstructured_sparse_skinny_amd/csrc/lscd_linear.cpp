@@ -96,7 +96,7 @@ lscd_status_t lscd_linear_model(int64_t M, int64_t K, int64_t nnz_padded, int64_
 
 lscd_status_t lscd_attach_dense(lscd_handle_t h) {
     if (!h) return LSCD_ERROR_INVALID_VALUE;
-    if (h->g.tm != lscd::kTileM || h->g.tk != lscd::kTileK) return LSCD_ERROR_NOT_SUPPORTED;
+    if (h->g.tk != lscd::kTileK) return LSCD_ERROR_NOT_SUPPORTED;  // lscd_debug_decode checks the rest
     if (h->g.M > INT32_MAX || h->g.K > INT32_MAX) return LSCD_ERROR_NOT_SUPPORTED;
     lscd_status_t st = on_device(h);
     if (st != LSCD_SUCCESS) return st;

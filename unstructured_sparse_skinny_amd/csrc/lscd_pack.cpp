@@ -156,7 +156,8 @@ lscd_status_t pack_offsets(const uint16_t* A, const uint8_t* mask, const Grid& g
 
 void pack_fill(const uint16_t* A, const uint8_t* mask, const Grid& g, const uint32_t* offsets,
                uint32_t* words) {
-    const bool reorder = reorder_enabled() && g.tm == kTileM && g.tk == kTileK;
+    // the bank of an index depends only on its row's low bits and its column: any row count
+    const bool reorder = reorder_enabled() && g.tk == kTileK && g.tm <= 128;
     parallel_for(g.MB, [&](int64_t lo, int64_t hi) {
         std::vector<uint32_t> buf, seq;
         std::vector<int> head, nxt;
