@@ -30,21 +30,38 @@ void free_handle(lscd_handle_s* h) {
     delete h;
 }
 
-// Number of K splits for one N padding: as many workgroups as the GPU holds at once
-// (CUs x resident workgroups per CU, from the kernel's real occupancy), so the whole grid
-// runs in a single wave with no tail; every wavefront keeps at least two k tiles.
-// LSCD_SPLITK overrides (tuning only).
-// The independent-wavefront variants already split each row block's k range inside the
-// workgroup; they split across workgroups (fp32 partials + second pass) only when the row
-// blocks fill less than half of the resident slots.
+// Number of K splits for one N padding.  LSCD_SPLITK overrides (tuning only).
+//
+// Independent-wavefront variants (one workgroup per row block and split): each work item is
+// 1/S of a row block's k range, and a CU ends up with ceil(groups * S / CUs) of them, so the
+// busiest CU carries ceil(groups * S / CUs) / S row blocks of work.  S minimises that, with
+// a 1 % charge per split for the fp32 partial sums and the second pass.  E.g. 192 row blocks
+// on 256 CUs: S = 1, 2, 3 leave the busiest CU one full block, S = 4 three quarters
+// (measured 15-25 % faster on 12288-row matrices).  Every split keeps at least
+// tiles_per_split_min k tiles.
+//
+// Shared-B variant: as many workgroups as the GPU holds at once (CUs x resident workgroups
+// per CU, from the kernel's real occupancy), so the whole grid runs in a single wave.
 int plan_splits(const Grid& g, int cus, int blocks_per_cu, int64_t groups, int tiles_per_split_min, bool indep) {
     int64_t S = 1;
+    const int64_t smax = std::max<int64_t>(1, std::min<int64_t>(g.KT / tiles_per_split_min, 64));
     if (const char* e = getenv("LSCD_SPLITK")) {
         S = atoll(e);
+    } else if (indep) {
+        // at most 4: measured on OPT-175B QKV (80-row tiles), 6 splits cost 22 % over 1
+        // although the count above favours them -- each split adds a pipeline start-up and
+        // an fp32 partial per workgroup
+        double best = 0;
+        for (int64_t s = 1; s <= std::min<int64_t>(smax, 4); ++s) {
+            const double load = (double)((groups * s + cus - 1) / cus) / (double)s * (1.0 + 0.01 * (double)s);
+            if (s == 1 || load < best) {
+                best = load;
+                S = s;
+            }
+        }
     } else {
         const int64_t slots = (int64_t)cus * std::max(1, blocks_per_cu);
-        S = indep ? slots / (2 * groups) : slots / groups;
-        S = std::min<int64_t>(S, std::max<int64_t>(1, g.KT / tiles_per_split_min));
+        S = std::min<int64_t>(slots / groups, smax);
     }
     S = std::max<int64_t>(1, std::min<int64_t>(S, g.KT));
     return (int)S;
