@@ -109,16 +109,17 @@ int64_t row_groups(const Grid& g, int kind) {
     return kind == lscd::kKernelShared ? (g.MB + lscd::kWaves - 1) / lscd::kWaves : g.MB;
 }
 
-// Variant per N padding (measured on MI355X): independent wavefronts for N <= 16, where
-// the per-wavefront B fragments are small; the shared B tile above that.
-// LSCD_KERNEL=shared|indep overrides where the variant exists (tuning only).
+// Variant per N padding (measured on MI355X): independent wavefronts for N <= 32 (at N = 32
+// they tie with the shared B tile on 12288-row matrices and are 10 % faster on 49152 rows);
+// the shared B tile for N = 64, where a per-wavefront B tile would not fit next to the A tile.
+// LSCD_KERNEL=shared|indep|indep8 overrides where the variant exists (tuning only).
 int pick_kind(int npad) {
     const char* e = getenv("LSCD_KERNEL");
     if (npad > 32) return lscd::kKernelShared;
     if (e && strcmp(e, "shared") == 0) return lscd::kKernelShared;
     if (e && strcmp(e, "indep") == 0) return lscd::kKernelIndep;
     if (e && strcmp(e, "indep8") == 0) return lscd::kKernelIndep8;
-    return npad <= 16 ? lscd::kKernelIndep : lscd::kKernelShared;
+    return npad <= 32 ? lscd::kKernelIndep : lscd::kKernelShared;
 }
 
 int npad_index(int N) { return N <= 16 ? 0 : (N <= 32 ? 1 : 2); }
