@@ -111,8 +111,9 @@ lscd_status_t lscd_pack(const uint16_t* A, const uint8_t* mask, int64_t M, int64
  * ceil(blocks / CUs) blocks; a taller tile is chosen when it cuts that CU's rows by at least
  * 10 %, e.g. 112 rows for M = 28672 on 256 CUs (256 blocks instead of 448).  Matrices whose
  * 64-row blocks do not fill the GPU keep 64 (K splits balance them).  The choice favours
- * N <= 32 (measured on MI355X, 28672 x 7168 at 80 %: N = 16 / 32 / 128 run 15-22 % faster
- * on 112-row tiles, N = 64 14 % slower); lscd_encode_tiled fixes the height instead.
+ * N <= 32 (measured on MI355X, 28672 x 7168 at 80 %: N = 16 / 32 / 128 run 10-22 % faster
+ * on 112-row tiles, N = 64 ties; 27648 x 9216 at 70 %: N = 64 is 18 % slower);
+ * lscd_encode_tiled fixes the height instead.
  * LSCD_ERROR_HIP if there is no device.
  */
 lscd_status_t lscd_default_tile_m(int64_t M, int64_t K, int32_t* tile_m);

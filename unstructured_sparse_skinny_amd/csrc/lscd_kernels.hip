@@ -1103,7 +1103,8 @@ hipError_t launch_spmm_rg(int kind, const SpmmArgs& a, int grid, hipStream_t st,
     }
     if (kind != kKernelShared) return hipErrorInvalidValue;
     if (!vec) return run(spmm_kernel<NPAD, (RG == 4 ? 16 : 12), 2, false, RG>, a, grid, st, occ);
-    return run(spmm_kernel<NPAD, R, stages<R>(), true, RG>, a, grid, st, occ);
+    // tall tiles: two stages (the accumulators of RG row groups leave no room for a third)
+    return run(spmm_kernel<NPAD, R, (RG == 4 ? stages<R>() : 2), true, RG>, a, grid, st, occ);
 }
 
 template <int NPAD, int RG>
