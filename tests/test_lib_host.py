@@ -195,3 +195,12 @@ def test_pack_bitmap_matches_oracle(M, K, keep):
     m2 = ((A & 0x7FFF) != 0).astype(np.uint8)
     ow2, oo2 = ob.encode(A, m2)
     assert np.array_equal(w2, ow2) and np.array_equal(o2, oo2)
+
+
+@pytest.mark.parametrize("tm", [80, 96, 112, 128])
+@pytest.mark.parametrize("M,K,keep", [(300, 200, 0.3), (129, 64 * 3 + 5, 1.0), (1, 1, 1.0), (500, 130, 0.05)])
+def test_pack_tall_tiles_matches_oracle(tm, M, K, keep):
+    """Taller tiles (the heights the product kernels run): same unique parts as the oracle's
+    canonical encoding, valid padding, bank-aware order inside each tile."""
+    case = syn.random_case(M, K, 1, keep, seed=M + K + tm)
+    _check_pack_against_oracle(case.A16, case.mask, tm, 64)
