@@ -18,18 +18,18 @@
 
 namespace {
 
-// Cost model, fitted to MI355X measurements of both paths for N = 8 .. 1024 on four OPT
-// shapes at 50-80% sparsity (it picks the faster path in 41 of the 44 cases; the three
-// misses are within 6% of a tie).  Skinny kernels (N <= 64): the packed words stream at a
-// sustained rate and the N-dependent on-chip work adds on top.  Wide kernel: per launch,
+// Cost model, fitted to MI355X measurements of both paths: N = 8 .. 1024 sweeps on the OPT-30B
+// MLP1 and OPT-175B OutProj shapes plus N = 8 .. 64 on every benchmark shape (it picks the
+// faster path in all 40 of those cases).  Skinny kernels (N <= 64): the packed words stream
+// at a sustained rate and the N-dependent on-chip work adds on top.  Wide kernel: per launch,
 // the larger of the stream time and the MFMA time (it overlaps the two).  Dense GEMM:
 // matrix stream plus MFMA time.
-constexpr double kSparseBytesPerUs = 5.6e6;   // packed words, B/us
+constexpr double kSparseBytesPerUs = 6.8e6;   // packed words, B/us
 constexpr double kNarrowFlopsPerUs = 2.0e9;   // dense-equivalent flop/us, N <= 64
 constexpr double kWideFlopsPerUs = 4.5e8;     // dense-equivalent flop/us, N > 64
 constexpr double kSparseCallUs = 8.0;         // fixed cost per sparse launch
-constexpr double kDenseBytesPerUs = 5.4e6;
-constexpr double kDenseFlopsPerUs = 1.6e9;
+constexpr double kDenseBytesPerUs = 5.8e6;
+constexpr double kDenseFlopsPerUs = 1.8e9;
 constexpr double kDenseCallUs = 6.0;
 
 void model(int64_t M, int64_t K, int64_t nnz_padded, int64_t T, int32_t N, double* ts, double* td) {
