@@ -43,8 +43,9 @@ def parse():
     ap.add_argument("--shape", type=int, default=0, help="config 5 only: 0 QKV, 1 OutProj, 2 MLP1, 3 MLP2")
     ap.add_argument("--n", type=int, default=None, help="batch width N (default: the config's)")
     ap.add_argument("--sparsity", type=float, default=None, help="override the config's sparsity")
-    ap.add_argument("--format", choices=("tiled-csl", "bitmap"), default="tiled-csl",
-                    help="sparse format of A: Tiled-CSL (the method's, default) or the bitmap-tile variant")
+    ap.add_argument("--format", choices=("tiled-csl", "bitmap", "three-level"), default="tiled-csl",
+                    help="sparse format of A: Tiled-CSL (the method's, default), the bitmap-tile variant or "
+                         "the three-level (4:2 + slot filling + residual) variant")
     ap.add_argument("--copies", type=int, default=0, help="encoded copies rotated in the timed loop (0: auto)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense hipBLASLt baseline")
@@ -261,6 +262,9 @@ def main():
     if args.format == "bitmap":
         words, offs = L.lscd_pack_bitmap(case.A16, case.mask)
         h0 = L.lscd_encode_bitmap(case.A16, case.mask)
+    elif args.format == "three-level":
+        words, offs = L.lscd_pack_three_level(case.A16, case.mask)
+        h0 = L.lscd_encode_three_level(case.A16, case.mask)
     else:
         tm = L.lscd_default_tile_m(M, K)       # the tile height lscd_encode would use
         words, offs = L.lscd_pack(case.A16, case.mask, tm, 64)
@@ -270,6 +274,8 @@ def main():
     copies = args.copies or max(2, min(32, math.ceil(3 * MALL_BYTES / fmt_bytes) + 1))
     if args.format == "bitmap":
         handles = [h0] + [L.lscd_encode_bitmap(case.A16, case.mask) for _ in range(copies - 1)]
+    elif args.format == "three-level":
+        handles = [h0] + [L.lscd_encode_three_level(case.A16, case.mask) for _ in range(copies - 1)]
     else:
         handles = [h0] + [L.lscd_import(words, offs, M, K, tm, 64) for _ in range(copies - 1)]
     del words, offs
@@ -279,8 +285,8 @@ def main():
 
     nnz, tiles = info["nnz"], info["num_tiles"]
     split = info["splits"][L.npad_index(N)]
-    # Tiled-CSL: one 4-byte word per nonzero; bitmap tiles: the blob as stored (masks + values)
-    stored = 4 * info["nnz_padded"] if args.format == "bitmap" else 4 * nnz
+    # Tiled-CSL: one 4-byte word per nonzero; bitmap and three-level tiles: the blob as stored
+    stored = 4 * info["nnz_padded"] if args.format != "tiled-csl" else 4 * nnz
     alg_bytes = stored + 4 * (tiles + 1) + 2 * K * N + 2 * M * N
     flops = 2 * M * N * K
 
@@ -353,7 +359,7 @@ def main():
         "config": {"workload": case.name, "format": args.format, "M": M, "K": K, "N": N,
                    "sparsity": round(case.sparsity, 4),
                    "nnz": nnz, "tile": f"{info['tile_m']}x{info['tile_k']}", "splits": split,
-                   "variant": ["shared-B", "independent-4", "independent-8", "wide", "bitmap"][info["variant"][L.npad_index(N)]],
+                   "variant": ["shared-B", "independent-4", "independent-8", "wide", "bitmap", "three-level"][info["variant"][L.npad_index(N)]],
                    "copies_rotated": copies, "gpu": props.name, "cus": props.multi_processor_count},
         "tflops": round(flops / (ms_step * 1e-3) / 1e12, 2),
         "pct_roofline": round(100 * value / HBM_PEAK_GBS, 1),

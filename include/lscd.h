@@ -66,12 +66,14 @@ typedef struct {
     int32_t splits[3];          /* K-splits across workgroups lscd_spmm uses for N padded to
                                    16, 32 and 64 (1: no second pass)                        */
     int32_t variant[3];         /* product kernel variant for N padded to 16, 32, 64:
-                                   0 shared B tile, 1 / 2 independent wavefronts (4 / 8)    */
+                                   0 shared B tile, 1 / 2 independent wavefronts (4 / 8),
+                                   4 bitmap tiles, 5 three-level tiles                      */
     int32_t splits_wide[3];     /* K-splits for N > 64, per launch of N padded to 128, 192,
                                    256 (N > 256 runs one launch per 256 columns)            */
     int32_t reg_vectors_wide;   /* 128-bit staging registers per thread, N > 64 kernel      */
-    int32_t format;             /* 0 Tiled-CSL, 1 bitmap tiles (lscd_encode_bitmap); for
-                                   bitmap handles nnz_padded counts the blob's 32-bit words */
+    int32_t format;             /* 0 Tiled-CSL, 1 bitmap tiles (lscd_encode_bitmap), 2 three-
+                                   level tiles (lscd_encode_three_level); for formats 1 and 2
+                                   nnz_padded counts the blob's 32-bit words                */
 } lscd_info_t;
 
 #define LSCD_DEFAULT_TILE_M 64
@@ -156,6 +158,47 @@ lscd_status_t lscd_pack_bitmap_size(const uint16_t* A, const uint8_t* mask, int6
 lscd_status_t lscd_pack_bitmap(const uint16_t* A, const uint8_t* mask, int64_t M, int64_t K, uint32_t* words,
                                int64_t words_len, uint32_t* tile_offsets, int64_t tile_offsets_len);
 lscd_status_t lscd_encode_bitmap(const uint16_t* A, const uint8_t* mask, int64_t M, int64_t K, lscd_handle_t* out);
+
+/*
+ * Three-level tiles (the follow-up summary of the pages, gist.science, section "Metodologia",
+ * part 1: a 4:2 structured layer for the sparse matrix instructions, a slot-filling layer
+ * whose entries occupy the slots the 4:2 layer leaves unused and whose positions are 4-bit
+ * distances, and a residual layer).  Tiles are 64 x 64, in row-block-major order; an empty
+ * tile stores nothing; tile_offsets (num_tiles + 1 entries) count 16-byte units.  A non-empty
+ * tile is 1280 words plus its residual words:
+ *   words 0..1023: 4:2 slots, fp16, in the operand order of v_smfmac_f32_16x16x64_f16:
+ *     operand i (0..3), lane l (0..63) at words 4*(64*i + l) .. +3 hold row 16*i + l%16,
+ *     columns 16*(l/16) .. +15; slot s (0..7) covers the group of columns 4*(s/2) .. +3 and
+ *     sits in the low (even s) or high half of word s/2.  The first two kept entries of a
+ *     group (ascending column) take its two slots; an unused slot holds +0.
+ *   words 1024 + 4*l .. +3 (lane l): 2-bit in-group positions of operands 0 and 1 (low and
+ *     high 16 bits, slot s at bits 2s..2s+1), the same for operands 2 and 3, the fill mask
+ *     (bit 8*i + s: the slot holds a slot-filling entry), the codes (code k in bits
+ *     4k..4k+3).  An unused slot's position is the lowest in-group position with no kept
+ *     entry.
+ *   slot filling: the third and fourth kept entries of the groups in lane l's region (its
+ *     four rows x 16 columns; region position p = 16*i + column % 16) are placed, in
+ *     ascending p, into the region's unused slots in order 8*i + s.  Code k is d - 1 for the
+ *     distance d to the previous placed point (the first from p = -1); a gap above 16 is
+ *     bridged by a dummy point (+0) 16 positions on; at most 8 codes.  The first entry or
+ *     dummy that finds no free slot or code ends the placement for the region.
+ *   residual: the remaining entries as (fp16 bits | (r*64 + c) << 16) words in ascending
+ *     in-tile position, padded to a multiple of four with copies of the last word.
+ *
+ * lscd_pack_three_level_size / lscd_pack_three_level -- host only, same argument rules as
+ *   lscd_pack_bitmap: the encoding into caller arrays of nwords words and num_tiles + 1
+ *   offsets.
+ * lscd_encode_three_level -- pack and upload.  lscd_spmm runs the three-level kernel in
+ *   launches of up to 64 columns (4:2 slots on the structured-sparse MFMA straight from
+ *   registers; slot-filling and residual entries through a dense LDS tile and the dense
+ *   MFMA); lscd_export, lscd_debug_decode and lscd_attach_dense work as for the bitmap format.
+ */
+lscd_status_t lscd_pack_three_level_size(const uint16_t* A, const uint8_t* mask, int64_t M, int64_t K,
+                                         int64_t* nwords, int64_t* num_tiles);
+lscd_status_t lscd_pack_three_level(const uint16_t* A, const uint8_t* mask, int64_t M, int64_t K, uint32_t* words,
+                                    int64_t words_len, uint32_t* tile_offsets, int64_t tile_offsets_len);
+lscd_status_t lscd_encode_three_level(const uint16_t* A, const uint8_t* mask, int64_t M, int64_t K,
+                                      lscd_handle_t* out);
 
 /*
  * lscd_encode_device -- lscd_encode for a matrix already in device memory: the encoding

@@ -34,6 +34,7 @@ LSCD_MAX_N = 65535
 #: Every entry point include/lscd.h declares.
 EXPORTS = ("lscd_pack_size", "lscd_pack", "lscd_default_tile_m", "lscd_encode", "lscd_encode_tiled", "lscd_encode_device",
            "lscd_pack_bitmap_size", "lscd_pack_bitmap", "lscd_encode_bitmap",
+           "lscd_pack_three_level_size", "lscd_pack_three_level", "lscd_encode_three_level",
            "lscd_import", "lscd_export",
            "lscd_get_info", "lscd_spmm", "lscd_debug_decode", "lscd_attach_dense", "lscd_linear",
            "lscd_linear_path", "lscd_set_linear_crossover", "lscd_linear_model", "lscd_destroy",
@@ -73,6 +74,9 @@ def _load():
         "lscd_pack_bitmap_size": [VP, VP, I64, I64, P(I64), P(I64)],
         "lscd_pack_bitmap": [VP, VP, I64, I64, VP, I64, VP, I64],
         "lscd_encode_bitmap": [VP, VP, I64, I64, P(VP)],
+        "lscd_pack_three_level_size": [VP, VP, I64, I64, P(I64), P(I64)],
+        "lscd_pack_three_level": [VP, VP, I64, I64, VP, I64, VP, I64],
+        "lscd_encode_three_level": [VP, VP, I64, I64, P(VP)],
         "lscd_import": [VP, I64, VP, I64, I64, I32, I32, P(VP)],
         "lscd_export": [VP, VP, VP],
         "lscd_get_info": [VP, P(lscd_info_t)],
@@ -209,6 +213,27 @@ def lscd_encode_bitmap(A16, mask=None) -> Handle:
     A16, m, pa, pm = _host_A(A16, mask)
     h = ctypes.c_void_p()
     _check(_lib.lscd_encode_bitmap(pa, pm, A16.shape[0], A16.shape[1], ctypes.byref(h)), "lscd_encode_bitmap")
+    return Handle(h.value)
+
+
+def lscd_pack_three_level(A16, mask=None):
+    """Host-only three-level encoding: (words uint32[nwords], tile_offsets uint32[T+1] in 16-byte units)."""
+    A16, m, pa, pm = _host_A(A16, mask)
+    nw, nt = ctypes.c_int64(), ctypes.c_int64()
+    _check(_lib.lscd_pack_three_level_size(pa, pm, A16.shape[0], A16.shape[1], ctypes.byref(nw), ctypes.byref(nt)),
+           "lscd_pack_three_level_size")
+    words = np.empty(max(nw.value, 1), dtype=np.uint32)
+    offs = np.empty(nt.value + 1, dtype=np.uint32)
+    _check(_lib.lscd_pack_three_level(pa, pm, A16.shape[0], A16.shape[1], words.ctypes.data, nw.value,
+                                      offs.ctypes.data, nt.value + 1), "lscd_pack_three_level")
+    return words[:nw.value], offs
+
+
+def lscd_encode_three_level(A16, mask=None) -> Handle:
+    A16, m, pa, pm = _host_A(A16, mask)
+    h = ctypes.c_void_p()
+    _check(_lib.lscd_encode_three_level(pa, pm, A16.shape[0], A16.shape[1], ctypes.byref(h)),
+           "lscd_encode_three_level")
     return Handle(h.value)
 
 

@@ -161,6 +161,16 @@ lscd_status_t new_handle(const Grid& g, int64_t nnz, int64_t nwords, int32_t max
             if (h->S[i] > 1) part = std::max<int64_t>(part, (int64_t)h->S[i] * g.M * npad * 4);
         }
     }
+    if (format == 2) {
+        // three-level tiles: one kernel, launches of <= 64 columns
+        for (int i = 0; i < 3 && kernel_tile; ++i) {
+            const int npad = 16 << i;
+            h->kind[i] = kKernelThreeLevel;
+            const int occ = spmm_blocks_per_cu(kKernelThreeLevel, npad, 0, (int)std::min<int64_t>(g.K, 1 << 30));
+            h->S[i] = plan_splits(g, h->cus, occ, g.MB, 8, false);
+            if (h->S[i] > 1) part = std::max<int64_t>(part, (int64_t)h->S[i] * g.M * npad * 4);
+        }
+    }
     if (format == 0) h->R = tall ? pick_reg_vectors_tall(maxw) : pick_reg_vectors(maxw);
     for (int i = 0; i < 3 && kernel_tile && format == 0; ++i) {
         // Tiles taller than 64 rows: eight wavefronts per row block for N <= 32, the shared B
@@ -395,6 +405,71 @@ lscd_status_t lscd_encode_bitmap(const uint16_t* A, const uint8_t* mask, int64_t
     }
 }
 
+lscd_status_t lscd_pack_three_level_size(const uint16_t* A, const uint8_t* mask, int64_t M, int64_t K,
+                                         int64_t* nwords, int64_t* num_tiles) {
+    try {
+        Grid g;
+        if (!A || !nwords || !num_tiles || !lscd::make_grid(M, K, lscd::kTileM, lscd::kTileK, &g))
+            return LSCD_ERROR_INVALID_VALUE;
+        std::vector<uint32_t> offs;
+        int64_t nnz = 0;
+        lscd_status_t st = lscd::three_level_offsets(A, mask, g, &offs, &nnz);
+        if (st != LSCD_SUCCESS) return st;
+        *nwords = 4 * (int64_t)offs[(size_t)g.T];
+        *num_tiles = g.T;
+        return LSCD_SUCCESS;
+    } catch (const std::bad_alloc&) {
+        return LSCD_ERROR_OUT_OF_MEMORY;
+    } catch (...) {
+        return LSCD_ERROR_INVALID_VALUE;
+    }
+}
+
+lscd_status_t lscd_pack_three_level(const uint16_t* A, const uint8_t* mask, int64_t M, int64_t K, uint32_t* words,
+                                    int64_t words_len, uint32_t* tile_offsets, int64_t tile_offsets_len) {
+    try {
+        Grid g;
+        if (!A || !tile_offsets || !lscd::make_grid(M, K, lscd::kTileM, lscd::kTileK, &g))
+            return LSCD_ERROR_INVALID_VALUE;
+        std::vector<uint32_t> offs;
+        int64_t nnz = 0;
+        lscd_status_t st = lscd::three_level_offsets(A, mask, g, &offs, &nnz);
+        if (st != LSCD_SUCCESS) return st;
+        const int64_t nw = 4 * (int64_t)offs[(size_t)g.T];
+        if (tile_offsets_len < g.T + 1 || words_len < nw || (nw > 0 && !words)) return LSCD_ERROR_INVALID_VALUE;
+        lscd::three_level_fill(A, mask, g, offs.data(), words);
+        memcpy(tile_offsets, offs.data(), (size_t)(g.T + 1) * 4);
+        return LSCD_SUCCESS;
+    } catch (const std::bad_alloc&) {
+        return LSCD_ERROR_OUT_OF_MEMORY;
+    } catch (...) {
+        return LSCD_ERROR_INVALID_VALUE;
+    }
+}
+
+lscd_status_t lscd_encode_three_level(const uint16_t* A, const uint8_t* mask, int64_t M, int64_t K,
+                                      lscd_handle_t* out) {
+    try {
+        Grid g;
+        if (!A || !out || !lscd::make_grid(M, K, lscd::kTileM, lscd::kTileK, &g)) return LSCD_ERROR_INVALID_VALUE;
+        *out = nullptr;
+        std::vector<uint32_t> offs;
+        int64_t nnz = 0;
+        lscd_status_t st = lscd::three_level_offsets(A, mask, g, &offs, &nnz);
+        if (st != LSCD_SUCCESS) return st;
+        const int64_t nw = 4 * (int64_t)offs[(size_t)g.T];
+        std::vector<uint32_t> words((size_t)std::max<int64_t>(nw, 1));
+        lscd::three_level_fill(A, mask, g, offs.data(), words.data());
+        int32_t maxw = 0;
+        for (int64_t t = 0; t < g.T; ++t) maxw = std::max<int32_t>(maxw, (int32_t)(4 * (offs[t + 1] - offs[t])));
+        return make_handle(words.data(), nw, offs.data(), g, nnz, maxw, out, 2);
+    } catch (const std::bad_alloc&) {
+        return LSCD_ERROR_OUT_OF_MEMORY;
+    } catch (...) {
+        return LSCD_ERROR_INVALID_VALUE;
+    }
+}
+
 lscd_status_t lscd_encode_device(const void* A, const void* mask, int64_t M, int64_t K, void* stream,
                                  lscd_handle_t* out) {
     Grid g;
@@ -515,7 +590,7 @@ lscd_status_t lscd_spmm(lscd_handle_t h, const void* B, void* C, int32_t N, void
     if (N == 0) return LSCD_SUCCESS;
     if (!B || !C || !aligned16(B) || !aligned16(C)) return LSCD_ERROR_INVALID_VALUE;
     if (N > LSCD_MAX_N) return LSCD_ERROR_NOT_SUPPORTED;
-    if (!kernel_shape(h->g) || (h->format == 1 && h->g.tm != lscd::kTileM)) return LSCD_ERROR_NOT_SUPPORTED;
+    if (!kernel_shape(h->g) || (h->format != 0 && h->g.tm != lscd::kTileM)) return LSCD_ERROR_NOT_SUPPORTED;
     const int nb = std::min(N, lscd::kWideMaxN);  // columns of B read by one launch
     if ((int64_t)nb * h->g.K * 2 >= ((int64_t)1 << 31)) return LSCD_ERROR_NOT_SUPPORTED;  // B as one buffer
     lscd_status_t st = check_device(h);
@@ -543,6 +618,27 @@ lscd_status_t lscd_spmm(lscd_handle_t h, const void* B, void* C, int32_t N, void
             a.items = a.G * a.S;
             a.per_xcd = (a.items + 7) / 8;
             hipError_t e = lscd::launch_spmm(lscd::kKernelBitmap, npad, h->R, a, 8 * a.per_xcd, s);
+            if (e != hipSuccess) return hip_status(e);
+            if (a.S > 1) {
+                e = lscd::launch_reduce(h->d_part, a.C, a.S, (int64_t)n * h->g.M, s);
+                if (e != hipSuccess) return hip_status(e);
+            }
+        }
+        return LSCD_SUCCESS;
+    }
+    if (h->format == 2) {
+        // three-level tiles: launches of up to 64 columns
+        for (int32_t c0 = 0; c0 < N; c0 += lscd::kThreeLevelMaxN) {
+            const int32_t n = std::min(N - c0, lscd::kThreeLevelMaxN);
+            const int npad = n <= 16 ? 16 : (n <= 32 ? 32 : 64);
+            a.B = (const uint16_t*)B + (int64_t)c0 * h->g.K;
+            a.C = (uint16_t*)C + (int64_t)c0 * h->g.M;
+            a.N = n;
+            a.G = (int32_t)h->g.MB;
+            a.S = h->S[npad_index(n)];
+            a.items = a.G * a.S;
+            a.per_xcd = (a.items + 7) / 8;
+            hipError_t e = lscd::launch_spmm(lscd::kKernelThreeLevel, npad, 0, a, 8 * a.per_xcd, s);
             if (e != hipSuccess) return hip_status(e);
             if (a.S > 1) {
                 e = lscd::launch_reduce(h->d_part, a.C, a.S, (int64_t)n * h->g.M, s);
@@ -587,7 +683,7 @@ lscd_status_t lscd_spmm(lscd_handle_t h, const void* B, void* C, int32_t N, void
 
 lscd_status_t lscd_debug_decode(lscd_handle_t h, void* A_dense, void* stream) {
     if (!h || !A_dense || !aligned16(A_dense)) return LSCD_ERROR_INVALID_VALUE;
-    if (!kernel_shape(h->g) || (h->format == 1 && h->g.tm != lscd::kTileM)) return LSCD_ERROR_NOT_SUPPORTED;
+    if (!kernel_shape(h->g) || (h->format != 0 && h->g.tm != lscd::kTileM)) return LSCD_ERROR_NOT_SUPPORTED;
     lscd_status_t st = check_device(h);
     if (st != LSCD_SUCCESS) return st;
     lscd::DecodeArgs a;
@@ -602,6 +698,7 @@ lscd_status_t lscd_debug_decode(lscd_handle_t h, void* A_dense, void* stream) {
     a.TM = h->g.tm;
     const int64_t grid = (h->g.T + lscd::kWaves - 1) / lscd::kWaves;
     if (h->format == 1) return hip_status(lscd::launch_decode_bitmap(a, (int)grid, (hipStream_t)stream));
+    if (h->format == 2) return hip_status(lscd::launch_decode_three_level(a, (int)grid, (hipStream_t)stream));
     return hip_status(lscd::launch_decode(h->R, a, (int)grid, (hipStream_t)stream));
 }
 

@@ -48,6 +48,16 @@ void pack_fill(const uint16_t* A, const uint8_t* mask, const Grid& g, const uint
 lscd_status_t bitmap_offsets(const uint16_t* A, const uint8_t* mask, const Grid& g,
                              std::vector<uint32_t>* offsets, int64_t* nnz);
 void bitmap_fill(const uint16_t* A, const uint8_t* mask, const Grid& g, const uint32_t* offsets, uint32_t* words);
+// Three-level variant (4:2 layer, slot filling, residual), 64 x 64 tiles: count pass -> offsets
+// in 16-byte units; fill pass into caller storage.
+constexpr int kThreeLevelValueWords = 1024;  // 4 operands x 64 lanes x 8 fp16 slots
+constexpr int kThreeLevelMetaWords = 256;    // per lane: positions 0|1, positions 2|3, fill mask, codes
+constexpr int kThreeLevelFixedWords = kThreeLevelValueWords + kThreeLevelMetaWords;
+constexpr int kThreeLevelMaxCodes = 8;
+lscd_status_t three_level_offsets(const uint16_t* A, const uint8_t* mask, const Grid& g,
+                                  std::vector<uint32_t>* offsets, int64_t* nnz);
+void three_level_fill(const uint16_t* A, const uint8_t* mask, const Grid& g, const uint32_t* offsets,
+                      uint32_t* words);
 // Validate an imported encoding; fills nnz and the largest tile.
 lscd_status_t validate_format(const uint32_t* words, int64_t nwords, const uint32_t* offsets,
                               const Grid& g, int64_t* nnz, int32_t* max_tile_words);
@@ -96,6 +106,11 @@ constexpr int kWideMaxN = 256;
 // padded to 16 or 32 per launch (wider N runs launches of 32 columns).
 constexpr int kKernelBitmap = 4;
 constexpr int kBitmapMaxN = 32;
+// Three-level tiles (4:2 layer on the structured-sparse MFMA, slot filling, residual): one
+// kernel, launches of <= 64 columns.
+constexpr int kKernelThreeLevel = 5;
+constexpr int kThreeLevelMaxN = 64;
+hipError_t launch_decode_three_level(const DecodeArgs& a, int grid, hipStream_t s);
 int pick_reg_vectors_bitmap(int32_t max_tile_words);
 hipError_t launch_decode_bitmap(const DecodeArgs& a, int grid, hipStream_t s);
 // Staging registers per thread and tile of the wide variant (1, 2 or 4).
@@ -133,7 +148,7 @@ struct lscd_handle_s {
     int R = 2;
     int S[3] = {1, 1, 1};     // K splits used by lscd_spmm for N padded to 16, 32, 64
     int kind[3] = {0, 0, 0};  // product kernel variant for N padded to 16, 32, 64
-    int format = 0;           // 0 Tiled-CSL, 1 bitmap tiles
+    int format = 0;           // 0 Tiled-CSL, 1 bitmap tiles, 2 three-level tiles
     int Rw = 1;               // staging vectors per thread of the wide (N > 64) variant
     int Sw[3] = {1, 1, 1};    // K splits of the wide variant for N padded to 128, 192, 256
     uint32_t* d_words = nullptr;

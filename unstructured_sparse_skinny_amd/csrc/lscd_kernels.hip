@@ -37,6 +37,7 @@ namespace {
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 half16 __attribute__((ext_vector_type(16)));
 
 typedef __attribute__((address_space(4))) const uint32_t kconst_u32;
 
@@ -935,6 +936,288 @@ __global__ __launch_bounds__(256) void spmm_bitmap_kernel(SpmmArgs a) {
     }
 }
 
+// ---------------------------------------------------------------- three-level tiles
+// Format (follow-up summary of the pages, section "Metodologia", three-level storage):
+// a 64 x 64 tile holds 1024 words of 4:2 slots, stored in the operand registers' order of
+// v_smfmac_f32_16x16x64_f16 (operand i, lane l: row 16i + l%16, columns 16*(l/16) .. +15,
+// two slots per group of four columns), 256 words of per-lane metadata (2-bit positions of
+// operands 0|1 and 2|3, fill mask, 4-bit distance codes) and the residual words.  Load as
+// sparse, compute as sparse: the slots go from HBM into the structured-sparse MFMA without
+// passing through LDS.  The entries that do not fit the 4:2 pattern -- slot-filled ones
+// (their value sits in a slot the 4:2 layer leaves unused, their position is the running sum
+// of the codes) and residual ones -- are placed into a dense LDS tile, as in Tiled-CSL, and
+// enter through a dense MFMA on the same B operand registers.
+constexpr int kTLFixedUnits = kThreeLevelFixedWords / 4;  // 16-byte units before the residual words
+constexpr int kTLValueBytes = kThreeLevelValueWords * 4;
+constexpr int kTLSlotStride = 80;  // bytes per lane of the slot copy: 16-byte stores of 8 lanes hit distinct banks
+
+// Slot-filling layer of one tile: copy the lane's 32 slots to Ps, move each filled slot's
+// value to its decoded position in the dense tile As and clear the slot, then reload the
+// slots.  p runs over the lane's region (4 rows x 16 columns): p = 16*i + column % 16.
+__device__ __forceinline__ void three_level_fill(u32x4 (&va)[4], uint32_t fill, uint32_t codes, unsigned char* As,
+                                                 unsigned char* Ps, int lane) {
+    u32x4* pv = reinterpret_cast<u32x4*>(Ps + lane * kTLSlotStride);
+    uint16_t* ph = reinterpret_cast<uint16_t*>(Ps + lane * kTLSlotStride);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pv[i] = va[i];
+    uint32_t p = 0xFFFFFFFFu;
+#pragma unroll
+    for (int k = 0; k < kThreeLevelMaxCodes; ++k) {
+        if (!__any(fill != 0u)) break;
+        if (fill != 0u) {
+            const uint32_t j = (uint32_t)__builtin_ctz(fill);  // slot 8*i + s = halfword j of the copy
+            fill &= fill - 1u;
+            p += ((codes >> (4 * k)) & 15u) + 1u;
+            const uint16_t x = ph[j];
+            ph[j] = 0;
+            const uint32_t r = 16u * ((p >> 4) & 3u) + ((uint32_t)lane & 15u);
+            const uint32_t c = 16u * ((uint32_t)lane >> 4) + (p & 15u);
+            *reinterpret_cast<uint16_t*>(As + r * kRowBytes + ((c * 2u) ^ ((r & 7u) << 4))) = x;
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) va[i] = pv[i];
+}
+
+// acc[i][j] += 4:2 slots of operand i (x B columns 16j..16j+15) and, when `dense`, the dense
+// tile As; both read the same B registers (k = 8q..8q+7 and 32+8q..32+8q+7 for q = lane/16).
+template <int NPAD>
+__device__ __forceinline__ void three_level_mma(f32x4 (&acc)[4][NPAD / 16], const u32x4 (&va)[4], uint32_t idx01,
+                                                uint32_t idx23, const unsigned char* As, const unsigned char* Bw,
+                                                bool dense, int lane) {
+    const uint32_t rl = lane & 15, kq = lane >> 4;
+    const half8 a0 = __builtin_bit_cast(half8, va[0]), a1 = __builtin_bit_cast(half8, va[1]);
+    const half8 a2 = __builtin_bit_cast(half8, va[2]), a3 = __builtin_bit_cast(half8, va[3]);
+#pragma unroll
+    for (int j = 0; j < NPAD / 16; ++j) {
+        const half8 b0 = *reinterpret_cast<const half8*>(Bw + lds_chunk(j * 16 + rl, kq));
+        const half8 b1 = *reinterpret_cast<const half8*>(Bw + lds_chunk(j * 16 + rl, 4 + kq));
+        const half16 bb = __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
+        acc[0][j] = __builtin_amdgcn_smfmac_f32_16x16x64_f16(a0, bb, acc[0][j], (int)idx01, 0, 0);
+        acc[1][j] = __builtin_amdgcn_smfmac_f32_16x16x64_f16(a1, bb, acc[1][j], (int)idx01, 0, 1);
+        acc[2][j] = __builtin_amdgcn_smfmac_f32_16x16x64_f16(a2, bb, acc[2][j], (int)idx23, 0, 0);
+        acc[3][j] = __builtin_amdgcn_smfmac_f32_16x16x64_f16(a3, bb, acc[3][j], (int)idx23, 0, 1);
+        if (dense) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const half8 f0 = *reinterpret_cast<const half8*>(As + lds_chunk(i * 16 + rl, kq));
+                const half8 f1 = *reinterpret_cast<const half8*>(As + lds_chunk(i * 16 + rl, 4 + kq));
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(f0, b0, acc[i][j], 0, 0, 0);
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(f1, b1, acc[i][j], 0, 0, 0);
+            }
+        }
+    }
+}
+
+// Three-level product, organised like the bitmap kernel: a workgroup owns one row block and
+// its WK wavefronts split the k range; each wavefront has its own dense tile, slot copy and B
+// tile, and needs no barrier until the final sum over wavefronts.
+template <int NPAD, int WK, bool VEC>
+__global__ __launch_bounds__(WK * 64) void spmm_three_level_kernel(SpmmArgs a) {
+    constexpr int P = 2;
+    constexpr int kBBytes = NPAD * kRowBytes;
+    constexpr int kWaveBytes = kTileBytes + 64 * kTLSlotStride + kBBytes;
+    static_assert(NPAD * kTileM * 4 <= kWaveBytes, "the reduction reuses each wavefront's area");
+    __shared__ __attribute__((aligned(16))) unsigned char smem[WK * kWaveBytes];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    unsigned char* As = smem + wave * kWaveBytes;
+    unsigned char* Ps = As + kTileBytes;
+    unsigned char* Bw = Ps + 64 * kTLSlotStride;
+
+    const int bid = blockIdx.x;
+    const int item = (bid & 7) * a.per_xcd + (bid >> 3);
+    if (item >= a.items) return;
+    const int s = item / a.G;
+    const int rb = item - s * a.G;
+    const int ks0 = (int)(((int64_t)s * a.KT) / a.S);
+    const int ks1 = (int)(((int64_t)(s + 1) * a.KT) / a.S);
+    const int kt0 = ks0 + (wave * (ks1 - ks0)) / WK;
+    const int kt1 = ks0 + ((wave + 1) * (ks1 - ks0)) / WK;
+    const kconst_u32* toff = (const kconst_u32*)(a.offs) + (int64_t)rb * a.KT;
+    const __amdgpu_buffer_rsrc_t bsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)a.B, (short)0, a.N * a.K * 2, kBufWord3);
+
+    u32x4 va[P][4];  // 4:2 slots of operands 0..3
+    u32x4 vm[P];     // metadata: positions 0|1, positions 2|3, fill mask, codes
+    u32x4 vr[P];     // residual words of unit `lane`
+    int nres[P];     // residual units of the tile, -1 for an empty tile
+    uint32_t first[P];
+    BWave<NPAD, VEC> bf[P];
+    auto fetch = [&](int q, int k) {
+        uint32_t o0 = 0, o1 = 0;
+        if (k < kt1) {
+            o0 = toff[k];
+            o1 = toff[k + 1];
+        }
+        const int units = (int)(o1 - o0);
+        first[q] = o0;
+        nres[q] = units > 0 ? units - kTLFixedUnits : -1;
+        // the descriptor covers exactly the tile: an empty tile or a lane past the residual
+        // words reads zeros without a fetch
+        __amdgpu_buffer_rsrc_t rs =
+            __builtin_amdgcn_make_buffer_rsrc((void*)(a.words + 4 * (size_t)o0), (short)0, units * 16, kBufWord3);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            va[q][i] = __builtin_amdgcn_raw_buffer_load_b128(rs, (i * 64 + lane) * 16, 0, kStreamPolicy);
+        vm[q] = __builtin_amdgcn_raw_buffer_load_b128(rs, kTLValueBytes + lane * 16, 0, kStreamPolicy);
+        vr[q] = __builtin_amdgcn_raw_buffer_load_b128(rs, (kTLFixedUnits + lane) * 16, 0, kStreamPolicy);
+        bf[q].load(bsrc, a.B, a.N, a.K, k, lane, k < kt1);
+    };
+#pragma unroll
+    for (int q = 0; q < P; ++q) fetch(q, kt0 + q);
+
+    zero_tile(As, lane);
+    f32x4 acc[4][NPAD / 16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < NPAD / 16; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    for (int kt = kt0; kt < kt1; kt += P) {
+#pragma unroll
+        for (int q = 0; q < P; ++q) {
+            const int k = kt + q;
+            const int nr = nres[q];
+            if (nr >= 0) {
+                bf[q].store(Bw, lane);
+                const uint32_t fill = vm[q][2];
+                const bool any_fill = __any(fill != 0u);
+                const bool dense = any_fill || nr > 0;
+                if (any_fill) three_level_fill(va[q], fill, vm[q][3], As, Ps, lane);
+                if (nr > 0) {
+                    if (lane < nr) {
+                        put_word(As, vr[q][0]);
+                        put_word(As, vr[q][1]);
+                        put_word(As, vr[q][2]);
+                        put_word(As, vr[q][3]);
+                    }
+                    const uint32_t* rw = a.words + 4 * ((size_t)first[q] + kTLFixedUnits);
+                    for (int u = 64 + lane; u < nr; u += 64) {
+                        const u32x4 x = *reinterpret_cast<const u32x4*>(rw + 4 * (size_t)u);
+                        put_word(As, x[0]);
+                        put_word(As, x[1]);
+                        put_word(As, x[2]);
+                        put_word(As, x[3]);
+                    }
+                }
+                three_level_mma<NPAD>(acc, va[q], vm[q][0], vm[q][1], As, Bw, dense, lane);
+                if (dense) zero_tile(As, lane);
+            }
+            fetch(q, k + P);
+        }
+    }
+
+    // the wavefronts' sums, added in wavefront order
+    float* red = reinterpret_cast<float*>(smem + wave * kWaveBytes);
+    const int ncol = lane & 15;
+    const int mq = (lane >> 4) * 4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < NPAD / 16; ++j)
+            *reinterpret_cast<f32x4*>(red + (j * 16 + ncol) * kTileM + i * 16 + mq) = acc[i][j];
+    __syncthreads();
+    const bool vec_m = (a.M & 3) == 0;
+    for (int it = tid; it < a.N * (kTileM / 4); it += WK * 64) {
+        const int nn = it / (kTileM / 4);
+        const int ml = (it - nn * (kTileM / 4)) * 4;
+        f32x4 sum = *reinterpret_cast<const f32x4*>(smem + (nn * kTileM + ml) * 4);
+#pragma unroll
+        for (int w = 1; w < WK; ++w)
+            sum += *reinterpret_cast<const f32x4*>(smem + w * kWaveBytes + (nn * kTileM + ml) * 4);
+        const int m = rb * kTileM + ml;
+        if (m >= a.M) continue;
+        if (a.S == 1) {
+            uint16_t* dst = a.C + (int64_t)nn * a.M + m;
+            if (vec_m) {
+                uint2 pk;
+                pk.x = (uint32_t)f16_bits(sum[0]) | ((uint32_t)f16_bits(sum[1]) << 16);
+                pk.y = (uint32_t)f16_bits(sum[2]) | ((uint32_t)f16_bits(sum[3]) << 16);
+                *reinterpret_cast<uint2*>(dst) = pk;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (m + e < a.M) dst[e] = f16_bits(sum[e]);
+            }
+        } else {
+            float* dst = a.part + ((int64_t)s * a.N + nn) * a.M + m;
+            if (vec_m) {
+                *reinterpret_cast<f32x4*>(dst) = sum;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (m + e < a.M) dst[e] = sum[e];
+            }
+        }
+    }
+}
+
+// Dense view of a three-level encoding: slot filling and residual through the product
+// kernel's placement code, then the 4:2 slots that are not filled, at their positions.
+__global__ __launch_bounds__(kThreads) void decode_three_level_kernel(DecodeArgs a) {
+    __shared__ __attribute__((aligned(16))) unsigned char smem[kWaves * (kTileBytes + 64 * kTLSlotStride)];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    unsigned char* As = smem + wave * (kTileBytes + 64 * kTLSlotStride);
+    unsigned char* Ps = As + kTileBytes;
+    const int64_t t = (int64_t)blockIdx.x * kWaves + wave;
+    const bool act = t < a.T;
+    uint32_t o0 = 0, o1 = 0;
+    if (act) {
+        o0 = a.offs[t];
+        o1 = a.offs[t + 1];
+    }
+    zero_tile(As, lane);
+    if (o1 > o0) {
+        const uint32_t* tw = a.words + 4 * (size_t)o0;
+        const int nr = (int)(o1 - o0) - kTLFixedUnits;
+        u32x4 va[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) va[i] = *reinterpret_cast<const u32x4*>(tw + 4 * (i * 64 + lane));
+        const u32x4 vm = *reinterpret_cast<const u32x4*>(tw + kThreeLevelValueWords + 4 * lane);
+        three_level_fill(va, vm[2], vm[3], As, Ps, lane);
+        for (int u = lane; u < nr; u += 64) {
+            const u32x4 x = *reinterpret_cast<const u32x4*>(tw + 4 * ((size_t)kTLFixedUnits + u));
+            put_word(As, x[0]);
+            put_word(As, x[1]);
+            put_word(As, x[2]);
+            put_word(As, x[3]);
+        }
+        const uint32_t r0 = (uint32_t)lane & 15u, cq = 16u * ((uint32_t)lane >> 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t idx = (i < 2 ? vm[0] : vm[1]) >> (16 * (i & 1));
+#pragma unroll
+            for (int sl = 0; sl < 8; ++sl) {
+                if ((vm[2] >> (8 * i + sl)) & 1u) continue;
+                const uint32_t r = 16u * i + r0;
+                const uint32_t c = cq + 4u * (sl >> 1) + ((idx >> (2 * sl)) & 3u);
+                const uint16_t v = (uint16_t)(va[i][sl >> 1] >> (16 * (sl & 1)));
+                *reinterpret_cast<uint16_t*>(As + r * kRowBytes + ((c * 2u) ^ ((r & 7u) << 4))) = v;
+            }
+        }
+    }
+    if (!act) return;
+    const int64_t bm = t / a.KT, bk = t - bm * a.KT;
+    // the tile in row order: lane -> (row, 16-byte chunk); 8 chunks per row
+    for (int v = lane; v < kTileM * 8; v += 64) {
+        const int r = v >> 3, ch = v & 7;
+        const int64_t gr = bm * kTileM + r;
+        if (gr >= a.M) continue;
+        const u32x4 x = *reinterpret_cast<const u32x4*>(As + lds_chunk(r, ch));
+        const int64_t gc = bk * kTileK + ch * 8;
+        uint16_t* dst = a.A + gr * a.K + gc;
+        const uint16_t h[8] = {(uint16_t)x[0], (uint16_t)(x[0] >> 16), (uint16_t)x[1], (uint16_t)(x[1] >> 16),
+                               (uint16_t)x[2], (uint16_t)(x[2] >> 16), (uint16_t)x[3], (uint16_t)(x[3] >> 16)};
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            if (gc + e < a.K) dst[e] = h[e];
+    }
+}
+
 // Dense view of a bitmap encoding through the same staging and placement code.
 __global__ __launch_bounds__(kThreads) void decode_bitmap_kernel(DecodeArgs a) {
     __shared__ __attribute__((aligned(16))) unsigned char smem[2 * kWaves * kTileBytes];
@@ -1160,6 +1443,22 @@ hipError_t launch_bitmap_any(int npad, int R, const SpmmArgs& a, int grid, hipSt
     }
 }
 
+template <int NPAD, int WK>
+hipError_t launch_three_level_n(const SpmmArgs& a, int grid, hipStream_t st, int* occ) {
+    if ((a.K & 7) != 0) return run(spmm_three_level_kernel<NPAD, WK, false>, a, grid, st, occ, WK * 64);
+    return run(spmm_three_level_kernel<NPAD, WK, true>, a, grid, st, occ, WK * 64);
+}
+
+// N padded to 64: two wavefronts per workgroup (each wavefront's LDS area grows with its B tile)
+hipError_t launch_three_level_any(int npad, const SpmmArgs& a, int grid, hipStream_t st, int* occ) {
+    switch (npad) {
+        case 16: return launch_three_level_n<16, 4>(a, grid, st, occ);
+        case 32: return launch_three_level_n<32, 4>(a, grid, st, occ);
+        case 64: return launch_three_level_n<64, 2>(a, grid, st, occ);
+        default: return hipErrorInvalidValue;
+    }
+}
+
 template <int NW, int RG>
 hipError_t launch_wide_rg(int R, const SpmmArgs& a, int grid, hipStream_t st, int* occ) {
     if ((a.K & 7) != 0) return run(spmm_wide_kernel<NW, (RG == 4 ? 4 : 8), false, RG>, a, grid, st, occ);
@@ -1250,6 +1549,7 @@ int pick_reg_vectors_wide(int32_t max_tile_words) {
 hipError_t launch_spmm(int kind, int npad, int R, const SpmmArgs& a, int grid, hipStream_t st) {
     if (kind == kKernelWide) return launch_wide_any(npad, R, a, grid, st, nullptr);
     if (kind == kKernelBitmap) return launch_bitmap_any(npad, R, a, grid, st, nullptr);
+    if (kind == kKernelThreeLevel) return launch_three_level_any(npad, a, grid, st, nullptr);
     switch (npad) {
         case 16: return launch_spmm_n<16>(kind, R, a, grid, st, nullptr);
         case 32: return launch_spmm_n<32>(kind, R, a, grid, st, nullptr);
@@ -1267,6 +1567,8 @@ int spmm_blocks_per_cu(int kind, int npad, int R, int K, int TM) {
     if (kind == kKernelWide) return (launch_wide_any(npad, R, dummy, 0, nullptr, &occ) == hipSuccess && occ > 0) ? occ : 1;
     if (kind == kKernelBitmap)
         return (launch_bitmap_any(npad, R, dummy, 0, nullptr, &occ) == hipSuccess && occ > 0) ? occ : 1;
+    if (kind == kKernelThreeLevel)
+        return (launch_three_level_any(npad, dummy, 0, nullptr, &occ) == hipSuccess && occ > 0) ? occ : 1;
     switch (npad) {
         case 16: e = launch_spmm_n<16>(kind, R, dummy, 0, nullptr, &occ); break;
         case 32: e = launch_spmm_n<32>(kind, R, dummy, 0, nullptr, &occ); break;
@@ -1286,6 +1588,11 @@ hipError_t launch_reduce(const float* part, uint16_t* C, int S, int64_t NM, hipS
 
 hipError_t launch_decode_bitmap(const DecodeArgs& a, int grid, hipStream_t st) {
     hipLaunchKernelGGL(decode_bitmap_kernel, dim3(grid), dim3(kThreads), 0, st, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_three_level(const DecodeArgs& a, int grid, hipStream_t st) {
+    hipLaunchKernelGGL(decode_three_level_kernel, dim3(grid), dim3(kThreads), 0, st, a);
     return hipGetLastError();
 }
 

@@ -253,6 +253,176 @@ void bitmap_fill(const uint16_t* A, const uint8_t* mask, const Grid& g, const ui
     });
 }
 
+// ---------------------------------------------------------------- three-level tiles
+// Layout (follow-up summary of the pages, section "Metodologia", three-level storage format):
+// 64 x 64 tiles; operand i (0..3) and lane l (0..63) of a tile own row 16i + l%16 and
+// columns 16*(l/16) .. +15, the lane mapping of the 16x16x64 structured-sparse MFMA.
+//   4:2 layer: per group of four columns, slots 2g and 2g+1 hold the first two kept entries
+//     with their 2-bit in-group positions; an unused slot holds +0 and the lowest in-group
+//     position without a kept entry.
+//   slot filling: the third and fourth kept entries of the groups of a lane's region (its 4
+//     rows x 16 columns) go, in ascending region position p = 16i + column%16, into the
+//     region's unused slots in slot order j = 8i + s; each costs a 4-bit code d - 1 (d = its
+//     distance to the previous one, from -1); a gap above 16 gets a +0 dummy 16 positions on;
+//     at most 8 codes; the first entry or dummy without a slot or a code stops the placement.
+//   residual: the rest, as (fp16 | (r*64 + c) << 16) words in ascending position, padded to
+//     a multiple of four with copies of the last word.
+// Blob per non-empty tile: 1024 value words (operand-major, 4 words per lane), 256 metadata
+// words (per lane: positions of operands 0|1, positions of operands 2|3, fill mask, codes),
+// residual words.  Offsets count 16-byte units.
+
+namespace {
+
+struct ThreeLevelTile {
+    uint32_t fixed[kThreeLevelFixedWords];
+    std::vector<uint32_t> residual;
+};
+
+// Build tile (bm, bk) of the three-level format; false when it has no kept entry.
+bool three_level_tile(const uint16_t* A, const uint8_t* mask, const Grid& g, int64_t bm, int64_t bk,
+                      ThreeLevelTile* out, int64_t* nnz) {
+    uint8_t km[64][64];
+    uint16_t kv[64][64];
+    memset(km, 0, sizeof km);
+    memset(kv, 0, sizeof kv);
+    int64_t n = 0;
+    const int64_t r0 = bm * 64, c0 = bk * 64;
+    const int64_t r1 = std::min<int64_t>(g.M, r0 + 64), c1 = std::min<int64_t>(g.K, c0 + 64);
+    for (int64_t r = r0; r < r1; ++r) {
+        const size_t base = (size_t)r * (size_t)g.K;
+        for (int64_t c = c0; c < c1; ++c) {
+            if (kept(A, mask, base + (size_t)c)) {
+                km[r - r0][c - c0] = 1;
+                kv[r - r0][c - c0] = A[base + (size_t)c];
+                ++n;
+            }
+        }
+    }
+    *nnz = n;
+    if (n == 0) return false;
+    memset(out->fixed, 0, sizeof out->fixed);
+    out->residual.clear();
+    uint16_t* vals = reinterpret_cast<uint16_t*>(out->fixed);  // [operand][lane][slot]
+    uint32_t* meta = out->fixed + kThreeLevelValueWords;       // [lane][4]
+    for (int l = 0; l < 64; ++l) {
+        const int q = l >> 4, lr = l & 15;
+        int ex_p[32], ex_rc[32], nex = 0;
+        uint16_t ex_v[32];
+        int unused[32], nun = 0;
+        uint32_t idx16[4] = {0, 0, 0, 0};
+        for (int i = 0; i < 4; ++i) {
+            const int r = 16 * i + lr;
+            for (int gi = 0; gi < 4; ++gi) {
+                const int cb = 16 * q + 4 * gi;
+                int kc[4], fc[4], nk = 0, nf = 0;
+                for (int c = 0; c < 4; ++c) {
+                    if (km[r][cb + c]) kc[nk++] = c;
+                    else fc[nf++] = c;
+                }
+                for (int s = 0; s < 2; ++s) {
+                    const int slot = 2 * gi + s;
+                    if (s < nk) {
+                        vals[(i * 64 + l) * 8 + slot] = kv[r][cb + kc[s]];
+                        idx16[i] |= (uint32_t)kc[s] << (2 * slot);
+                    } else {
+                        idx16[i] |= (uint32_t)fc[s - nk] << (2 * slot);
+                        unused[nun++] = 8 * i + slot;
+                    }
+                }
+                for (int e = 2; e < nk; ++e) {  // ascending region position by construction
+                    ex_p[nex] = 16 * i + 4 * gi + kc[e];
+                    ex_rc[nex] = r * 64 + cb + kc[e];
+                    ex_v[nex] = kv[r][cb + kc[e]];
+                    ++nex;
+                }
+            }
+        }
+        uint32_t fill = 0, codes = 0;
+        int prev = -1, k = 0, u = 0;
+        bool stopped = false;
+        for (int e = 0; e < nex; ++e) {
+            if (!stopped) {
+                while (ex_p[e] - prev > 16) {
+                    if (u >= nun || k >= kThreeLevelMaxCodes) {
+                        stopped = true;
+                        break;
+                    }
+                    fill |= 1u << unused[u++];  // dummy point: the slot keeps +0
+                    codes |= 15u << (4 * k++);
+                    prev += 16;
+                }
+                if (!stopped && (u >= nun || k >= kThreeLevelMaxCodes)) stopped = true;
+            }
+            if (stopped) {
+                out->residual.push_back((uint32_t)ex_v[e] | ((uint32_t)ex_rc[e] << 16));
+                continue;
+            }
+            const int j = unused[u++];
+            fill |= 1u << j;
+            codes |= (uint32_t)(ex_p[e] - prev - 1) << (4 * k++);
+            prev = ex_p[e];
+            vals[((j >> 3) * 64 + l) * 8 + (j & 7)] = ex_v[e];
+        }
+        meta[4 * l + 0] = idx16[0] | (idx16[1] << 16);
+        meta[4 * l + 1] = idx16[2] | (idx16[3] << 16);
+        meta[4 * l + 2] = fill;
+        meta[4 * l + 3] = codes;
+    }
+    std::vector<uint32_t>& rw = out->residual;
+    std::sort(rw.begin(), rw.end(), [](uint32_t x, uint32_t y) { return (x >> 16) < (y >> 16); });
+    while (!rw.empty() && (rw.size() & 3)) rw.push_back(rw.back());
+    return true;
+}
+
+}  // namespace
+
+lscd_status_t three_level_offsets(const uint16_t* A, const uint8_t* mask, const Grid& g,
+                                  std::vector<uint32_t>* offsets, int64_t* nnz_out) {
+    if (g.tm != 64 || g.tk != 64) return LSCD_ERROR_INVALID_VALUE;
+    std::vector<uint32_t> units((size_t)g.T, 0);
+    std::vector<int64_t> cnt((size_t)g.MB, 0);
+    parallel_for(g.MB, [&](int64_t lo, int64_t hi) {
+        ThreeLevelTile tile;
+        for (int64_t bm = lo; bm < hi; ++bm) {
+            for (int64_t bk = 0; bk < g.KT; ++bk) {
+                int64_t n = 0;
+                if (three_level_tile(A, mask, g, bm, bk, &tile, &n))
+                    units[(size_t)(bm * g.KT + bk)] = (uint32_t)((kThreeLevelFixedWords + tile.residual.size()) / 4);
+                cnt[(size_t)bm] += n;
+            }
+        }
+    });
+    offsets->assign((size_t)g.T + 1, 0);
+    uint64_t run = 0;
+    int64_t nnz = 0;
+    for (int64_t bm = 0; bm < g.MB; ++bm) nnz += cnt[(size_t)bm];
+    for (int64_t t = 0; t < g.T; ++t) {
+        run += units[(size_t)t];
+        if (run * 4 >= ((uint64_t)1 << 32)) return LSCD_ERROR_NOT_SUPPORTED;
+        (*offsets)[(size_t)t + 1] = (uint32_t)run;
+    }
+    *nnz_out = nnz;
+    return LSCD_SUCCESS;
+}
+
+void three_level_fill(const uint16_t* A, const uint8_t* mask, const Grid& g, const uint32_t* offsets,
+                      uint32_t* words) {
+    parallel_for(g.MB, [&](int64_t lo, int64_t hi) {
+        ThreeLevelTile tile;
+        for (int64_t bm = lo; bm < hi; ++bm) {
+            for (int64_t bk = 0; bk < g.KT; ++bk) {
+                const int64_t t = bm * g.KT + bk;
+                int64_t n = 0;
+                if (!three_level_tile(A, mask, g, bm, bk, &tile, &n)) continue;
+                uint32_t* dst = words + 4 * (size_t)offsets[t];
+                memcpy(dst, tile.fixed, sizeof tile.fixed);
+                if (!tile.residual.empty())
+                    memcpy(dst + kThreeLevelFixedWords, tile.residual.data(), tile.residual.size() * 4);
+            }
+        }
+    });
+}
+
 lscd_status_t validate_format(const uint32_t* words, int64_t nwords, const uint32_t* offsets,
                               const Grid& g, int64_t* nnz_out, int32_t* maxw_out) {
     if (offsets[0] != 0 || (int64_t)offsets[g.T] != nwords) return LSCD_ERROR_INVALID_FORMAT;
