@@ -197,6 +197,34 @@ def test_pack_bitmap_matches_oracle(M, K, keep):
     assert np.array_equal(w2, ow2) and np.array_equal(o2, oo2)
 
 
+@pytest.mark.parametrize("M,K,keep", [(64, 64, 0.5), (130, 200, 0.5), (1, 1, 1.0), (65, 129, 0.9), (100, 300, 0.0),
+                                      (257, 700, 0.45), (200, 130, 0.05), (128, 64, 1.0)])
+def test_pack_three_level_matches_oracle(M, K, keep):
+    """The three-level layout is fully determined (slot order, codes, residual order), so the
+    host encoder must equal the oracle's encoding word for word."""
+    from oracle import three_level as otl
+    case = syn.random_case(M, K, 1, keep, seed=M + 5 * K)
+    words, offs = L.lscd_pack_three_level(case.A16, case.mask)
+    ow, oo = otl.encode(case.A16, case.mask)
+    assert np.array_equal(offs, oo)
+    assert np.array_equal(words, ow)
+    A = case.A16.copy()
+    A[case.mask == 0] = 0
+    A[0, 0] = 0x8000                                         # -0 is dropped without a mask
+    w2, o2 = L.lscd_pack_three_level(A, None)
+    m2 = ((A & 0x7FFF) != 0).astype(np.uint8)
+    ow2, oo2 = otl.encode(A, m2)
+    assert np.array_equal(w2, ow2) and np.array_equal(o2, oo2)
+
+
+def test_pack_three_level_size_and_errors():
+    case = syn.random_case(100, 100, 1, 0.5, seed=1)
+    words, offs = L.lscd_pack_three_level(case.A16, case.mask)
+    assert offs.size == 5 and words.size == 4 * int(offs[-1]) and words.size >= 4 * 1280
+    with pytest.raises(L.LSCDError):
+        L.lscd_pack_three_level(np.zeros((0, 5), dtype=np.uint16), None)
+
+
 @pytest.mark.parametrize("tm", [80, 96, 112, 128])
 @pytest.mark.parametrize("M,K,keep", [(300, 200, 0.3), (129, 64 * 3 + 5, 1.0), (1, 1, 1.0), (500, 130, 0.05)])
 def test_pack_tall_tiles_matches_oracle(tm, M, K, keep):
