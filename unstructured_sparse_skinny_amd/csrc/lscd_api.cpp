@@ -167,7 +167,9 @@ lscd_status_t new_handle(const Grid& g, int64_t nnz, int64_t nwords, int32_t max
             const int npad = 16 << i;
             h->kind[i] = kKernelThreeLevel;
             const int occ = spmm_blocks_per_cu(kKernelThreeLevel, npad, 0, (int)std::min<int64_t>(g.K, 1 << 30));
-            h->S[i] = plan_splits(g, h->cus, occ, g.MB, 8, false);
+            // N padded to 64: workgroups of four row blocks sharing the B tile
+            const int64_t groups = npad == 64 ? (g.MB + kWaves - 1) / kWaves : g.MB;
+            h->S[i] = plan_splits(g, h->cus, occ, groups, 8, false);
             if (h->S[i] > 1) part = std::max<int64_t>(part, (int64_t)h->S[i] * g.M * npad * 4);
         }
     }
@@ -634,7 +636,7 @@ lscd_status_t lscd_spmm(lscd_handle_t h, const void* B, void* C, int32_t N, void
             a.B = (const uint16_t*)B + (int64_t)c0 * h->g.K;
             a.C = (uint16_t*)C + (int64_t)c0 * h->g.M;
             a.N = n;
-            a.G = (int32_t)h->g.MB;
+            a.G = (int32_t)(npad == 64 ? (h->g.MB + lscd::kWaves - 1) / lscd::kWaves : h->g.MB);
             a.S = h->S[npad_index(n)];
             a.items = a.G * a.S;
             a.per_xcd = (a.items + 7) / 8;

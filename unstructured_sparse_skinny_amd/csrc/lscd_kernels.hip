@@ -954,25 +954,34 @@ constexpr int kTLSlotStride = 80;  // bytes per lane of the slot copy: 16-byte s
 // Slot-filling layer of one tile: copy the lane's 32 slots to Ps, move each filled slot's
 // value to its decoded position in the dense tile As and clear the slot, then reload the
 // slots.  p runs over the lane's region (4 rows x 16 columns): p = 16*i + column % 16.
+// Slots and positions are worked out first, so that the LDS reads of all eight points are in
+// flight together.
 __device__ __forceinline__ void three_level_fill(u32x4 (&va)[4], uint32_t fill, uint32_t codes, unsigned char* As,
                                                  unsigned char* Ps, int lane) {
     u32x4* pv = reinterpret_cast<u32x4*>(Ps + lane * kTLSlotStride);
     uint16_t* ph = reinterpret_cast<uint16_t*>(Ps + lane * kTLSlotStride);
 #pragma unroll
     for (int i = 0; i < 4; ++i) pv[i] = va[i];
+    uint32_t slot[kThreeLevelMaxCodes], dst[kThreeLevelMaxCodes];
     uint32_t p = 0xFFFFFFFFu;
+    const uint32_t n = (uint32_t)__popc(fill);
 #pragma unroll
     for (int k = 0; k < kThreeLevelMaxCodes; ++k) {
-        if (!__any(fill != 0u)) break;
-        if (fill != 0u) {
-            const uint32_t j = (uint32_t)__builtin_ctz(fill);  // slot 8*i + s = halfword j of the copy
-            fill &= fill - 1u;
-            p += ((codes >> (4 * k)) & 15u) + 1u;
-            const uint16_t x = ph[j];
-            ph[j] = 0;
-            const uint32_t r = 16u * ((p >> 4) & 3u) + ((uint32_t)lane & 15u);
-            const uint32_t c = 16u * ((uint32_t)lane >> 4) + (p & 15u);
-            *reinterpret_cast<uint16_t*>(As + r * kRowBytes + ((c * 2u) ^ ((r & 7u) << 4))) = x;
+        slot[k] = (uint32_t)__builtin_ctz(fill | 0x80000000u);  // filled slot 8*i + s = halfword of the copy
+        fill &= fill - 1u;
+        p += ((codes >> (4 * k)) & 15u) + 1u;
+        const uint32_t r = 16u * ((p >> 4) & 3u) + ((uint32_t)lane & 15u);
+        const uint32_t c = 16u * ((uint32_t)lane >> 4) + (p & 15u);
+        dst[k] = r * kRowBytes + ((c * 2u) ^ ((r & 7u) << 4));
+    }
+    uint16_t x[kThreeLevelMaxCodes];
+#pragma unroll
+    for (int k = 0; k < kThreeLevelMaxCodes; ++k) x[k] = (uint32_t)k < n ? ph[slot[k]] : (uint16_t)0;
+#pragma unroll
+    for (int k = 0; k < kThreeLevelMaxCodes; ++k) {
+        if ((uint32_t)k < n) {
+            ph[slot[k]] = 0;
+            *reinterpret_cast<uint16_t*>(As + dst[k]) = x[k];
         }
     }
 #pragma unroll
@@ -988,6 +997,14 @@ __device__ __forceinline__ void three_level_mma(f32x4 (&acc)[4][NPAD / 16], cons
     const uint32_t rl = lane & 15, kq = lane >> 4;
     const half8 a0 = __builtin_bit_cast(half8, va[0]), a1 = __builtin_bit_cast(half8, va[1]);
     const half8 a2 = __builtin_bit_cast(half8, va[2]), a3 = __builtin_bit_cast(half8, va[3]);
+    half8 f[4][2];
+    if (dense) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            f[i][0] = *reinterpret_cast<const half8*>(As + lds_chunk(i * 16 + rl, kq));
+            f[i][1] = *reinterpret_cast<const half8*>(As + lds_chunk(i * 16 + rl, 4 + kq));
+        }
+    }
 #pragma unroll
     for (int j = 0; j < NPAD / 16; ++j) {
         const half8 b0 = *reinterpret_cast<const half8*>(Bw + lds_chunk(j * 16 + rl, kq));
@@ -1000,10 +1017,8 @@ __device__ __forceinline__ void three_level_mma(f32x4 (&acc)[4][NPAD / 16], cons
         if (dense) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const half8 f0 = *reinterpret_cast<const half8*>(As + lds_chunk(i * 16 + rl, kq));
-                const half8 f1 = *reinterpret_cast<const half8*>(As + lds_chunk(i * 16 + rl, 4 + kq));
-                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(f0, b0, acc[i][j], 0, 0, 0);
-                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(f1, b1, acc[i][j], 0, 0, 0);
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(f[i][0], b0, acc[i][j], 0, 0, 0);
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(f[i][1], b1, acc[i][j], 0, 0, 0);
             }
         }
     }
@@ -1149,6 +1164,156 @@ __global__ __launch_bounds__(WK * 64) void spmm_three_level_kernel(SpmmArgs a) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
                     if (m + e < a.M) dst[e] = sum[e];
+            }
+        }
+    }
+}
+
+// N padded to 64: four wavefronts own four consecutive row blocks and share one B tile per k
+// step, staged by the whole workgroup into a double buffer (one barrier per step).  With a
+// private B tile per wavefront, the 8 KB of B per step would outweigh the ~5.5 KB of the A
+// tile it multiplies (B is re-read from L2 by every row block).
+template <int NPAD, bool VEC>
+__global__ __launch_bounds__(kThreads) void spmm_three_level_shared_kernel(SpmmArgs a) {
+    constexpr int P = 2;
+    constexpr int kWaveBytes = kTileBytes + 64 * kTLSlotStride;
+    __shared__ __attribute__((aligned(16))) unsigned char smem[kWaves * kWaveBytes + 2 * NPAD * kRowBytes];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    unsigned char* As = smem + wave * kWaveBytes;
+    unsigned char* Ps = As + kTileBytes;
+    unsigned char* Bs0 = smem + kWaves * kWaveBytes;
+
+    const int bid = blockIdx.x;
+    const int item = (bid & 7) * a.per_xcd + (bid >> 3);
+    if (item >= a.items) return;  // whole workgroup
+    const int s = item / a.G;
+    const int g = item - s * a.G;
+    const int kt0 = (int)(((int64_t)s * a.KT) / a.S);
+    const int kt1 = (int)(((int64_t)(s + 1) * a.KT) / a.S);
+    const int rb = g * kWaves + wave;
+    const bool active = rb < a.MB;
+    const kconst_u32* toff = (const kconst_u32*)(a.offs) + (int64_t)(active ? rb : 0) * a.KT;
+    const __amdgpu_buffer_rsrc_t bsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)a.B, (short)0, a.N * a.K * 2, kBufWord3);
+
+    // B rows n >= N stay zero for the whole kernel (both buffers).
+    for (int ch = tid; ch < 2 * NPAD * 8; ch += kThreads) {
+        const int row = ch >> 3;
+        if (row % NPAD >= a.N) {
+            const u32x4 z = {0u, 0u, 0u, 0u};
+            *reinterpret_cast<u32x4*>(Bs0 + row * kRowBytes + (ch & 7) * 16) = z;
+        }
+    }
+
+    u32x4 va[P][4];
+    u32x4 vm[P];
+    u32x4 vr[P];
+    int nres[P];
+    uint32_t first[P];
+    BStage<NPAD, VEC> bst[P];
+    auto fetch = [&](int q, int k) {
+        uint32_t o0 = 0, o1 = 0;
+        if (active && k < kt1) {
+            o0 = toff[k];
+            o1 = toff[k + 1];
+        }
+        const int units = (int)(o1 - o0);
+        first[q] = o0;
+        nres[q] = units > 0 ? units - kTLFixedUnits : -1;
+        __amdgpu_buffer_rsrc_t rs =
+            __builtin_amdgcn_make_buffer_rsrc((void*)(a.words + 4 * (size_t)o0), (short)0, units * 16, kBufWord3);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            va[q][i] = __builtin_amdgcn_raw_buffer_load_b128(rs, (i * 64 + lane) * 16, 0, kStreamPolicy);
+        vm[q] = __builtin_amdgcn_raw_buffer_load_b128(rs, kTLValueBytes + lane * 16, 0, kStreamPolicy);
+        vr[q] = __builtin_amdgcn_raw_buffer_load_b128(rs, (kTLFixedUnits + lane) * 16, 0, kStreamPolicy);
+        bst[q].load(bsrc, a.B, a.N, a.K, k, tid, k < kt1);
+    };
+#pragma unroll
+    for (int q = 0; q < P; ++q) fetch(q, kt0 + q);
+
+    zero_tile(As, lane);
+    f32x4 acc[4][NPAD / 16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < NPAD / 16; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    for (int kt = kt0; kt < kt1; kt += P) {
+#pragma unroll
+        for (int q = 0; q < P; ++q) {
+            const int k = kt + q;
+            unsigned char* Bs = Bs0 + (k & 1) * NPAD * kRowBytes;
+            bst[q].store(Bs, a.N, tid);
+            const int nr = nres[q];
+            bool dense = false;
+            u32x4 cur[4] = {va[q][0], va[q][1], va[q][2], va[q][3]};
+            const uint32_t idx01 = vm[q][0], idx23 = vm[q][1];
+            if (nr >= 0) {
+                const uint32_t fill = vm[q][2];
+                const bool any_fill = __any(fill != 0u);
+                dense = any_fill || nr > 0;
+                if (any_fill) three_level_fill(cur, fill, vm[q][3], As, Ps, lane);
+                if (nr > 0) {
+                    if (lane < nr) {
+                        put_word(As, vr[q][0]);
+                        put_word(As, vr[q][1]);
+                        put_word(As, vr[q][2]);
+                        put_word(As, vr[q][3]);
+                    }
+                    const uint32_t* rw = a.words + 4 * ((size_t)first[q] + kTLFixedUnits);
+                    for (int u = 64 + lane; u < nr; u += 64) {
+                        const u32x4 x = *reinterpret_cast<const u32x4*>(rw + 4 * (size_t)u);
+                        put_word(As, x[0]);
+                        put_word(As, x[1]);
+                        put_word(As, x[2]);
+                        put_word(As, x[3]);
+                    }
+                }
+            }
+            fetch(q, k + P);
+            __syncthreads();
+            if (nr >= 0) three_level_mma<NPAD>(acc, cur, idx01, idx23, As, Bs, dense, lane);
+            if (dense) zero_tile(As, lane);
+        }
+    }
+    // MFMA 16x16 result layout: lane holds column (lane & 15), rows 4*(lane >> 4) + 0..3.
+    const int ncol = lane & 15;
+    const int mrow = rb * kTileM + (lane >> 4) * 4;
+    const bool vec_m = (a.M & 3) == 0;
+    if (active) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+            for (int j = 0; j < NPAD / 16; ++j) {
+                const int n = j * 16 + ncol;
+                const int m = mrow + i * 16;
+                if (n >= a.N || m >= a.M) continue;
+                const f32x4 v = acc[i][j];
+                if (a.S == 1) {
+                    uint16_t* dst = a.C + (int64_t)n * a.M + m;
+                    if (vec_m && m + 3 < a.M) {
+                        uint2 pk;
+                        pk.x = (uint32_t)f16_bits(v[0]) | ((uint32_t)f16_bits(v[1]) << 16);
+                        pk.y = (uint32_t)f16_bits(v[2]) | ((uint32_t)f16_bits(v[3]) << 16);
+                        *reinterpret_cast<uint2*>(dst) = pk;
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (m + e < a.M) dst[e] = f16_bits(v[e]);
+                    }
+                } else {
+                    float* dst = a.part + ((int64_t)s * a.N + n) * a.M + m;
+                    if (vec_m && m + 3 < a.M) {
+                        *reinterpret_cast<f32x4*>(dst) = v;
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (m + e < a.M) dst[e] = v[e];
+                    }
+                }
             }
         }
     }
@@ -1449,12 +1614,15 @@ hipError_t launch_three_level_n(const SpmmArgs& a, int grid, hipStream_t st, int
     return run(spmm_three_level_kernel<NPAD, WK, true>, a, grid, st, occ, WK * 64);
 }
 
-// N padded to 64: two wavefronts per workgroup (each wavefront's LDS area grows with its B tile)
+// N <= 32: the wavefronts of a workgroup split the k range of one row block; N padded to 64:
+// four row blocks share the staged B tile.
 hipError_t launch_three_level_any(int npad, const SpmmArgs& a, int grid, hipStream_t st, int* occ) {
     switch (npad) {
         case 16: return launch_three_level_n<16, 4>(a, grid, st, occ);
         case 32: return launch_three_level_n<32, 4>(a, grid, st, occ);
-        case 64: return launch_three_level_n<64, 2>(a, grid, st, occ);
+        case 64:
+            if ((a.K & 7) != 0) return run(spmm_three_level_shared_kernel<64, false>, a, grid, st, occ);
+            return run(spmm_three_level_shared_kernel<64, true>, a, grid, st, occ);
         default: return hipErrorInvalidValue;
     }
 }
