@@ -228,7 +228,10 @@ lscd_status_t lscd_import(const uint32_t* nonzeros, int64_t nnz_padded, const ui
                           int64_t M, int64_t K, int32_t tile_m, int32_t tile_k, lscd_handle_t* out);
 
 /* lscd_export -- copy the handle's encoding back into host arrays of nnz_padded words
- * and num_tiles + 1 offsets (sizes from lscd_get_info).  Synchronous. */
+ * and num_tiles + 1 offsets (sizes from lscd_get_info).  Synchronous.  The words are in the
+ * format's layout (value | in-tile index << 16) whatever form the device copy keeps: on
+ * kernel tile shapes the handle stores each word with its LDS byte offset in place of the
+ * index, and the export converts back. */
 lscd_status_t lscd_export(lscd_handle_t h, uint32_t* nonzeros, uint32_t* tile_offsets);
 
 /* lscd_get_info -- describe a handle (no device work). */

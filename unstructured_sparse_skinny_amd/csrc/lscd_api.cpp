@@ -225,7 +225,20 @@ lscd_status_t make_handle(const uint32_t* words, int64_t nwords, const uint32_t*
         free_handle(h);
         return hip_status(e);
     }
-    if (nwords > 0 && (e = hipMemcpy(h->d_words, words, (size_t)nwords * 4, hipMemcpyHostToDevice)) != hipSuccess) {
+    if (format == 0 && kernel_shape(g)) {
+        // device form of the words (lds byte offset | value << 16), uploaded in slices
+        const int64_t slice = (int64_t)1 << 22;
+        std::vector<uint32_t> buf((size_t)std::min<int64_t>(std::max<int64_t>(nwords, 1), slice));
+        for (int64_t o = 0; o < nwords; o += slice) {
+            const int64_t n = std::min<int64_t>(slice, nwords - o);
+            lscd::to_device_words(words + o, buf.data(), n);
+            if ((e = hipMemcpy(h->d_words + o, buf.data(), (size_t)n * 4, hipMemcpyHostToDevice)) != hipSuccess) {
+                free_handle(h);
+                return hip_status(e);
+            }
+        }
+    } else if (nwords > 0 &&
+               (e = hipMemcpy(h->d_words, words, (size_t)nwords * 4, hipMemcpyHostToDevice)) != hipSuccess) {
         free_handle(h);
         return hip_status(e);
     }
@@ -557,6 +570,7 @@ lscd_status_t lscd_export(lscd_handle_t h, uint32_t* nonzeros, uint32_t* tile_of
     if (h->nnz_padded > 0 &&
         (e = hipMemcpy(nonzeros, h->d_words, (size_t)h->nnz_padded * 4, hipMemcpyDeviceToHost)) != hipSuccess)
         return hip_status(e);
+    if (h->format == 0 && kernel_shape(h->g)) lscd::to_format_words(nonzeros, h->nnz_padded);
     if ((e = hipMemcpy(tile_offsets, h->d_offs, (size_t)(h->g.T + 1) * 4, hipMemcpyDeviceToHost)) != hipSuccess)
         return hip_status(e);
     return LSCD_SUCCESS;

@@ -154,7 +154,7 @@ __global__ __launch_bounds__(kEncWaves * 64) void enc_fill_kernel(EncArgs a) {
             const unsigned long long bal = __ballot(k);
             if (k) {
                 const uint32_t q = base + (uint32_t)__popcll(bal & below);
-                const uint32_t w = ((uint32_t)(r * kTileK + lane) << 16) | a.A[i];
+                const uint32_t w = device_word((uint32_t)(r * kTileK + lane), a.A[i]);
                 out[slot_of(q, nvec)] = w;
                 last_q = q;
                 last_w = w;
@@ -201,7 +201,7 @@ __global__ __launch_bounds__(kEncWaves * 64) void enc_fill_kernel(EncArgs a) {
         const uint32_t bank = scatter_bank(idx);
         const uint32_t ri = rank[wave][idx];
         const uint32_t q = roff[wave][ri] + (uint32_t)__popcll(rmask[wave][ri] & ((1ull << bank) - 1ull));
-        const uint32_t w = (idx << 16) | a.A[i];
+        const uint32_t w = device_word(idx, a.A[i]);
         out[slot_of(q, nvec)] = w;
         if (q == n - 1u)
             for (uint32_t p = n; p < 4u * nvec; ++p) out[slot_of(p, nvec)] = w;

@@ -58,6 +58,23 @@ lscd_status_t three_level_offsets(const uint16_t* A, const uint8_t* mask, const 
                                   std::vector<uint32_t>* offsets, int64_t* nnz);
 void three_level_fill(const uint16_t* A, const uint8_t* mask, const Grid& g, const uint32_t* offsets,
                       uint32_t* words);
+// Device form of a Tiled-CSL word on a kernel tile shape (64 columns, 64..128 rows): the
+// entry's byte offset in the kernels' swizzled LDS tile (row r at r*128 bytes, 16-byte chunk
+// (c/8) ^ (r%8), 2 bytes per column) in bits [15:0], the fp16 value in bits [31:16].  The
+// format's word is value | (r*64 + c) << 16; handles keep the device form so that the
+// product places a word with one mask, and lscd_export converts back.
+__host__ __device__ inline uint32_t device_word(uint32_t idx, uint32_t value) {
+    const uint32_t r = idx >> 6, c = idx & 63u;
+    return (r * 128u + ((c * 2u) ^ ((r & 7u) << 4))) | (value << 16);
+}
+__host__ __device__ inline uint32_t format_word(uint32_t dw) {
+    const uint32_t b = dw & 0xFFFFu, r = b >> 7;
+    const uint32_t c = ((((b >> 4) & 7u) ^ (r & 7u)) << 3) | ((b >> 1) & 7u);
+    return (dw >> 16) | ((r * 64u + c) << 16);
+}
+// Format words <-> device words, n words, on the host threads.
+void to_device_words(const uint32_t* in, uint32_t* out, int64_t n);
+void to_format_words(uint32_t* words, int64_t n);
 // Validate an imported encoding; fills nnz and the largest tile.
 lscd_status_t validate_format(const uint32_t* words, int64_t nwords, const uint32_t* offsets,
                               const Grid& g, int64_t* nnz, int32_t* max_tile_words);

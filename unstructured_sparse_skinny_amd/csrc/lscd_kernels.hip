@@ -55,9 +55,10 @@ __device__ __forceinline__ uint16_t f16_bits(float x) {
     return __builtin_bit_cast(uint16_t, h);
 }
 
-// Extract one packed word into the wavefront's LDS tile: value bits [15:0] go to the
-// row-major in-tile index in bits [31:16].  The index is masked to the 4096-entry tile,
-// so no word can reach outside the wavefront's own 8 KB.
+// Place one word of the Tiled-CSL layout as written by the encoder (fp16 value in bits
+// [15:0], row-major in-tile index r*64 + c in bits [31:16]) into the wavefront's LDS tile.
+// The index is masked to the 4096-entry tile, so no word can reach outside the wavefront's
+// own 8 KB.  Used for the residual words of the three-level format.
 __device__ __forceinline__ void put_word(unsigned char* As, uint32_t w) {
     uint32_t b = (w >> 15) & 0x1FFEu;  // byte offset r*128 + c*2
     b ^= (b >> 3) & 0x70u;             // chunk ^= row & 7
@@ -91,39 +92,19 @@ __device__ __forceinline__ void zero_rows(unsigned char* As, int lane) {
     for (int j = 0; j < TM * kRowBytes / 1024; ++j) *reinterpret_cast<u32x4*>(As + (j * 64 + lane) * 16) = z;
 }
 
-template <int R>
-__device__ __forceinline__ void scatter_tile(const u32x4 (&wb)[R], int nvec, unsigned char* As,
-                                             const uint32_t* tile_words, int lane) {
-#pragma unroll
-    for (int j = 0; j < R; ++j) {
-        if (j * 64 + lane < nvec) {
-            put_word(As, wb[j][0]);
-            put_word(As, wb[j][1]);
-            put_word(As, wb[j][2]);
-            put_word(As, wb[j][3]);
-        }
-    }
-    // Tiles larger than the register stage: the rest is fetched and placed directly.
-    if (nvec > R * 64) {
-        for (int v = R * 64 + lane; v < nvec; v += 64) {
-            const u32x4 x = *reinterpret_cast<const u32x4*>(tile_words + 4 * (size_t)v);
-            put_word(As, x[0]);
-            put_word(As, x[1]);
-            put_word(As, x[2]);
-            put_word(As, x[3]);
-        }
-    }
-}
-
 // Scatter the register stage and keep, in place of each stored word, its LDS byte offset:
 // once the tile has been multiplied, unscatter() writes zeros at exactly those offsets, which
 // returns the tile to all zeros for a fraction of the cost of clearing all 8 KB.  Words past
 // the register stage (tiles of more than R * 64 vectors) are placed by scatter_rest(); such
 // a tile is cleared whole afterwards.
-__device__ __forceinline__ uint32_t lds_offset(uint32_t w) {
-    uint32_t b = (w >> 15) & 0x3FFEu;  // up to 128 rows of 64
-    return b ^ ((b >> 3) & 0x70u);
-}
+//
+// Device words.  A Tiled-CSL handle on a kernel tile shape keeps its words on the device as
+// (LDS byte offset | fp16 value << 16): the offset is where the entry lands in the swizzled
+// LDS tile (row r*128 bytes, 16-byte chunk (c/8) ^ (r%8), 2 bytes per column), worked out once
+// when the words are uploaded or encoded on the device instead of for every word of every
+// product; lscd_export turns them back into the format.
+__device__ __forceinline__ uint32_t lds_offset(uint32_t w) { return w & 0xFFFFu; }
+__device__ __forceinline__ uint16_t word_value(uint32_t w) { return (uint16_t)(w >> 16); }
 
 template <int R>
 __device__ __forceinline__ void scatter_keep(u32x4 (&wb)[R], int nvec, unsigned char* As, int lane) {
@@ -134,7 +115,7 @@ __device__ __forceinline__ void scatter_keep(u32x4 (&wb)[R], int nvec, unsigned 
             for (int e = 0; e < 4; ++e) {
                 const uint32_t w = wb[j][e];
                 const uint32_t b = lds_offset(w);
-                *reinterpret_cast<uint16_t*>(As + b) = (uint16_t)w;
+                *reinterpret_cast<uint16_t*>(As + b) = word_value(w);
                 wb[j][e] = b;
             }
         }
@@ -146,7 +127,7 @@ __device__ __forceinline__ void scatter_rest(int nvec, unsigned char* As, const 
     for (int v = R * 64 + lane; v < nvec; v += 64) {
         const u32x4 x = *reinterpret_cast<const u32x4*>(tile_words + 4 * (size_t)v);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) *reinterpret_cast<uint16_t*>(As + lds_offset(x[e])) = (uint16_t)x[e];
+        for (int e = 0; e < 4; ++e) *reinterpret_cast<uint16_t*>(As + lds_offset(x[e])) = word_value(x[e]);
     }
 }
 
@@ -191,7 +172,7 @@ __device__ __forceinline__ void scatter_tile_wg(const u32x4 (&wb)[R], int nvec, 
     for (int j = 0; j < R; ++j) {
         if (j * kThreads + tid < nvec) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) *reinterpret_cast<uint16_t*>(As + lds_offset(wb[j][e])) = (uint16_t)wb[j][e];
+            for (int e = 0; e < 4; ++e) *reinterpret_cast<uint16_t*>(As + lds_offset(wb[j][e])) = word_value(wb[j][e]);
         }
     }
 }

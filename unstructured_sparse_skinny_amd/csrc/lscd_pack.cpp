@@ -423,6 +423,20 @@ void three_level_fill(const uint16_t* A, const uint8_t* mask, const Grid& g, con
     });
 }
 
+void to_device_words(const uint32_t* in, uint32_t* out, int64_t n) {
+    parallel_for((n + 65535) / 65536, [&](int64_t lo, int64_t hi) {
+        const int64_t e = std::min<int64_t>(n, hi * 65536);
+        for (int64_t i = lo * 65536; i < e; ++i) out[i] = device_word(in[i] >> 16, in[i] & 0xFFFFu);
+    });
+}
+
+void to_format_words(uint32_t* words, int64_t n) {
+    parallel_for((n + 65535) / 65536, [&](int64_t lo, int64_t hi) {
+        const int64_t e = std::min<int64_t>(n, hi * 65536);
+        for (int64_t i = lo * 65536; i < e; ++i) words[i] = format_word(words[i]);
+    });
+}
+
 lscd_status_t validate_format(const uint32_t* words, int64_t nwords, const uint32_t* offsets,
                               const Grid& g, int64_t* nnz_out, int32_t* maxw_out) {
     if (offsets[0] != 0 || (int64_t)offsets[g.T] != nwords) return LSCD_ERROR_INVALID_FORMAT;
