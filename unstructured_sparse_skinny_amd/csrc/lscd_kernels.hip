@@ -92,8 +92,8 @@ __device__ __forceinline__ void zero_rows(unsigned char* As, int lane) {
     for (int j = 0; j < TM * kRowBytes / 1024; ++j) *reinterpret_cast<u32x4*>(As + (j * 64 + lane) * 16) = z;
 }
 
-// Scatter the register stage and keep, in place of each stored word, its LDS byte offset:
-// once the tile has been multiplied, unscatter() writes zeros at exactly those offsets, which
+// Scatter the register stage and keep, in place of each stored word, its LDS address: once
+// the tile has been multiplied, unscatter() writes zeros at exactly those addresses, which
 // returns the tile to all zeros for a fraction of the cost of clearing all 8 KB.  Words past
 // the register stage (tiles of more than R * 64 vectors) are placed by scatter_rest(); such
 // a tile is cleared whole afterwards.
@@ -106,18 +106,44 @@ __device__ __forceinline__ void zero_rows(unsigned char* As, int lane) {
 __device__ __forceinline__ uint32_t lds_offset(uint32_t w) { return w & 0xFFFFu; }
 __device__ __forceinline__ uint16_t word_value(uint32_t w) { return (uint16_t)(w >> 16); }
 
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+typedef __attribute__((address_space(3))) uint16_t lds_u16;
+
+// 32-bit LDS address of a pointer into shared memory, and a 2-byte store at such an address.
+__device__ __forceinline__ uint32_t lds_address(unsigned char* p) {
+    return (uint32_t)(uintptr_t)(lds_u8*)p;  // address-space cast: shared -> LDS
+}
+__device__ __forceinline__ void lds_store16(uint32_t addr, uint16_t v) {
+    *(lds_u16*)(uintptr_t)addr = v;
+}
+
+// The register stage keeps each word's absolute LDS address, so the reset costs no address
+// arithmetic at all.
 template <int R>
 __device__ __forceinline__ void scatter_keep(u32x4 (&wb)[R], int nvec, unsigned char* As, int lane) {
+    const uint32_t base = lds_address(As);
 #pragma unroll
     for (int j = 0; j < R; ++j) {
         if (j * 64 + lane < nvec) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const uint32_t w = wb[j][e];
-                const uint32_t b = lds_offset(w);
-                *reinterpret_cast<uint16_t*>(As + b) = word_value(w);
-                wb[j][e] = b;
+                const uint32_t a = base + lds_offset(w);
+                lds_store16(a, word_value(w));
+                wb[j][e] = a;
             }
+        }
+    }
+}
+
+// Scatter without keeping the addresses (the tile is cleared whole afterwards).
+template <int R>
+__device__ __forceinline__ void scatter_place(const u32x4 (&wb)[R], int nvec, unsigned char* As, int lane) {
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+        if (j * 64 + lane < nvec) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) *reinterpret_cast<uint16_t*>(As + lds_offset(wb[j][e])) = word_value(wb[j][e]);
         }
     }
 }
@@ -132,12 +158,12 @@ __device__ __forceinline__ void scatter_rest(int nvec, unsigned char* As, const 
 }
 
 template <int R>
-__device__ __forceinline__ void unscatter(const u32x4 (&wb)[R], int nvec, unsigned char* As, int lane) {
+__device__ __forceinline__ void unscatter(const u32x4 (&wb)[R], int nvec, int lane) {
 #pragma unroll
     for (int j = 0; j < R; ++j) {
         if (j * 64 + lane < nvec) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) *reinterpret_cast<uint16_t*>(As + wb[j][e]) = (uint16_t)0;
+            for (int e = 0; e < 4; ++e) lds_store16(wb[j][e], 0);
         }
     }
 }
@@ -354,7 +380,7 @@ __global__ __launch_bounds__(kThreads) void spmm_kernel(SpmmArgs a) {
                 const int n = nv[q];
                 if (n > 0) {
                     zero_rows<TM>(As, lane);
-                    scatter_keep<R>(wb[q], n, As, lane);
+                    scatter_place<R>(wb[q], n, As, lane);
                     if (n > R * 64) scatter_rest<R>(n, As, a.words + first[q], lane);
                 }
                 // refill this register stage with tile k + P
@@ -538,7 +564,7 @@ __global__ __launch_bounds__(WK * 64) void spmm_indep_kernel(SpmmArgs a) {
                 if (n > R * 64 || 4 * n > kUnscatterMaxWords)
                     zero_rows<TM>(As, lane);
                 else
-                    unscatter<R>(wb[q], n, As, lane);
+                    unscatter<R>(wb[q], n, lane);
             }
             uint32_t o0 = 0, o1 = 0;
             if (kn < kt1) {
@@ -1457,7 +1483,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     u32x4 wb[R];
     load_tile<R>(wb, a.words, o0, nvec, lane);
     zero_rows<TM>(As, lane);
-    scatter_keep<R>(wb, nvec, As, lane);
+    scatter_place<R>(wb, nvec, As, lane);
     if (nvec > R * 64) scatter_rest<R>(nvec, As, a.words + o0, lane);
     __syncthreads();
     if (!act) return;
