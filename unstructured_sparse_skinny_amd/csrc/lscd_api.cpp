@@ -167,9 +167,11 @@ lscd_status_t new_handle(const Grid& g, int64_t nnz, int64_t nwords, int32_t max
             const int npad = 16 << i;
             h->kind[i] = kKernelThreeLevel;
             const int occ = spmm_blocks_per_cu(kKernelThreeLevel, npad, 0, (int)std::min<int64_t>(g.K, 1 << 30));
-            // N padded to 64: workgroups of four row blocks sharing the B tile
+            // N padded to 64: workgroups of four row blocks sharing the B tile, splits that fill
+            // the resident slots; N <= 32: one row block per workgroup, splits that balance the
+            // busiest CU (OPT-175B QKV at N = 16: 145 -> 131 us with 4 splits)
             const int64_t groups = npad == 64 ? (g.MB + kWaves - 1) / kWaves : g.MB;
-            h->S[i] = plan_splits(g, h->cus, occ, groups, 8, false);
+            h->S[i] = plan_splits(g, h->cus, occ, groups, 8, npad != 64);
             if (h->S[i] > 1) part = std::max<int64_t>(part, (int64_t)h->S[i] * g.M * npad * 4);
         }
     }
