@@ -13,7 +13,9 @@ Printed (one JSON line on stdout):
   tflops        dense-equivalent 2*M*N*K / wall time per step
   roofline      the product kernel's algorithmic bytes / its average duration from a HIP
                 event pair around the timed steps (one graph replay), against 8 TB/s HBM
-  dense_hipblaslt  the same product as a dense fp16 GEMM (torch -> hipBLASLt), timed the same way
+  dense_hipblaslt  the same product as a dense fp16 GEMM: hipBLASLt with the fastest of its
+                heuristic's candidates (lscd_tune_dense, through lscd_linear), timed the same way;
+                torch.mm's default choice beside it
   cpu_baseline  the CPU oracle on a bounded row sample (reported baseline only)
 """
 import argparse
@@ -318,22 +320,52 @@ def main():
 
     dense = None
     if not args.no_dense:
-        log("[bench] timing dense fp16 GEMM (torch -> hipBLASLt)")
         dense_bytes = 2 * M * K + 2 * K * N + 2 * M * N
+        ncopy = min(len(handles), max(2, min(16, math.ceil(3 * MALL_BYTES / (2 * M * K)) + 1)))
+        Cd = torch.empty((N, M), dtype=torch.float16, device="cuda")
+        # hipBLASLt with the fastest of its heuristic's candidates for this N (lscd_tune_dense),
+        # run through lscd_linear's dense path on dense copies decoded from the encoding and
+        # timed like the sparse product: rotating copies, one graph replay
+        log("[bench] timing dense fp16 GEMM: hipBLASLt, fastest of its heuristic's candidates")
+        tuned = []
+        for h in handles[:ncopy]:
+            L.lscd_attach_dense(h)
+            tuned.append(L.lscd_tune_dense(h, B, Cd))
+            L.lscd_set_linear_crossover(h, 0)
+        lin = L._lib.lscd_linear
+
+        def lin_checked(*a):
+            st = lin(*a)
+            if st != 0:
+                raise L.LSCDError(st, "lscd_linear")
+
+        dcalls = [(lin_checked, (ctypes.c_void_p(h.ptr), ctypes.c_void_p(B.data_ptr()), ctypes.c_void_p(Cd.data_ptr()),
+                                 N, _Cur())) for h in handles[:ncopy]]
+        d_graph = not args.eager
+        try:
+            d_ms, d_mean, _, _, _ = time_calls(dcalls, args.steps, args.warmup, torch, graph=d_graph)
+        except RuntimeError:
+            d_graph = False
+            d_ms, d_mean, _, _, _ = time_calls(dcalls, args.steps, args.warmup, torch, graph=False)
+        # torch.mm on the masked matrix (hipBLASLt through PyTorch, its default choice), eager
+        log("[bench] timing dense fp16 GEMM: torch.mm (default algorithm)")
         Ad = torch.from_numpy(np.where(case.mask.astype(bool), case.A16, 0).astype(np.uint16).view(np.float16))
-        ncopy = max(2, min(16, math.ceil(3 * MALL_BYTES / (2 * M * K)) + 1))
         Ads = [Ad.to("cuda") for _ in range(ncopy)]
         del Ad
-        Cd = torch.empty((N, M), dtype=torch.float16, device="cuda")
-        dcalls = [(lambda x, y: torch.mm(x, y, out=Cd), (B, a.t())) for a in Ads]
-        d_ms, d_mean, d_med, _, _ = time_calls(dcalls, args.steps, args.warmup, torch, graph=False)
+        tcalls = [(lambda x, y: torch.mm(x, y, out=Cd), (B, a.t())) for a in Ads]
+        t_ms, _, _, _, _ = time_calls(tcalls, args.steps, args.warmup, torch, graph=False)
+        del Ads
         dense = {"ms_per_step": round(d_ms, 5), "kernel_ms_mean": round(d_mean, 5),
                  "effective_gbs": round(dense_bytes / (d_ms * 1e-3) / 1e9, 1),
                  "tflops": round(flops / (d_ms * 1e-3) / 1e12, 2), "copies": ncopy,
                  "lscd_speedup": round(d_ms / ms_step, 3),
+                 "library": "hipBLASLt, fastest of %d heuristic candidates (lscd_tune_dense)" % tuned[0][1],
+                 "timing": "one HIP graph replay" if d_graph else "eager, event pair per call",
+                 "tune_us_back_to_back": [round(t[0], 2) for t in tuned],
+                 "torch_mm_ms_per_step": round(t_ms, 5), "lscd_speedup_vs_torch_mm": round(t_ms / ms_step, 3),
                  "blas": str(torch.backends.cuda.preferred_blas_library())}
-        log(f"[bench] dense: {d_ms * 1e3:.1f} us/step -> speedup of lscd {d_ms / ms_step:.2f}x")
-        del Ads
+        log(f"[bench] dense (tuned hipBLASLt): {d_ms * 1e3:.1f} us/step -> speedup of lscd {d_ms / ms_step:.2f}x; "
+            f"torch.mm {t_ms * 1e3:.1f} us/step ({t_ms / ms_step:.2f}x)")
 
     cpu = None
     if not args.no_cpu:

@@ -275,11 +275,25 @@ lscd_status_t lscd_attach_dense(lscd_handle_t h);
 
 /*
  * lscd_linear -- C = A x B like lscd_spmm (same B, C layouts, alignment and errors), run as
- * the sparse product or, when a dense copy is attached and lscd_linear_path says so, as a
- * rocBLAS fp16 GEMM with fp32 accumulation and one fp16 rounding.  Asynchronous on
- * `stream`.  The dense path may allocate inside the GEMM library on its first call.
+ * the sparse product or, when a dense copy is attached and lscd_linear_path says so, as an
+ * fp16 GEMM with fp32 accumulation and one fp16 rounding: the hipBLASLt algorithm that
+ * lscd_tune_dense chose for this N, else rocBLAS.  Asynchronous on `stream`.  The dense path
+ * may allocate inside the GEMM library on its first call.
  */
 lscd_status_t lscd_linear(lscd_handle_t h, const void* B, void* C, int32_t N, void* stream);
+
+/*
+ * lscd_tune_dense -- time up to 16 candidates of hipBLASLt's heuristic for the dense GEMM of
+ * this handle at width N (the comparison the pages make against the vendor dense library,
+ * Flash-LLM review section 6) and keep the fastest for lscd_linear's dense path.  B (N x K)
+ * and C (N x M) are caller device buffers as for lscd_spmm; C is overwritten.  Each candidate
+ * runs 3 times untimed and 20 times back to back between two events on the default stream;
+ * *best_us receives the fastest mean time per GEMM, *candidates how many were timed.
+ * Synchronous.  Needs lscd_attach_dense first (NOT_SUPPORTED otherwise); allocates a 64 MiB
+ * workspace on its first call, freed by lscd_destroy.
+ */
+lscd_status_t lscd_tune_dense(lscd_handle_t h, const void* B, void* C, int32_t N, double* best_us,
+                              int32_t* candidates);
 
 /* lscd_linear_path -- the path lscd_linear takes for N: *path = 0 sparse, 1 dense (dense
  * only with a dense copy attached).  No device work. */

@@ -67,6 +67,25 @@ def test_wide_full_size_sampled_rows():
         assert_gates(C[:, rows], osp.spmm_f64(case.A16, case.mask, B16, rows=rows), f"N={N}")
 
 
+@pytest.mark.parametrize("N", [16, 100])
+def test_tuned_dense_path(N):
+    """lscd_tune_dense times hipBLASLt candidates and lscd_linear then runs the fastest; integer
+    inputs keep the GEMM bit-exact whichever algorithm (any summation order is exact)."""
+    case = syn.random_case(700, 1100, N, 0.3, seed=N + 3, values="int3")
+    h = L.lscd_encode(case.A16, case.mask)
+    B = torch.from_numpy(case.B16.view(np.float16)).to("cuda")
+    C = torch.empty((N, case.M), dtype=torch.float16, device="cuda")
+    with pytest.raises(L.LSCDError):
+        L.lscd_tune_dense(h, B, C)                              # no dense copy yet
+    L.lscd_attach_dense(h)
+    us, n = L.lscd_tune_dense(h, B, C)
+    say(f"tuned dense N={N}: {us:.1f} us over {n} candidates")
+    assert n >= 1 and us > 0
+    L.lscd_set_linear_crossover(h, 0)
+    want = osp.fp16_rne(osp.spmm_f64(case.A16, case.mask, case.B16))
+    assert np.array_equal(run(L.lscd_linear, h, case.B16, case.M), want)
+
+
 def test_linear_paths():
     case = syn.random_case(500, 900, 96, 0.3, seed=21, values="int3")
     h = L.lscd_encode(case.A16, case.mask)

@@ -37,7 +37,7 @@ EXPORTS = ("lscd_pack_size", "lscd_pack", "lscd_default_tile_m", "lscd_encode", 
            "lscd_pack_three_level_size", "lscd_pack_three_level", "lscd_encode_three_level",
            "lscd_import", "lscd_export",
            "lscd_get_info", "lscd_spmm", "lscd_debug_decode", "lscd_attach_dense", "lscd_linear",
-           "lscd_linear_path", "lscd_set_linear_crossover", "lscd_linear_model", "lscd_destroy",
+           "lscd_linear_path", "lscd_set_linear_crossover", "lscd_linear_model", "lscd_tune_dense", "lscd_destroy",
            "lscd_status_string")
 
 
@@ -87,6 +87,7 @@ def _load():
         "lscd_linear_path": [VP, I32, P(I32)],
         "lscd_set_linear_crossover": [VP, I32],
         "lscd_linear_model": [I64, I64, I64, I64, I32, P(ctypes.c_double), P(ctypes.c_double)],
+        "lscd_tune_dense": [VP, VP, VP, I32, P(ctypes.c_double), P(I32)],
         "lscd_destroy": [VP],
     }
     for name, args in sig.items():
@@ -307,6 +308,19 @@ def lscd_linear(h: Handle, B, C, stream=None):
     pc = _device_fp16(C, "C", (N, info["M"]))
     _check(_lib.lscd_linear(ctypes.c_void_p(h.ptr), pb, pc, N, _stream(stream)), "lscd_linear")
     return C
+
+
+def lscd_tune_dense(h: Handle, B, C):
+    """Time hipBLASLt's heuristic candidates for the dense GEMM at width N = B.shape[0] and keep
+    the fastest for lscd_linear; returns (best microseconds per GEMM, candidates timed)."""
+    info = lscd_get_info(h)
+    N = int(B.shape[0]) if isinstance(B, torch.Tensor) and B.dim() == 2 else -1
+    pb = _device_fp16(B, "B", (N, info["K"]))
+    pc = _device_fp16(C, "C", (N, info["M"]))
+    us, n = ctypes.c_double(), ctypes.c_int32()
+    _check(_lib.lscd_tune_dense(ctypes.c_void_p(h.ptr), pb, pc, N, ctypes.byref(us), ctypes.byref(n)),
+           "lscd_tune_dense")
+    return us.value, n.value
 
 
 def lscd_linear_path(h: Handle, N: int) -> int:

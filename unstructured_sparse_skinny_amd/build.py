@@ -69,7 +69,7 @@ def build(verbose: bool = False, pkg_dir: str = HERE, defines=()) -> str:
     rocm_lib = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "lib")
     # rocBLAS (dense path of lscd_linear): when torch is loaded first, its copy (same soname)
     # is the one bound.
-    cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-pthread", *objs, "-L", rocm_lib, "-lrocblas",
+    cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-pthread", *objs, "-L", rocm_lib, "-lrocblas", "-lhipblaslt",
            "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:

@@ -175,5 +175,6 @@ struct lscd_handle_s {
     // dense path of lscd_linear (lscd_attach_dense)
     uint16_t* d_dense = nullptr;  // M x K fp16, row-major
     void* blas = nullptr;         // rocblas_handle
+    void* lt = nullptr;           // hipBLASLt state: handle, workspace, tuned algorithms per N
     int32_t crossover = -1;       // sparse iff N <= crossover; -1: cost model
 };

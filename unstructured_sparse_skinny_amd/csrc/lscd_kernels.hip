@@ -963,13 +963,13 @@ constexpr int kTLSlotStride = 80;  // bytes per lane of the slot copy: 16-byte s
 // slots.  p runs over the lane's region (4 rows x 16 columns): p = 16*i + column % 16.
 // Slots and positions are worked out first, so that the LDS reads of all eight points are in
 // flight together.
-__device__ __forceinline__ void three_level_fill(u32x4 (&va)[4], uint32_t fill, uint32_t codes, unsigned char* As,
-                                                 unsigned char* Ps, int lane) {
+__device__ __forceinline__ uint32_t three_level_fill(u32x4 (&va)[4], uint32_t fill, uint32_t codes, unsigned char* As,
+                                                     unsigned char* Ps, uint32_t (&dst)[kThreeLevelMaxCodes], int lane) {
     u32x4* pv = reinterpret_cast<u32x4*>(Ps + lane * kTLSlotStride);
     uint16_t* ph = reinterpret_cast<uint16_t*>(Ps + lane * kTLSlotStride);
 #pragma unroll
     for (int i = 0; i < 4; ++i) pv[i] = va[i];
-    uint32_t slot[kThreeLevelMaxCodes], dst[kThreeLevelMaxCodes];
+    uint32_t slot[kThreeLevelMaxCodes];
     uint32_t p = 0xFFFFFFFFu;
     const uint32_t n = (uint32_t)__popc(fill);
 #pragma unroll
@@ -993,6 +993,21 @@ __device__ __forceinline__ void three_level_fill(u32x4 (&va)[4], uint32_t fill, 
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) va[i] = pv[i];
+    return n;
+}
+
+// Reset of the dense tile after a step: zeros at the slot-filled points (n of them, offsets
+// dst) and at the residual words held in registers (the lane's unit of the first 64); a tile
+// with more residual units was cleared whole instead.
+__device__ __forceinline__ void three_level_reset(unsigned char* As, const uint32_t (&dst)[kThreeLevelMaxCodes],
+                                                  uint32_t n, const u32x4& vr, bool has_res) {
+#pragma unroll
+    for (int k = 0; k < kThreeLevelMaxCodes; ++k)
+        if ((uint32_t)k < n) *reinterpret_cast<uint16_t*>(As + dst[k]) = 0;
+    if (has_res) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) put_word(As, vr[e] & 0xFFFF0000u);
+    }
 }
 
 // acc[i][j] += 4:2 slots of operand i (x B columns 16j..16j+15) and, when `dense`, the dense
@@ -1107,7 +1122,8 @@ __global__ __launch_bounds__(WK * 64) void spmm_three_level_kernel(SpmmArgs a) {
                 const uint32_t fill = vm[q][2];
                 const bool any_fill = __any(fill != 0u);
                 const bool dense = any_fill || nr > 0;
-                if (any_fill) three_level_fill(va[q], fill, vm[q][3], As, Ps, lane);
+                uint32_t dst[kThreeLevelMaxCodes];
+                if (any_fill) (void)three_level_fill(va[q], fill, vm[q][3], As, Ps, dst, lane);
                 if (nr > 0) {
                     if (lane < nr) {
                         put_word(As, vr[q][0]);
@@ -1125,6 +1141,8 @@ __global__ __launch_bounds__(WK * 64) void spmm_three_level_kernel(SpmmArgs a) {
                     }
                 }
                 three_level_mma<NPAD>(acc, va[q], vm[q][0], vm[q][1], As, Bw, dense, lane);
+                // cleared whole: measured faster here than rewriting the placed positions
+                // (which the shared-B kernel for N = 64 does)
                 if (dense) zero_tile(As, lane);
             }
             fetch(q, k + P);
@@ -1258,11 +1276,14 @@ __global__ __launch_bounds__(kThreads) void spmm_three_level_shared_kernel(SpmmA
             bool dense = false;
             u32x4 cur[4] = {va[q][0], va[q][1], va[q][2], va[q][3]};
             const uint32_t idx01 = vm[q][0], idx23 = vm[q][1];
+            const u32x4 res = vr[q];
+            uint32_t dst[kThreeLevelMaxCodes];
+            uint32_t npts = 0;
             if (nr >= 0) {
                 const uint32_t fill = vm[q][2];
                 const bool any_fill = __any(fill != 0u);
                 dense = any_fill || nr > 0;
-                if (any_fill) three_level_fill(cur, fill, vm[q][3], As, Ps, lane);
+                if (any_fill) npts = three_level_fill(cur, fill, vm[q][3], As, Ps, dst, lane);
                 if (nr > 0) {
                     if (lane < nr) {
                         put_word(As, vr[q][0]);
@@ -1283,7 +1304,10 @@ __global__ __launch_bounds__(kThreads) void spmm_three_level_shared_kernel(SpmmA
             fetch(q, k + P);
             __syncthreads();
             if (nr >= 0) three_level_mma<NPAD>(acc, cur, idx01, idx23, As, Bs, dense, lane);
-            if (dense) zero_tile(As, lane);
+            if (nr > 64)
+                zero_tile(As, lane);
+            else if (dense)
+                three_level_reset(As, dst, npts, res, lane < nr);
         }
     }
     // MFMA 16x16 result layout: lane holds column (lane & 15), rows 4*(lane >> 4) + 0..3.
@@ -1350,7 +1374,8 @@ __global__ __launch_bounds__(kThreads) void decode_three_level_kernel(DecodeArgs
 #pragma unroll
         for (int i = 0; i < 4; ++i) va[i] = *reinterpret_cast<const u32x4*>(tw + 4 * (i * 64 + lane));
         const u32x4 vm = *reinterpret_cast<const u32x4*>(tw + kThreeLevelValueWords + 4 * lane);
-        three_level_fill(va, vm[2], vm[3], As, Ps, lane);
+        uint32_t dst[kThreeLevelMaxCodes];
+        (void)three_level_fill(va, vm[2], vm[3], As, Ps, dst, lane);
         for (int u = lane; u < nr; u += 64) {
             const u32x4 x = *reinterpret_cast<const u32x4*>(tw + 4 * ((size_t)kTLFixedUnits + u));
             put_word(As, x[0]);

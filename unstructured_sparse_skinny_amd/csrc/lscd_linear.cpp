@@ -5,14 +5,19 @@
 // "N dimension") describes a GEMM wrapper that picks the dense or the sparse MatMul per
 // call, because the sparse kernel only wins while the product is memory-bound (small N);
 // once N is large the work is compute-bound and the dense library GEMM is faster.  Here
-// the dense copy is decoded from the encoding itself, and the dense product is a rocBLAS
-// fp16 GEMM with fp32 accumulation.
+// the dense copy is decoded from the encoding itself, and the dense product is an fp16 GEMM
+// with fp32 accumulation: hipBLASLt with the fastest of its heuristic's candidates once
+// lscd_tune_dense has timed them for that N, rocBLAS otherwise.
 
 #include <math.h>
 
 #include <algorithm>
 
+#include <hipblaslt/hipblaslt.h>
 #include <rocblas/rocblas.h>
+
+#include <utility>
+#include <vector>
 
 #include "lscd_internal.h"
 
@@ -52,6 +57,47 @@ void model(int64_t M, int64_t K, int64_t nnz_padded, int64_t T, int32_t N, doubl
     *td = kDenseCallUs + (2 * m * k + 2 * k * n + 2 * m * n) / kDenseBytesPerUs + 2 * m * k * n / kDenseFlopsPerUs;
 }
 
+// hipBLASLt state of a handle with a dense copy.
+struct LtState {
+    hipblasLtHandle_t handle = nullptr;
+    void* ws = nullptr;
+    size_t ws_bytes = 0;
+    std::vector<std::pair<int32_t, hipblasLtMatmulAlgo_t>> tuned;  // per N
+};
+constexpr size_t kLtWorkspace = (size_t)64 << 20;
+constexpr int kLtCandidates = 16;
+
+// Descriptors of C (N x M row-major = M x N column-major) = A (M x K row-major, i.e. K x M
+// column-major, transposed) times B (N x K row-major = K x N column-major).
+struct LtProblem {
+    hipblasLtMatmulDesc_t desc = nullptr;
+    hipblasLtMatrixLayout_t a = nullptr, b = nullptr, c = nullptr;
+    bool make(int64_t M, int64_t K, int32_t N) {
+        const hipblasOperation_t ta = HIPBLAS_OP_T, tb = HIPBLAS_OP_N;
+        return hipblasLtMatmulDescCreate(&desc, HIPBLAS_COMPUTE_32F, HIP_R_32F) == HIPBLAS_STATUS_SUCCESS &&
+               hipblasLtMatmulDescSetAttribute(desc, HIPBLASLT_MATMUL_DESC_TRANSA, &ta, sizeof ta) ==
+                   HIPBLAS_STATUS_SUCCESS &&
+               hipblasLtMatmulDescSetAttribute(desc, HIPBLASLT_MATMUL_DESC_TRANSB, &tb, sizeof tb) ==
+                   HIPBLAS_STATUS_SUCCESS &&
+               hipblasLtMatrixLayoutCreate(&a, HIP_R_16F, (uint64_t)K, (uint64_t)M, K) == HIPBLAS_STATUS_SUCCESS &&
+               hipblasLtMatrixLayoutCreate(&b, HIP_R_16F, (uint64_t)K, (uint64_t)N, K) == HIPBLAS_STATUS_SUCCESS &&
+               hipblasLtMatrixLayoutCreate(&c, HIP_R_16F, (uint64_t)M, (uint64_t)N, M) == HIPBLAS_STATUS_SUCCESS;
+    }
+    ~LtProblem() {
+        if (c) (void)hipblasLtMatrixLayoutDestroy(c);
+        if (b) (void)hipblasLtMatrixLayoutDestroy(b);
+        if (a) (void)hipblasLtMatrixLayoutDestroy(a);
+        if (desc) (void)hipblasLtMatmulDescDestroy(desc);
+    }
+};
+
+hipblasStatus_t lt_run(const lscd_handle_s* h, LtState* lt, LtProblem& pb, const hipblasLtMatmulAlgo_t* algo,
+                       const void* B, void* C, hipStream_t s) {
+    const float alpha = 1.0f, beta = 0.0f;
+    return hipblasLtMatmul(lt->handle, pb.desc, &alpha, h->d_dense, pb.a, B, pb.b, &beta, C, pb.c, C, pb.c, algo,
+                           lt->ws, lt->ws_bytes, s);
+}
+
 lscd_status_t hip_st(hipError_t e) {
     if (e == hipSuccess) return LSCD_SUCCESS;
     return e == hipErrorOutOfMemory ? LSCD_ERROR_OUT_OF_MEMORY : LSCD_ERROR_HIP;
@@ -76,6 +122,13 @@ bool use_dense(const lscd_handle_s* h, int32_t N) {
 namespace lscd {
 
 void release_dense(lscd_handle_s* h) {
+    if (h->lt) {
+        LtState* lt = (LtState*)h->lt;
+        if (lt->handle) (void)hipblasLtDestroy(lt->handle);
+        if (lt->ws) (void)hipFree(lt->ws);
+        delete lt;
+        h->lt = nullptr;
+    }
     if (h->blas) (void)rocblas_destroy_handle((rocblas_handle)h->blas);
     if (h->d_dense) (void)hipFree(h->d_dense);
     h->blas = nullptr;
@@ -138,6 +191,15 @@ lscd_status_t lscd_linear(lscd_handle_t h, const void* B, void* C, int32_t N, vo
     if (N > LSCD_MAX_N) return LSCD_ERROR_NOT_SUPPORTED;
     lscd_status_t st = on_device(h);
     if (st != LSCD_SUCCESS) return st;
+    if (LtState* lt = (LtState*)h->lt) {
+        for (auto& t : lt->tuned) {
+            if (t.first != N) continue;
+            LtProblem pb;
+            if (!pb.make(h->g.M, h->g.K, N)) return LSCD_ERROR_HIP;
+            return lt_run(h, lt, pb, &t.second, B, C, (hipStream_t)stream) == HIPBLAS_STATUS_SUCCESS ? LSCD_SUCCESS
+                                                                                                   : LSCD_ERROR_HIP;
+        }
+    }
     rocblas_handle rh = (rocblas_handle)h->blas;
     if (rocblas_set_stream(rh, (hipStream_t)stream) != rocblas_status_success) return LSCD_ERROR_HIP;
     // Column-major view: C (N x M row-major) is the M x N matrix A * B^T with ldc = M; A (M x
@@ -149,6 +211,80 @@ lscd_status_t lscd_linear(lscd_handle_t h, const void* B, void* C, int32_t N, vo
                                         rocblas_datatype_f16_r, m, C, rocblas_datatype_f16_r, m,
                                         rocblas_datatype_f32_r, rocblas_gemm_algo_standard, 0, 0);
     return rs == rocblas_status_success ? LSCD_SUCCESS : LSCD_ERROR_HIP;
+}
+
+lscd_status_t lscd_tune_dense(lscd_handle_t h, const void* B, void* C, int32_t N, double* best_us,
+                              int32_t* candidates) {
+    if (!h || !B || !C || !best_us || !candidates || N < 1 || N > LSCD_MAX_N) return LSCD_ERROR_INVALID_VALUE;
+    if (((uintptr_t)B & 15u) || ((uintptr_t)C & 15u)) return LSCD_ERROR_INVALID_VALUE;
+    if (!h->d_dense) return LSCD_ERROR_NOT_SUPPORTED;
+    lscd_status_t st = on_device(h);
+    if (st != LSCD_SUCCESS) return st;
+    LtState* lt = (LtState*)h->lt;
+    if (!lt) {
+        lt = new (std::nothrow) LtState();
+        if (!lt) return LSCD_ERROR_OUT_OF_MEMORY;
+        h->lt = lt;
+        if (hipblasLtCreate(&lt->handle) != HIPBLAS_STATUS_SUCCESS) return LSCD_ERROR_HIP;
+        hipError_t e = hipMalloc(&lt->ws, kLtWorkspace);
+        if (e != hipSuccess) {
+            lt->ws = nullptr;
+            return hip_st(e);
+        }
+        lt->ws_bytes = kLtWorkspace;
+    }
+    LtProblem pb;
+    hipblasLtMatmulPreference_t pref = nullptr;
+    if (!pb.make(h->g.M, h->g.K, N) || hipblasLtMatmulPreferenceCreate(&pref) != HIPBLAS_STATUS_SUCCESS)
+        return LSCD_ERROR_HIP;
+    const uint64_t wsb = lt->ws_bytes;
+    (void)hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES, &wsb, sizeof wsb);
+    hipblasLtMatmulHeuristicResult_t res[kLtCandidates];
+    int got = 0;
+    hipblasStatus_t hs = hipblasLtMatmulAlgoGetHeuristic(lt->handle, pb.desc, pb.a, pb.b, pb.c, pb.c, pref,
+                                                         kLtCandidates, res, &got);
+    (void)hipblasLtMatmulPreferenceDestroy(pref);
+    if (hs != HIPBLAS_STATUS_SUCCESS || got < 1) return LSCD_ERROR_NOT_SUPPORTED;
+    hipEvent_t e0, e1;
+    if (hipEventCreate(&e0) != hipSuccess) return LSCD_ERROR_HIP;
+    if (hipEventCreate(&e1) != hipSuccess) {
+        (void)hipEventDestroy(e0);
+        return LSCD_ERROR_HIP;
+    }
+    // each candidate: 3 untimed runs, then 20 back to back between one event pair (default stream)
+    double best = -1;
+    int best_i = -1, tried = 0;
+    for (int i = 0; i < got; ++i) {
+        if (res[i].state != HIPBLAS_STATUS_SUCCESS || res[i].workspaceSize > lt->ws_bytes) continue;
+        bool ok = true;
+        for (int r = 0; r < 3 && ok; ++r) ok = lt_run(h, lt, pb, &res[i].algo, B, C, nullptr) == HIPBLAS_STATUS_SUCCESS;
+        if (!ok) continue;
+        (void)hipEventRecord(e0, nullptr);
+        for (int r = 0; r < 20 && ok; ++r) ok = lt_run(h, lt, pb, &res[i].algo, B, C, nullptr) == HIPBLAS_STATUS_SUCCESS;
+        (void)hipEventRecord(e1, nullptr);
+        if (hipEventSynchronize(e1) != hipSuccess || !ok) continue;
+        float ms = 0;
+        (void)hipEventElapsedTime(&ms, e0, e1);
+        ++tried;
+        const double us = 1e3 * (double)ms / 20.0;
+        if (best < 0 || us < best) {
+            best = us;
+            best_i = i;
+        }
+    }
+    (void)hipEventDestroy(e0);
+    (void)hipEventDestroy(e1);
+    if (best_i < 0) return LSCD_ERROR_NOT_SUPPORTED;
+    bool found = false;
+    for (auto& t : lt->tuned)
+        if (t.first == N) {
+            t.second = res[best_i].algo;
+            found = true;
+        }
+    if (!found) lt->tuned.emplace_back(N, res[best_i].algo);
+    *best_us = best;
+    *candidates = tried;
+    return LSCD_SUCCESS;
 }
 
 }  // extern "C"
