@@ -170,8 +170,9 @@ def cpu_baseline(case, alg_bytes, flops, budget_s):
 
 
 def sweep_n(args, case, L, torch, np):
-    """N sweep to the dense crossover: sparse (lscd_spmm), dense (torch.mm -> hipBLASLt) and
-    lscd_linear on the attached dense copy, for every N of --sweep-n."""
+    """N sweep to the dense crossover: sparse (lscd_spmm), dense (torch.mm -> hipBLASLt's default
+    choice, and the library's dense path with hipBLASLt tuned for N) and lscd_linear's own
+    choice on the attached dense copy, for every N of --sweep-n."""
     M, K = case.M, case.K
     tm = L.lscd_default_tile_m(M, K)
     words, offs = L.lscd_pack(case.A16, case.mask, tm, 64)
@@ -192,13 +193,19 @@ def sweep_n(args, case, L, torch, np):
         C = torch.empty(N, M, dtype=torch.float16, device="cuda")
         _, ts, *_ = time_calls([(L.lscd_spmm, (h, B, C)) for h in hs], args.steps, args.warmup, torch)
         _, td, *_ = time_calls([(torch.mm, (B, a.t())) for a in Ads], args.steps, args.warmup, torch)
+        # the library's dense path with hipBLASLt tuned for this N, then lscd_linear's own choice
+        tune_us, _ = L.lscd_tune_dense(h0, B, C)
+        L.lscd_set_linear_crossover(h0, 0)
+        _, tt, *_ = time_calls([(L.lscd_linear, (h0, B, C))], args.steps, args.warmup, torch, graph=False)
+        L.lscd_set_linear_crossover(h0, -1)
         _, tl, *_ = time_calls([(L.lscd_linear, (h0, B, C))], args.steps, args.warmup, torch, graph=False)
         ms, md = L.lscd_linear_model(M, K, info["nnz_padded"], info["num_tiles"], N)
-        if ts < td:
+        if ts < min(td, tt):
             last_sparse_win = N
         print(json.dumps({"sweep": "n", "workload": case.name, "M": M, "K": K, "N": N,
                           "sparsity": round(case.sparsity, 4), "sparse_us": round(ts * 1e3, 1),
-                          "dense_hipblaslt_us": round(td * 1e3, 1), "linear_us": round(tl * 1e3, 1),
+                          "dense_hipblaslt_us": round(td * 1e3, 1), "dense_tuned_us": round(tt * 1e3, 1),
+                          "tune_us": round(tune_us, 1), "linear_us": round(tl * 1e3, 1),
                           "linear_path": ["sparse", "dense"][L.lscd_linear_path(h0, N)],
                           "model_sparse_us": round(ms, 1), "model_dense_us": round(md, 1),
                           "sparse_tflops": round(2 * M * N * K / (ts * 1e-3) / 1e12, 1)}), flush=True)

@@ -296,7 +296,9 @@ lscd_status_t lscd_tune_dense(lscd_handle_t h, const void* B, void* C, int32_t N
                               int32_t* candidates);
 
 /* lscd_linear_path -- the path lscd_linear takes for N: *path = 0 sparse, 1 dense (dense
- * only with a dense copy attached).  No device work. */
+ * only with a dense copy attached): dense iff its time is below the sparse product's, taking
+ * the time lscd_tune_dense measured for this N when there is one and lscd_linear_model's
+ * prediction otherwise.  No device work. */
 lscd_status_t lscd_linear_path(lscd_handle_t h, int32_t N, int32_t* path);
 
 /* lscd_set_linear_crossover -- fix the choice: sparse iff N <= n_max_sparse; -1 returns

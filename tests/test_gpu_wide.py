@@ -81,6 +81,8 @@ def test_tuned_dense_path(N):
     us, n = L.lscd_tune_dense(h, B, C)
     say(f"tuned dense N={N}: {us:.1f} us over {n} candidates")
     assert n >= 1 and us > 0
+    ts, _ = L.lscd_linear_model(case.M, case.K, h.info["nnz_padded"], h.info["num_tiles"], N)
+    assert L.lscd_linear_path(h, N) == (1 if us < ts else 0)     # the measured dense time decides
     L.lscd_set_linear_crossover(h, 0)
     want = osp.fp16_rne(osp.spmm_f64(case.A16, case.mask, case.B16))
     assert np.array_equal(run(L.lscd_linear, h, case.B16, case.M), want)

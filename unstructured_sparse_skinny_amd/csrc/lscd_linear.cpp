@@ -62,7 +62,12 @@ struct LtState {
     hipblasLtHandle_t handle = nullptr;
     void* ws = nullptr;
     size_t ws_bytes = 0;
-    std::vector<std::pair<int32_t, hipblasLtMatmulAlgo_t>> tuned;  // per N
+    struct Tuned {
+        int32_t N;
+        hipblasLtMatmulAlgo_t algo;
+        double us;  // measured mean time per GEMM
+    };
+    std::vector<Tuned> tuned;
 };
 constexpr size_t kLtWorkspace = (size_t)64 << 20;
 constexpr int kLtCandidates = 16;
@@ -109,11 +114,16 @@ lscd_status_t on_device(const lscd_handle_s* h) {
     return dev == h->device ? LSCD_SUCCESS : LSCD_ERROR_INVALID_VALUE;
 }
 
+// Dense iff the dense time is lower: the time lscd_tune_dense measured for this N when there
+// is one, the cost model's otherwise; the sparse time is always the model's.
 bool use_dense(const lscd_handle_s* h, int32_t N) {
     if (!h->d_dense) return false;
     if (h->crossover >= 0) return N > h->crossover;
     double ts, td;
     model(h->g.M, h->g.K, h->nnz_padded, h->g.T, N, &ts, &td);
+    if (const LtState* lt = (const LtState*)h->lt)
+        for (const auto& t : lt->tuned)
+            if (t.N == N) td = t.us;
     return td < ts;
 }
 
@@ -193,11 +203,11 @@ lscd_status_t lscd_linear(lscd_handle_t h, const void* B, void* C, int32_t N, vo
     if (st != LSCD_SUCCESS) return st;
     if (LtState* lt = (LtState*)h->lt) {
         for (auto& t : lt->tuned) {
-            if (t.first != N) continue;
+            if (t.N != N) continue;
             LtProblem pb;
             if (!pb.make(h->g.M, h->g.K, N)) return LSCD_ERROR_HIP;
-            return lt_run(h, lt, pb, &t.second, B, C, (hipStream_t)stream) == HIPBLAS_STATUS_SUCCESS ? LSCD_SUCCESS
-                                                                                                   : LSCD_ERROR_HIP;
+            return lt_run(h, lt, pb, &t.algo, B, C, (hipStream_t)stream) == HIPBLAS_STATUS_SUCCESS ? LSCD_SUCCESS
+                                                                                                 : LSCD_ERROR_HIP;
         }
     }
     rocblas_handle rh = (rocblas_handle)h->blas;
@@ -277,11 +287,12 @@ lscd_status_t lscd_tune_dense(lscd_handle_t h, const void* B, void* C, int32_t N
     if (best_i < 0) return LSCD_ERROR_NOT_SUPPORTED;
     bool found = false;
     for (auto& t : lt->tuned)
-        if (t.first == N) {
-            t.second = res[best_i].algo;
+        if (t.N == N) {
+            t.algo = res[best_i].algo;
+            t.us = best;
             found = true;
         }
-    if (!found) lt->tuned.emplace_back(N, res[best_i].algo);
+    if (!found) lt->tuned.push_back({N, res[best_i].algo, best});
     *best_us = best;
     *candidates = tried;
     return LSCD_SUCCESS;
