@@ -138,12 +138,14 @@ lscd_status_t lscd_encode_tiled(const uint16_t* A, const uint8_t* mask, int64_t 
 /*
  * Bitmap-tile variant of the format (the pages' follow-up summary, section "Problematica":
  * per-entry position metadata is as large as the values near 50% sparsity, one bit per
- * position is not).  Same 64 x 64 tiles and tile order as above; a tile with k kept
- * entries stores 64 row masks (uint64, little-endian, bit c of mask r = entry (r, c)
- * kept), then its k fp16 values in row-major order padded with 0x0000 to a multiple of 8
- * values; an empty tile stores nothing.  tile_offsets (num_tiles + 1 entries) count
- * 16-byte units.  Bytes: 512 + 16*ceil(k/8) per non-empty tile, against 16*ceil(k/4) for
- * Tiled-CSL.
+ * position is not).  Same 64 x 64 tiles and tile order as above.  Positions follow the
+ * operand layout of the 16x16x32 fp16 MFMA: lane l (0..63), mask bit b (chunk g = b/8) is
+ * tile row 16*(g/2) + l%16, column 32*(g%2) + 8*(l/16) + b%8.  A tile with k kept entries
+ * stores the 64 lane masks (uint64, little-endian), then its k fp16 values chunk by chunk --
+ * for g = 0..7 the values of bits 8g..8g+7 of lanes 0..63, lane after lane, each lane's in
+ * ascending bit order -- padded with 0x0000 to a multiple of 8 values; an empty tile stores
+ * nothing.  tile_offsets (num_tiles + 1 entries) count 16-byte units.  Bytes:
+ * 512 + 16*ceil(k/8) per non-empty tile, against 16*ceil(k/4) for Tiled-CSL.
  *
  * lscd_pack_bitmap_size / lscd_pack_bitmap -- host only.  The encoding of (A, mask) (same
  *   argument rules as lscd_pack; tiles are always 64 x 64) into caller arrays of nwords

@@ -1,7 +1,6 @@
 """GPU parity of the bitmap-tile path (lscd_encode_bitmap + lscd_spmm / lscd_debug_decode).
 
-Bit-exact: the decoded matrix (including tiles past the register stage), the exported blob
-against the host encoder, integer-valued products for N across the 16 / 32-column launch
+Bit-exact: the decoded matrix, the exported blob against the host encoder, fully dense tiles, integer-valued products for N across the 16 / 32-column launch
 boundaries with forced K splits.  Tolerance gates (tests/_util.py) for Gaussian inputs on
 ragged shapes and, with sampled rows, at full OPT shapes.
 """
@@ -51,12 +50,12 @@ def test_bitmap_decode_and_export_bit_exact(M, K, keep):
     assert np.array_equal(words, ow) and np.array_equal(offs, oo)
 
 
-def test_bitmap_tiles_past_the_register_stage():
-    case = syn.random_case(200, 300, 16, 1.0, seed=2, values="int3")
-    with env(LSCD_MAX_R="1"):
-        h = L.lscd_encode_bitmap(case.A16, case.mask)
-    say(f"bitmap dense R={h.info['reg_vectors']}")
-    assert h.info["reg_vectors"] == 1
+@pytest.mark.parametrize("N", [16, 32])
+def test_bitmap_full_tiles_bit_exact(N):
+    # every position kept: all 16 groups of every lane hold 4 values
+    case = syn.random_case(200, 300, N, 1.0, seed=2, values="int3")
+    h = L.lscd_encode_bitmap(case.A16, case.mask)
+    say(f"bitmap dense N={N}")
     C64 = osp.spmm_f64(case.A16, case.mask, case.B16)
     assert np.array_equal(run(h, case.B16, case.M), osp.fp16_rne(C64))
 

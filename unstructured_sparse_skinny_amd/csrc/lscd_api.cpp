@@ -152,12 +152,11 @@ lscd_status_t new_handle(const Grid& g, int64_t nnz, int64_t nwords, int32_t max
     int64_t part = 0;
     if (format == 1) {
         // bitmap tiles: one kernel, launches of <= 32 columns
-        h->R = pick_reg_vectors_bitmap(maxw);
         for (int i = 0; i < 3 && kernel_tile; ++i) {
             const int npad = i == 0 ? 16 : 32;
             h->kind[i] = kKernelBitmap;
-            const int occ = spmm_blocks_per_cu(kKernelBitmap, npad, h->R, (int)std::min<int64_t>(g.K, 1 << 30));
-            h->S[i] = plan_splits(g, h->cus, occ, g.MB, 8, false);  // decode-bound: fill every slot
+            const int occ = spmm_blocks_per_cu(kKernelBitmap, npad, 0, (int)std::min<int64_t>(g.K, 1 << 30));
+            h->S[i] = plan_splits(g, h->cus, occ, g.MB, 4 * kBitmapWaves, false);  // fill the resident slots
             if (h->S[i] > 1) part = std::max<int64_t>(part, (int64_t)h->S[i] * g.M * npad * 4);
         }
     }
@@ -221,7 +220,7 @@ lscd_status_t make_handle(const uint32_t* words, int64_t nwords, const uint32_t*
     lscd_status_t st = lscd::new_handle(g, nnz, nwords, maxw, &h, format);
     if (st != LSCD_SUCCESS) return st;
     hipError_t e;
-    const size_t wbytes = (size_t)std::max<int64_t>(nwords, 4) * 4;
+    const size_t wbytes = (size_t)std::max<int64_t>(nwords, 4) * 4 + (format == 1 ? lscd::kBitmapSlackBytes : 0);
     if ((e = hipMalloc((void**)&h->d_words, wbytes)) != hipSuccess ||
         (e = hipMalloc((void**)&h->d_offs, (size_t)(g.T + 1) * 4)) != hipSuccess) {
         free_handle(h);

@@ -119,16 +119,19 @@ constexpr int kKernelIndep8 = 2;  // 8 wavefronts per row block
 // of B per wavefront (N padded to 128, 192 or 256 per launch).
 constexpr int kKernelWide = 3;
 constexpr int kWideMaxN = 256;
-// Bitmap-tile format: one row block per workgroup, four wavefronts over its k range, N
-// padded to 16 or 32 per launch (wider N runs launches of 32 columns).
+// Bitmap-tile format: one row block per workgroup, kBitmapWaves wavefronts over its k range,
+// N padded to 16 or 32 per launch (wider N runs launches of 32 columns).  The allocation of a
+// bitmap blob carries kBitmapSlackBytes past its end: a tile's value loads may read up to that
+// far past its last value.
 constexpr int kKernelBitmap = 4;
 constexpr int kBitmapMaxN = 32;
+constexpr int kBitmapWaves = 4;
+constexpr int kBitmapSlackBytes = 16;
 // Three-level tiles (4:2 layer on the structured-sparse MFMA, slot filling, residual): one
 // kernel, launches of <= 64 columns.
 constexpr int kKernelThreeLevel = 5;
 constexpr int kThreeLevelMaxN = 64;
 hipError_t launch_decode_three_level(const DecodeArgs& a, int grid, hipStream_t s);
-int pick_reg_vectors_bitmap(int32_t max_tile_words);
 hipError_t launch_decode_bitmap(const DecodeArgs& a, int grid, hipStream_t s);
 // Staging registers per thread and tile of the wide variant (1, 2 or 4).
 int pick_reg_vectors_wide(int32_t max_tile_words);

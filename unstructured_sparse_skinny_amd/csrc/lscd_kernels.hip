@@ -763,69 +763,164 @@ __global__ __launch_bounds__(kThreads) void spmm_wide_kernel(SpmmArgs a) {
 
 // ---------------------------------------------------------------- bitmap tiles
 // Variant format with one bit per position (the pages' follow-up summary, section
-// "Problematica"): a non-empty tile holds 64 row masks (64-bit, little-endian) and then
-// its kept values in row-major order, padded to 16-byte vectors; offsets count 16-byte
-// units.  Decoding moves work on chip: each wavefront stages the tile's values in its own
-// LDS area, lane r takes row r, finds where its row's values start (exclusive prefix of
-// the rows' popcounts across the wavefront) and writes each value at the column of the
-// next set bit of its mask.  The dense tile then feeds the same MFMA step as Tiled-CSL.
-constexpr int kMaskUnits = kTileM * 8 / 16;  // 16-byte units of a tile's masks (32)
+// "Problematica").  Positions are numbered in the operand order of the 16x16x32 MFMA: lane
+// l's mask bit b (chunk g = b/8, element b%8) is tile row 16*(g/2) + l%16, column
+// 32*(g%2) + 8*(l/16) + b%8, so lane l's 64 bits are exactly the 8 A-operand vectors it feeds
+// to the matrix unit (chunk g = row group g/2, k step g%2).  A non-empty tile holds the 64
+// lane masks (512 bytes), then its values chunk by chunk (chunk g of lanes 0..63 in lane
+// order), padded to 16-byte vectors; offsets count 16-byte units.
+//
+// Decoding needs no LDS tile: a lane finds where each of its 4-bit groups starts in the value
+// stream (a prefix over the wavefront of its chunk counts, plus the chunk totals before it),
+// fetches the group's up to 4 values with one dword-aligned 12-byte load, shifts them down by
+// 16 bits when the group starts at an odd value, and spreads them to the group's positions
+// with two byte permutes (v_perm_b32) whose selectors come from a 16-entry table.  (Loads at
+// 2-byte alignment were measured at about 1000 CU cycles per tile whatever the density.)  In
+// chunk-major order the lanes of one load read neighbouring runs, a few cache lines per
+// instruction.
+constexpr int kMaskUnits = kTileM * 8 / 16;     // 16-byte units of a tile's masks (32)
+constexpr int kMaskBytes = kMaskUnits * 16;     // 512
+constexpr int kBitmapTableBytes = 16 * 8;       // selector table: 16 groups x 2 dwords
+constexpr int kBitmapSlack = kBitmapSlackBytes;  // readable bytes past a tile's values
 
-// Place row `lane`'s values (staged at Vs from value index `first`) into the zero-filled
-// dense tile As, one 32-bit half of the mask at a time; values are read eight at a time so
-// that eight LDS reads are in flight per round trip.
-__device__ __forceinline__ void bitmap_place_half(unsigned char* As, const uint16_t* Vs, uint32_t m, uint32_t col0,
-                                                  uint32_t first, int lane) {
-    const int cnt = __popc(m);
-    const uint32_t rowb = (uint32_t)lane * kRowBytes, swz = ((uint32_t)lane & 7u) << 4;
-    for (int g = 0; g < cnt; g += 8) {
-        uint16_t v[8];
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
+
+// Entry q: selectors of output dwords 0 (elements 0, 1) and 1 (elements 2, 3) of a 4-bit
+// group with mask q.  The group's values are packed at the front of an 8-byte load (value r
+// in bytes 2r, 2r+1); element e takes value popc(q & ((1 << e) - 1)) when bit e is set, the
+// constant zero byte (selector 12) otherwise.
+__device__ __forceinline__ void bitmap_table(unsigned char* tbl, int lane) {
+    if (lane < 16) {
+        uint32_t sel[2] = {0u, 0u};
+        uint32_t r = 0;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = (g + e < cnt) ? Vs[first + g + e] : (uint16_t)0;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            if (g + e < cnt) {
-                const uint32_t c = col0 + (uint32_t)__builtin_ctz(m);
-                m &= m - 1u;
-                *reinterpret_cast<uint16_t*>(As + rowb + ((c * 2u) ^ swz)) = v[e];
+        for (int e = 0; e < 4; ++e) {
+            uint32_t s = 0x0C0Cu;
+            if ((lane >> e) & 1) {
+                s = (2u * r) | ((2u * r + 1u) << 8);
+                ++r;
             }
+            sel[e >> 1] |= s << (16 * (e & 1));
         }
+        *reinterpret_cast<u32x2*>(tbl + lane * 8) = u32x2{sel[0], sel[1]};
     }
 }
 
-__device__ __forceinline__ void bitmap_place(unsigned char* As, const uint16_t* Vs, uint32_t mlo, uint32_t mhi,
-                                             int lane) {
-    const uint32_t cnt = (uint32_t)__popc(mlo) + (uint32_t)__popc(mhi);
-    uint32_t x = cnt;  // inclusive prefix over the wavefront's rows
+// Inclusive prefix sum over the wavefront (row shifts within rows of 16 lanes, then the row
+// broadcasts of lanes 15 and 31).
+__device__ __forceinline__ uint32_t wave_scan(uint32_t x) {
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, false);  // row_shr:1
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, false);  // row_shr:2
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, false);  // row_shr:4
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, false);  // row_shr:8
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xa, 0xf, false);  // row_bcast:15 -> rows 1, 3
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xc, 0xf, false);  // row_bcast:31 -> rows 2, 3
+    return x;
+}
+
+// Byte offsets (from the tile's first value) of the 16 groups of lane masks (lo, hi): group
+// 2g + h is bits 8g + 4h .. +3.  Chunk counts are packed 10 bits a field, three fields a word,
+// so three wavefront scans give every chunk's lane prefix; the chunk totals (lane 63's
+// inclusive sums) are wave-uniform.
+__device__ __forceinline__ void bitmap_group_offsets(uint32_t lo, uint32_t hi, uint32_t (&voff)[16]) {
+    uint32_t c[8];
 #pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const uint32_t y = (uint32_t)__shfl_up((int)x, d, 64);
-        if (lane >= d) x += y;
+    for (int g = 0; g < 4; ++g) {
+        c[g] = (uint32_t)__popc((lo >> (8 * g)) & 0xFFu);
+        c[g + 4] = (uint32_t)__popc((hi >> (8 * g)) & 0xFFu);
     }
-    const uint32_t first = x - cnt;
-    bitmap_place_half(As, Vs, mlo, 0u, first, lane);
-    bitmap_place_half(As, Vs, mhi, 32u, first + (uint32_t)__popc(mlo), lane);
+    const uint32_t p0 = c[0] | (c[1] << 10) | (c[2] << 20);
+    const uint32_t p1 = c[3] | (c[4] << 10) | (c[5] << 20);
+    const uint32_t p2 = c[6] | (c[7] << 10);
+    const uint32_t i0 = wave_scan(p0), i1 = wave_scan(p1), i2 = wave_scan(p2);
+    const uint32_t t0 = (uint32_t)__builtin_amdgcn_readlane((int)i0, 63);
+    const uint32_t t1 = (uint32_t)__builtin_amdgcn_readlane((int)i1, 63);
+    const uint32_t t2 = (uint32_t)__builtin_amdgcn_readlane((int)i2, 63);
+    const uint32_t e[3] = {i0 - p0, i1 - p1, i2 - p2};
+    const uint32_t t[3] = {t0, t1, t2};
+    uint32_t base = 0;
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+        const int w = g / 3, f = 10 * (g % 3);
+        const uint32_t first = base + ((e[w] >> f) & 0x3FFu);
+        const uint32_t m = g < 4 ? lo : hi;
+        voff[2 * g] = 2u * first;
+        voff[2 * g + 1] = 2u * (first + (uint32_t)__popc((m >> (8 * (g & 3))) & 0xFu));
+        base += (t[w] >> f) & 0x3FFu;
+    }
 }
 
-// Bitmap-tile product for N <= 32 per launch, organised like the independent-wavefront
-// kernel: a workgroup owns one row block and its four wavefronts split the k range; each
-// wavefront has its own dense tile, value staging area and B tile, and needs no barrier.
-template <int NPAD, int R, bool VEC>
-__global__ __launch_bounds__(256) void spmm_bitmap_kernel(SpmmArgs a) {
-    constexpr int WK = 4, P = 2;
+// The 16 value loads of a tile, each the dword-aligned 12 bytes around its group's run.  The
+// descriptor covers the values plus the slack, so a load that holds at least one of the
+// group's values lies wholly inside it (it ends at most 10 bytes past the group's last value).
+__device__ __forceinline__ void bitmap_load_values(u32x3 (&x)[16], const uint32_t* words, uint32_t first_unit,
+                                                   uint32_t units, const uint32_t (&voff)[16]) {
+    const __amdgpu_buffer_rsrc_t vs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(words + 4 * (size_t)first_unit + 4 * kMaskUnits), (short)0,
+        units > (uint32_t)kMaskUnits ? (int)((units - kMaskUnits) * 16 + kBitmapSlack) : 0, kBufWord3);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) x[i] = __builtin_amdgcn_raw_buffer_load_b96(vs, voff[i] & ~3u, 0, 0);
+}
+
+// Lane masks of a tile (zero for an empty tile: the descriptor then covers nothing).
+__device__ __forceinline__ u32x2 bitmap_load_masks(const uint32_t* words, uint32_t first_unit, uint32_t units,
+                                                   int lane) {
+    const __amdgpu_buffer_rsrc_t ms = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(words + 4 * (size_t)first_unit), (short)0, units > 0 ? kMaskBytes : 0, kBufWord3);
+    return __builtin_amdgcn_raw_buffer_load_b64(ms, lane * 8, 0, kStreamPolicy);
+}
+
+// Bit i set: group i's run starts in the high half of its load's first dword.
+__device__ __forceinline__ uint32_t bitmap_odd_starts(const uint32_t (&voff)[16]) {
+    uint32_t b = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) b |= ((voff[i] >> 1) & 1u) << i;
+    return b;
+}
+
+// A operand of lane `lane` for chunk g: 4 dwords, elements 8g .. 8g+7 of its mask.
+__device__ __forceinline__ u32x4 bitmap_chunk(const u32x3 (&x)[16], uint32_t odd, uint32_t lo, uint32_t hi,
+                                              const unsigned char* tbl, int g) {
+    const uint32_t m = g < 4 ? lo : hi;
+    u32x4 r;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const uint32_t q = (m >> (8 * (g & 3) + 4 * h)) & 0xFu;
+        const u32x2 s = *reinterpret_cast<const u32x2*>(tbl + q * 8);
+        const u32x3 v = x[2 * g + h];
+        const uint32_t sh = ((odd >> (2 * g + h)) & 1u) << 4;  // 16 or 0
+        const uint32_t v0 = __builtin_amdgcn_alignbit(v[1], v[0], sh);
+        const uint32_t v1 = __builtin_amdgcn_alignbit(v[2], v[1], sh);
+        r[2 * h] = __builtin_amdgcn_perm(v1, v0, s[0]);
+        r[2 * h + 1] = __builtin_amdgcn_perm(v1, v0, s[1]);
+    }
+    return r;
+}
+
+// Bitmap-tile product for N <= 32 per launch: a workgroup owns one row block and its WK
+// wavefronts split the k range; each wavefront keeps its own B tile in LDS and needs no
+// barrier until the final sum over wavefronts.  Pipeline: masks two tiles ahead, values one
+// tile ahead (their offsets need the masks), B two tiles ahead.
+template <int NPAD, int WK, bool VEC>
+__global__ __launch_bounds__(WK * 64) void spmm_bitmap_kernel(SpmmArgs a) {
     constexpr int kBBytes = NPAD * kRowBytes;
-    static_assert(NPAD * kTileM * 4 <= kTileBytes, "the reduction reuses each wavefront's tile");
-    __shared__ __attribute__((aligned(16))) unsigned char smem[WK * (2 * kTileBytes + kBBytes)];
+    constexpr int kRedBytes = NPAD * kTileM * 4;
+    constexpr int kWaveBytes = kBBytes > kRedBytes ? kBBytes : kRedBytes;
+    __shared__ __attribute__((aligned(16))) unsigned char smem[kBitmapTableBytes + WK * kWaveBytes];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    unsigned char* As = smem + wave * kTileBytes;
-    uint16_t* Vs = reinterpret_cast<uint16_t*>(smem + WK * kTileBytes + wave * kTileBytes);
-    unsigned char* Bw = smem + 2 * WK * kTileBytes + wave * kBBytes;
 
     const int bid = blockIdx.x;
     const int item = (bid & 7) * a.per_xcd + (bid >> 3);
     if (item >= a.items) return;
+    unsigned char* tbl = smem;
+    unsigned char* area = smem + kBitmapTableBytes;
+    unsigned char* Bw = area + wave * kWaveBytes;
+    if (wave == 0) bitmap_table(tbl, lane);
+    __syncthreads();
+
     const int s = item / a.G;
     const int rb = item - s * a.G;
     const int ks0 = (int)(((int64_t)s * a.KT) / a.S);
@@ -836,37 +931,36 @@ __global__ __launch_bounds__(256) void spmm_bitmap_kernel(SpmmArgs a) {
     const __amdgpu_buffer_rsrc_t bsrc =
         __builtin_amdgcn_make_buffer_rsrc((void*)a.B, (short)0, a.N * a.K * 2, kBufWord3);
 
-    u32x4 vb[P][R];
-    uint32_t mlo[P], mhi[P];
-    int nv[P];
-    uint32_t first[P];
-    BWave<NPAD, VEC> bf[P];
-    // tile k into stage q: masks (lane = row) and the first R * 64 value vectors
-    auto fetch = [&](int q, int k) {
+    u32x2 mk[2];          // lane masks of the tile in each stage
+    uint32_t fu[2];       // its first 16-byte unit
+    uint32_t nu[2];       // its 16-byte units (0: empty)
+    u32x3 xv[2][16];      // its value loads
+    uint32_t od[2];       // and which of them start at an odd value
+    BWave<NPAD, VEC> bf[2];
+    auto fetch_masks = [&](int q, int k) {
         uint32_t o0 = 0, o1 = 0;
         if (k < kt1) {
             o0 = toff[k];
             o1 = toff[k + 1];
         }
-        const int units = (int)(o1 - o0);
-        first[q] = o0;
-        nv[q] = units > 0 ? units - kMaskUnits : 0;
-        const uint32_t* tw = a.words + 4 * (size_t)o0;
-        __amdgpu_buffer_rsrc_t ms =
-            __builtin_amdgcn_make_buffer_rsrc((void*)tw, (short)0, units > 0 ? kTileM * 8 : 0, kBufWord3);
-        const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b32(ms, lane * 8, 0, kStreamPolicy);
-        const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b32(ms, lane * 8 + 4, 0, kStreamPolicy);
-        mlo[q] = lo;
-        mhi[q] = hi;
-        __amdgpu_buffer_rsrc_t vs = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)(tw + (units > 0 ? 4 * kMaskUnits : 0)), (short)0, nv[q] * 16, kBufWord3);
-#pragma unroll
-        for (int j = 0; j < R; ++j)
-            vb[q][j] = __builtin_amdgcn_raw_buffer_load_b128(vs, (j * 64 + lane) * 16, 0, kStreamPolicy);
-        bf[q].load(bsrc, a.B, a.N, a.K, k, lane, k < kt1);
+        fu[q] = o0;
+        nu[q] = o1 - o0;
+        mk[q] = bitmap_load_masks(a.words, o0, o1 - o0, lane);
     };
-#pragma unroll
-    for (int q = 0; q < P; ++q) fetch(q, kt0 + q);
+    auto fetch_values = [&](int q) {
+        uint32_t voff[16];
+        bitmap_group_offsets(mk[q][0], mk[q][1], voff);
+        bitmap_load_values(xv[q], a.words, fu[q], nu[q], voff);
+        od[q] = bitmap_odd_starts(voff);
+    };
+    fetch_masks(0, kt0);
+    bf[0].load(bsrc, a.B, a.N, a.K, kt0, lane, kt0 < kt1);
+    fetch_masks(1, kt0 + 1);
+    bf[1].load(bsrc, a.B, a.N, a.K, kt0 + 1, lane, kt0 + 1 < kt1);
+    // issue order as in the loop (the next masks before the current values), so that the wait
+    // for the next masks at the top of the loop leaves the current values in flight
+    __builtin_amdgcn_sched_barrier(0);
+    fetch_values(0);
 
     f32x4 acc[4][NPAD / 16];
 #pragma unroll
@@ -874,32 +968,41 @@ __global__ __launch_bounds__(256) void spmm_bitmap_kernel(SpmmArgs a) {
 #pragma unroll
         for (int j = 0; j < NPAD / 16; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    for (int kt = kt0; kt < kt1; kt += P) {
+    const uint32_t rl = lane & 15, kq = lane >> 4;
+    for (int kt = kt0; kt < kt1; kt += 2) {
 #pragma unroll
-        for (int q = 0; q < P; ++q) {
+        for (int q = 0; q < 2; ++q) {
             const int k = kt + q;
-            const int n = nv[q];
-            if (n > 0) {
-                zero_tile(As, lane);
-#pragma unroll
-                for (int j = 0; j < R; ++j)
-                    if (j * 64 + lane < n) *reinterpret_cast<u32x4*>(reinterpret_cast<unsigned char*>(Vs) + (j * 64 + lane) * 16) = vb[q][j];
-                if (n > R * 64) {
-                    const uint32_t* tv = a.words + 4 * (size_t)first[q] + 4 * kMaskUnits;
-                    for (int v = R * 64 + lane; v < n; v += 64)
-                        *reinterpret_cast<u32x4*>(reinterpret_cast<unsigned char*>(Vs) + v * 16) =
-                            *reinterpret_cast<const u32x4*>(tv + 4 * (size_t)v);
-                }
-                bitmap_place(As, Vs, mlo[q], mhi[q], lane);
+            const u32x2 m = mk[q];
+            const uint32_t units = nu[q];
+            fetch_masks(q, k + 2);
+            fetch_values(q ^ 1);  // tile k + 1
+            if (units > 0) {
                 bf[q].store(Bw, lane);
-                mma_tile<NPAD>(acc, As, Bw, lane);
+                // chunk g = 2i + ks, expanded right before its MFMAs (k step outer, so that
+                // consecutive MFMAs write different accumulators)
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    half8 bfr[NPAD / 16];
+#pragma unroll
+                    for (int j = 0; j < NPAD / 16; ++j)
+                        bfr[j] = *reinterpret_cast<const half8*>(Bw + lds_chunk(j * 16 + rl, ks * 4 + kq));
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const half8 af =
+                            __builtin_bit_cast(half8, bitmap_chunk(xv[q], od[q], m[0], m[1], tbl, 2 * i + ks));
+#pragma unroll
+                        for (int j = 0; j < NPAD / 16; ++j)
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bfr[j], acc[i][j], 0, 0, 0);
+                    }
+                }
             }
-            fetch(q, k + P);
+            bf[q].load(bsrc, a.B, a.N, a.K, k + 2, lane, k + 2 < kt1);
         }
     }
 
-    // the wavefronts' sums, added in wavefront order (as in the independent-wavefront kernel)
-    float* red = reinterpret_cast<float*>(As);
+    // the wavefronts' sums, added in wavefront order
+    float* red = reinterpret_cast<float*>(Bw);
     const int ncol = lane & 15;
     const int mq = (lane >> 4) * 4;
 #pragma unroll
@@ -912,14 +1015,14 @@ __global__ __launch_bounds__(256) void spmm_bitmap_kernel(SpmmArgs a) {
     for (int it = tid; it < a.N * (kTileM / 4); it += WK * 64) {
         const int nn = it / (kTileM / 4);
         const int ml = (it - nn * (kTileM / 4)) * 4;
-        f32x4 sum = *reinterpret_cast<const f32x4*>(smem + (nn * kTileM + ml) * 4);
+        f32x4 sum = *reinterpret_cast<const f32x4*>(area + (nn * kTileM + ml) * 4);
 #pragma unroll
         for (int w = 1; w < WK; ++w)
-            sum += *reinterpret_cast<const f32x4*>(smem + w * kTileBytes + (nn * kTileM + ml) * 4);
-        const int m = rb * kTileM + ml;
-        if (m >= a.M) continue;
+            sum += *reinterpret_cast<const f32x4*>(area + w * kWaveBytes + (nn * kTileM + ml) * 4);
+        const int mm = rb * kTileM + ml;
+        if (mm >= a.M) continue;
         if (a.S == 1) {
-            uint16_t* dst = a.C + (int64_t)nn * a.M + m;
+            uint16_t* dst = a.C + (int64_t)nn * a.M + mm;
             if (vec_m) {
                 uint2 pk;
                 pk.x = (uint32_t)f16_bits(sum[0]) | ((uint32_t)f16_bits(sum[1]) << 16);
@@ -928,16 +1031,16 @@ __global__ __launch_bounds__(256) void spmm_bitmap_kernel(SpmmArgs a) {
             } else {
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    if (m + e < a.M) dst[e] = f16_bits(sum[e]);
+                    if (mm + e < a.M) dst[e] = f16_bits(sum[e]);
             }
         } else {
-            float* dst = a.part + ((int64_t)s * a.N + nn) * a.M + m;
+            float* dst = a.part + ((int64_t)s * a.N + nn) * a.M + mm;
             if (vec_m) {
                 *reinterpret_cast<f32x4*>(dst) = sum;
             } else {
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    if (m + e < a.M) dst[e] = sum[e];
+                    if (mm + e < a.M) dst[e] = sum[e];
             }
         }
     }
@@ -1415,42 +1518,32 @@ __global__ __launch_bounds__(kThreads) void decode_three_level_kernel(DecodeArgs
     }
 }
 
-// Dense view of a bitmap encoding through the same staging and placement code.
+// Dense view of a bitmap encoding through the same offset, load and expansion code: one
+// wavefront per tile, lane l writes its 8 operand chunks (8 columns each) to their rows.
 __global__ __launch_bounds__(kThreads) void decode_bitmap_kernel(DecodeArgs a) {
-    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * kWaves * kTileBytes];
+    __shared__ __attribute__((aligned(16))) unsigned char tbl[kBitmapTableBytes];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    unsigned char* As = smem + wave * kTileBytes;
-    uint16_t* Vs = reinterpret_cast<uint16_t*>(smem + (kWaves + wave) * kTileBytes);
-    const int64_t t = (int64_t)blockIdx.x * kWaves + wave;
-    const bool act = t < a.T;
-    uint32_t o0 = 0, o1 = 0;
-    if (act) {
-        o0 = a.offs[t];
-        o1 = a.offs[t + 1];
-    }
-    zero_tile(As, lane);
-    if (o1 > o0) {
-        const uint32_t* tw = a.words + 4 * (size_t)o0;
-        const uint32_t mlo = tw[2 * lane], mhi = tw[2 * lane + 1];
-        const int n = (int)(o1 - o0) - kMaskUnits;
-        for (int v = lane; v < n; v += 64)
-            *reinterpret_cast<u32x4*>(reinterpret_cast<unsigned char*>(Vs) + v * 16) =
-                *reinterpret_cast<const u32x4*>(tw + 4 * kMaskUnits + 4 * (size_t)v);
-        bitmap_place(As, Vs, mlo, mhi, lane);
-    }
+    if (wave == 0) bitmap_table(tbl, lane);
     __syncthreads();
-    if (!act) return;
+    const int64_t t = (int64_t)blockIdx.x * kWaves + wave;
+    if (t >= a.T) return;
+    const uint32_t o0 = a.offs[t], units = a.offs[t + 1] - o0;
+    const u32x2 m = bitmap_load_masks(a.words, o0, units, lane);
+    uint32_t voff[16];
+    bitmap_group_offsets(m[0], m[1], voff);
+    u32x3 x[16];
+    bitmap_load_values(x, a.words, o0, units, voff);
+    const uint32_t odd = bitmap_odd_starts(voff);
     const int bm = (int)(t / a.KT), bk = (int)(t % a.KT);
 #pragma unroll
-    for (int p = 0; p < 8; ++p) {
-        const int ch = p * 64 + lane;
-        const int r = ch >> 3, c = ch & 7;
-        const int gi = bm * kTileM + r, gj = bk * kTileK + c * 8;
+    for (int g = 0; g < 8; ++g) {
+        const int gi = bm * kTileM + 16 * (g >> 1) + (lane & 15);
+        const int gj = bk * kTileK + 32 * (g & 1) + 8 * (lane >> 4);
         if (gi >= a.M || gj >= a.K) continue;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(As + lds_chunk(r, c));
         uint16_t* dst = a.A + (int64_t)gi * a.K + gj;
+        const u32x4 v = bitmap_chunk(x, odd, m[0], m[1], tbl, g);
         if ((a.K & 7) == 0 && gj + 8 <= a.K) {
             *reinterpret_cast<u32x4*>(dst) = v;
         } else {
@@ -1620,22 +1713,16 @@ hipError_t launch_spmm_n(int kind, int R, const SpmmArgs& a, int grid, hipStream
     }
 }
 
-template <int NPAD>
-hipError_t launch_bitmap_n(int R, const SpmmArgs& a, int grid, hipStream_t st, int* occ) {
-    if ((a.K & 7) != 0) return run(spmm_bitmap_kernel<NPAD, 2, false>, a, grid, st, occ);
-    switch (R) {
-        case 1: return run(spmm_bitmap_kernel<NPAD, 1, true>, a, grid, st, occ);
-        case 2: return run(spmm_bitmap_kernel<NPAD, 2, true>, a, grid, st, occ);
-        case 4: return run(spmm_bitmap_kernel<NPAD, 4, true>, a, grid, st, occ);
-        case 8: return run(spmm_bitmap_kernel<NPAD, 8, true>, a, grid, st, occ);
-        default: return hipErrorInvalidValue;
-    }
+template <int NPAD, int WK>
+hipError_t launch_bitmap_n(const SpmmArgs& a, int grid, hipStream_t st, int* occ) {
+    if ((a.K & 7) != 0) return run(spmm_bitmap_kernel<NPAD, WK, false>, a, grid, st, occ, WK * 64);
+    return run(spmm_bitmap_kernel<NPAD, WK, true>, a, grid, st, occ, WK * 64);
 }
 
-hipError_t launch_bitmap_any(int npad, int R, const SpmmArgs& a, int grid, hipStream_t st, int* occ) {
+hipError_t launch_bitmap_any(int npad, const SpmmArgs& a, int grid, hipStream_t st, int* occ) {
     switch (npad) {
-        case 16: return launch_bitmap_n<16>(R, a, grid, st, occ);
-        case 32: return launch_bitmap_n<32>(R, a, grid, st, occ);
+        case 16: return launch_bitmap_n<16, kBitmapWaves>(a, grid, st, occ);
+        case 32: return launch_bitmap_n<32, kBitmapWaves>(a, grid, st, occ);
         default: return hipErrorInvalidValue;
     }
 }
@@ -1748,7 +1835,7 @@ int pick_reg_vectors_wide(int32_t max_tile_words) {
 
 hipError_t launch_spmm(int kind, int npad, int R, const SpmmArgs& a, int grid, hipStream_t st) {
     if (kind == kKernelWide) return launch_wide_any(npad, R, a, grid, st, nullptr);
-    if (kind == kKernelBitmap) return launch_bitmap_any(npad, R, a, grid, st, nullptr);
+    if (kind == kKernelBitmap) return launch_bitmap_any(npad, a, grid, st, nullptr);
     if (kind == kKernelThreeLevel) return launch_three_level_any(npad, a, grid, st, nullptr);
     switch (npad) {
         case 16: return launch_spmm_n<16>(kind, R, a, grid, st, nullptr);
@@ -1766,7 +1853,7 @@ int spmm_blocks_per_cu(int kind, int npad, int R, int K, int TM) {
     hipError_t e = hipErrorInvalidValue;
     if (kind == kKernelWide) return (launch_wide_any(npad, R, dummy, 0, nullptr, &occ) == hipSuccess && occ > 0) ? occ : 1;
     if (kind == kKernelBitmap)
-        return (launch_bitmap_any(npad, R, dummy, 0, nullptr, &occ) == hipSuccess && occ > 0) ? occ : 1;
+        return (launch_bitmap_any(npad, dummy, 0, nullptr, &occ) == hipSuccess && occ > 0) ? occ : 1;
     if (kind == kKernelThreeLevel)
         return (launch_three_level_any(npad, dummy, 0, nullptr, &occ) == hipSuccess && occ > 0) ? occ : 1;
     switch (npad) {
@@ -1794,16 +1881,6 @@ hipError_t launch_decode_bitmap(const DecodeArgs& a, int grid, hipStream_t st) {
 hipError_t launch_decode_three_level(const DecodeArgs& a, int grid, hipStream_t st) {
     hipLaunchKernelGGL(decode_three_level_kernel, dim3(grid), dim3(kThreads), 0, st, a);
     return hipGetLastError();
-}
-
-int pick_reg_vectors_bitmap(int32_t max_tile_words) {
-    // value vectors of the largest tile (its words minus the masks), per lane
-    const int vec = max_tile_words / 4 > kMaskUnits ? max_tile_words / 4 - kMaskUnits : 0;
-    const int need = (vec + 63) / 64;
-    int r = need <= 1 ? 1 : (need <= 2 ? 2 : (need <= 4 ? 4 : 8));
-    if (const char* e = getenv("LSCD_MAX_R"))  // tests: force the path for tiles past the stage
-        if (atoi(e) > 0 && atoi(e) < r) r = atoi(e) >= 4 ? 4 : (atoi(e) >= 2 ? 2 : 1);
-    return r;
 }
 
 hipError_t launch_decode(int R, const DecodeArgs& a, int grid, hipStream_t st) {

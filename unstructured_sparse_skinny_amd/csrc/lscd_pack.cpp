@@ -185,14 +185,17 @@ void pack_fill(const uint16_t* A, const uint8_t* mask, const Grid& g, const uint
 
 // ---------------------------------------------------------------- bitmap tiles
 // Layout (follow-up summary of the pages, section "Problematica": one bit per position in
-// place of per-entry positions): a tile with k kept entries stores tm 64-bit row masks,
-// little-endian (bit c of mask r = entry (r, c) kept), then the k fp16 values in row-major
-// order padded with zeros to a multiple of 8 values; an empty tile stores nothing.
-// Offsets count 16-byte units.
+// place of per-entry positions), 64 x 64 tiles: the positions of a tile are numbered in the
+// operand order of the 16x16x32 MFMA -- lane l, bit b (chunk g = b/8, element b%8) is tile row
+// 16*(g/2) + l%16, column 32*(g%2) + 8*(l/16) + b%8 -- and a tile with k kept entries stores the
+// 64 lane masks (64-bit, little-endian), then its values chunk by chunk: for g = 0..7 the
+// values of bits 8g..8g+7 of lanes 0..63, lane after lane, each lane's in ascending bit order;
+// padded with zeros to a multiple of 8 values.  An empty tile stores nothing.  Offsets count
+// 16-byte units.
 
 lscd_status_t bitmap_offsets(const uint16_t* A, const uint8_t* mask, const Grid& g, std::vector<uint32_t>* offsets,
                              int64_t* nnz_out) {
-    if (g.tk > 64) return LSCD_ERROR_INVALID_VALUE;
+    if (g.tm != 64 || g.tk != 64) return LSCD_ERROR_INVALID_VALUE;
     std::vector<int64_t> cnt((size_t)g.T, 0);
     parallel_for(g.MB, [&](int64_t lo, int64_t hi) {
         for (int64_t bm = lo; bm < hi; ++bm) {
@@ -226,27 +229,40 @@ lscd_status_t bitmap_offsets(const uint16_t* A, const uint8_t* mask, const Grid&
 void bitmap_fill(const uint16_t* A, const uint8_t* mask, const Grid& g, const uint32_t* offsets, uint32_t* words) {
     parallel_for(g.MB, [&](int64_t lo, int64_t hi) {
         for (int64_t bm = lo; bm < hi; ++bm) {
-            const int64_t r0 = bm * g.tm, r1 = std::min<int64_t>(g.M, r0 + g.tm);
+            const int64_t r0 = bm * 64, r1 = std::min<int64_t>(g.M, r0 + 64);
             for (int64_t bk = 0; bk < g.KT; ++bk) {
                 const int64_t t = bm * g.KT + bk;
                 if (offsets[t + 1] == offsets[t]) continue;
                 uint32_t* out = words + 4 * (size_t)offsets[t];
-                uint16_t* vals = reinterpret_cast<uint16_t*>(out + 2 * (size_t)g.tm);
                 const size_t nwords = 4 * (size_t)(offsets[t + 1] - offsets[t]);
                 memset(out, 0, nwords * 4);
-                const int64_t c0 = bk * g.tk, c1 = std::min<int64_t>(g.K, c0 + g.tk);
-                size_t v = 0;
+                const int64_t c0 = bk * 64, c1 = std::min<int64_t>(g.K, c0 + 64);
+                uint64_t m[64] = {};
                 for (int64_t r = r0; r < r1; ++r) {
                     const size_t base = (size_t)r * (size_t)g.K;
-                    uint64_t m = 0;
+                    const int rr = (int)(r - r0);
                     for (int64_t c = c0; c < c1; ++c) {
-                        if (kept(A, mask, base + (size_t)c)) {
-                            m |= (uint64_t)1 << (c - c0);
-                            vals[v++] = A[base + (size_t)c];
+                        if (!kept(A, mask, base + (size_t)c)) continue;
+                        const int cc = (int)(c - c0);
+                        const int lane = rr % 16 + 16 * ((cc % 32) / 8);
+                        const int bit = 8 * (2 * (rr / 16) + cc / 32) + cc % 8;
+                        m[lane] |= (uint64_t)1 << bit;
+                    }
+                }
+                for (int l = 0; l < 64; ++l) {
+                    out[2 * l] = (uint32_t)m[l];
+                    out[2 * l + 1] = (uint32_t)(m[l] >> 32);
+                }
+                uint16_t* vals = reinterpret_cast<uint16_t*>(out + 128);
+                size_t v = 0;
+                for (int gg = 0; gg < 8; ++gg) {
+                    for (int l = 0; l < 64; ++l) {
+                        for (int bit = 8 * gg; bit < 8 * gg + 8; ++bit) {
+                            if (!((m[l] >> bit) & 1)) continue;
+                            const int rr = 16 * (gg / 2) + l % 16, cc = 32 * (gg % 2) + 8 * (l / 16) + bit % 8;
+                            vals[v++] = A[(size_t)(r0 + rr) * (size_t)g.K + (size_t)(c0 + cc)];
                         }
                     }
-                    out[2 * (r - r0)] = (uint32_t)m;
-                    out[2 * (r - r0) + 1] = (uint32_t)(m >> 32);
                 }
             }
         }
