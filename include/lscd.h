@@ -62,7 +62,8 @@ typedef struct {
     int32_t max_tile_words;     /* largest tile, in words                                  */
     int32_t device;             /* HIP device the handle's buffers live on                 */
     int64_t workspace_bytes;    /* device split-K workspace owned by the handle            */
-    int32_t reg_vectors;        /* 128-bit staging registers per lane and tile (kernel cfg) */
+    int32_t reg_vectors;        /* 128-bit staging registers per lane and tile of the
+                                   Tiled-CSL kernels; 0 for formats 1 and 2 (fixed loads)   */
     int32_t splits[3];          /* K-splits across workgroups lscd_spmm uses for N padded to
                                    16, 32 and 64 (1: no second pass)                        */
     int32_t variant[3];         /* product kernel variant for N padded to 16, 32, 64:
