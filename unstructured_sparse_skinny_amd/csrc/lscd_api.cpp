@@ -174,7 +174,7 @@ lscd_status_t new_handle(const Grid& g, int64_t nnz, int64_t nwords, int32_t max
             if (h->S[i] > 1) part = std::max<int64_t>(part, (int64_t)h->S[i] * g.M * npad * 4);
         }
     }
-    if (format == 0) h->R = tall ? pick_reg_vectors_tall(maxw) : pick_reg_vectors(maxw);
+    h->R = format != 0 ? 0 : (tall ? pick_reg_vectors_tall(maxw) : pick_reg_vectors(maxw));
     for (int i = 0; i < 3 && kernel_tile && format == 0; ++i) {
         // Tiles taller than 64 rows: eight wavefronts per row block for N <= 32, the shared B
         // tile above.
@@ -634,7 +634,7 @@ lscd_status_t lscd_spmm(lscd_handle_t h, const void* B, void* C, int32_t N, void
             a.S = h->S[npad_index(n)];
             a.items = a.G * a.S;
             a.per_xcd = (a.items + 7) / 8;
-            hipError_t e = lscd::launch_spmm(lscd::kKernelBitmap, npad, h->R, a, 8 * a.per_xcd, s);
+            hipError_t e = lscd::launch_spmm(lscd::kKernelBitmap, npad, 0, a, 8 * a.per_xcd, s);
             if (e != hipSuccess) return hip_status(e);
             if (a.S > 1) {
                 e = lscd::launch_reduce(h->d_part, a.C, a.S, (int64_t)n * h->g.M, s);
