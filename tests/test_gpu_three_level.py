@@ -42,7 +42,7 @@ def test_three_level_decode_and_export_bit_exact(M, K, keep):
     case = syn.random_case(M, K, 1, keep, seed=M * 7 + K)
     say(f"three-level decode M={M} K={K} keep={keep}")
     h = L.lscd_encode_three_level(case.A16, case.mask)
-    assert h.info["format"] == 2 and h.info["nnz"] == int(case.mask.sum())
+    assert h.info["format"] == 2 and h.info["nnz"] == int(case.mask.sum()) and h.info["reg_vectors"] == 0
     A = torch.empty((M, K), dtype=torch.float16, device="cuda")
     L.lscd_debug_decode(h, A)
     torch.cuda.synchronize()
