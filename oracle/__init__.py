@@ -22,7 +22,8 @@ What it computes, from the Flash-LLM pages:
   C[n][i] = sum_k A[i][k] * B[n][k], accumulated in fp64.
 * `bitmap` -- the bitmap-tile variant of the format (the pages' follow-up summary,
   section "Problematica": one bit per position instead of per-entry positions): per
-  tile, 64-bit row masks followed by the kept values in row-major order.
+  tile, 64 lane masks whose bits follow the matrix-core operand layout, then the kept
+  values chunk by chunk.
 * `accounting` -- the compute-intensity formula and the byte/flop counts used
   for effective bandwidth (same review, section 3 "core formulas").
 
