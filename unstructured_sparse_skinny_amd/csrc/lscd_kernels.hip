@@ -871,17 +871,11 @@ __device__ __forceinline__ u32x2 bitmap_load_masks(const uint32_t* words, uint32
     return __builtin_amdgcn_raw_buffer_load_b64(ms, lane * 8, 0, kStreamPolicy);
 }
 
-// Bit i set: group i's run starts in the high half of its load's first dword.
-__device__ __forceinline__ uint32_t bitmap_odd_starts(const uint32_t (&voff)[16]) {
-    uint32_t b = 0;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) b |= ((voff[i] >> 1) & 1u) << i;
-    return b;
-}
-
-// A operand of lane `lane` for chunk g: 4 dwords, elements 8g .. 8g+7 of its mask.
-__device__ __forceinline__ u32x4 bitmap_chunk(const u32x3 (&x)[16], uint32_t odd, uint32_t lo, uint32_t hi,
-                                              const unsigned char* tbl, int g) {
+// A operand of lane `lane` for chunk g: 4 dwords, elements 8g .. 8g+7 of its mask.  voff are
+// the groups' byte offsets: v_alignbit_b32 reads bits 4:0 of voff << 3, i.e. 16 when the run
+// starts in the high half of its first dword, 0 otherwise.
+__device__ __forceinline__ u32x4 bitmap_chunk(const u32x3 (&x)[16], const uint32_t (&voff)[16], uint32_t lo,
+                                              uint32_t hi, const unsigned char* tbl, int g) {
     const uint32_t m = g < 4 ? lo : hi;
     u32x4 r;
 #pragma unroll
@@ -889,7 +883,7 @@ __device__ __forceinline__ u32x4 bitmap_chunk(const u32x3 (&x)[16], uint32_t odd
         const uint32_t q = (m >> (8 * (g & 3) + 4 * h)) & 0xFu;
         const u32x2 s = *reinterpret_cast<const u32x2*>(tbl + q * 8);
         const u32x3 v = x[2 * g + h];
-        const uint32_t sh = ((odd >> (2 * g + h)) & 1u) << 4;  // 16 or 0
+        const uint32_t sh = voff[2 * g + h] << 3;
         const uint32_t v0 = __builtin_amdgcn_alignbit(v[1], v[0], sh);
         const uint32_t v1 = __builtin_amdgcn_alignbit(v[2], v[1], sh);
         r[2 * h] = __builtin_amdgcn_perm(v1, v0, s[0]);
@@ -900,9 +894,10 @@ __device__ __forceinline__ u32x4 bitmap_chunk(const u32x3 (&x)[16], uint32_t odd
 
 // Bitmap-tile product for N <= 32 per launch: a workgroup owns one row block and its WK
 // wavefronts split the k range; each wavefront keeps its own B tile in LDS and needs no
-// barrier until the final sum over wavefronts.  Pipeline: masks two tiles ahead, values one
-// tile ahead (their offsets need the masks), B two tiles ahead.
-template <int NPAD, int WK, bool VEC>
+// barrier until the final sum over wavefronts.  Pipeline of P stages: masks P tiles ahead,
+// values P - 1 tiles ahead (their offsets need the masks).  B is one tile ahead in one set of
+// registers, loaded first in each step: waiting for it never waits for the value loads.
+template <int NPAD, int WK, int P, bool VEC>
 __global__ __launch_bounds__(WK * 64) void spmm_bitmap_kernel(SpmmArgs a) {
     constexpr int kBBytes = NPAD * kRowBytes;
     constexpr int kRedBytes = NPAD * kTileM * 4;
@@ -931,12 +926,12 @@ __global__ __launch_bounds__(WK * 64) void spmm_bitmap_kernel(SpmmArgs a) {
     const __amdgpu_buffer_rsrc_t bsrc =
         __builtin_amdgcn_make_buffer_rsrc((void*)a.B, (short)0, a.N * a.K * 2, kBufWord3);
 
-    u32x2 mk[2];          // lane masks of the tile in each stage
-    uint32_t fu[2];       // its first 16-byte unit
-    uint32_t nu[2];       // its 16-byte units (0: empty)
-    u32x3 xv[2][16];      // its value loads
-    uint32_t od[2];       // and which of them start at an odd value
-    BWave<NPAD, VEC> bf[2];
+    u32x2 mk[P];          // lane masks of the tile in each stage
+    uint32_t fu[P];       // its first 16-byte unit
+    uint32_t nu[P];       // its 16-byte units (0: empty)
+    u32x3 xv[P][16];      // its value loads
+    uint32_t vo[P][16];   // and their groups' byte offsets
+    BWave<NPAD, VEC> bw;  // B tile of the current step's tile
     auto fetch_masks = [&](int q, int k) {
         uint32_t o0 = 0, o1 = 0;
         if (k < kt1) {
@@ -948,19 +943,17 @@ __global__ __launch_bounds__(WK * 64) void spmm_bitmap_kernel(SpmmArgs a) {
         mk[q] = bitmap_load_masks(a.words, o0, o1 - o0, lane);
     };
     auto fetch_values = [&](int q) {
-        uint32_t voff[16];
-        bitmap_group_offsets(mk[q][0], mk[q][1], voff);
-        bitmap_load_values(xv[q], a.words, fu[q], nu[q], voff);
-        od[q] = bitmap_odd_starts(voff);
+        bitmap_group_offsets(mk[q][0], mk[q][1], vo[q]);
+        bitmap_load_values(xv[q], a.words, fu[q], nu[q], vo[q]);
     };
-    fetch_masks(0, kt0);
-    bf[0].load(bsrc, a.B, a.N, a.K, kt0, lane, kt0 < kt1);
-    fetch_masks(1, kt0 + 1);
-    bf[1].load(bsrc, a.B, a.N, a.K, kt0 + 1, lane, kt0 + 1 < kt1);
-    // issue order as in the loop (the next masks before the current values), so that the wait
-    // for the next masks at the top of the loop leaves the current values in flight
+    bw.load(bsrc, a.B, a.N, a.K, kt0, lane, kt0 < kt1);
+#pragma unroll
+    for (int q = 0; q < P; ++q) fetch_masks(q, kt0 + q);
+    // issue order as in the loop (the masks of later tiles before the values of earlier
+    // ones), so that waiting for masks leaves the values in flight
     __builtin_amdgcn_sched_barrier(0);
-    fetch_values(0);
+#pragma unroll
+    for (int q = 0; q + 1 < P; ++q) fetch_values(q);
 
     f32x4 acc[4][NPAD / 16];
 #pragma unroll
@@ -969,16 +962,17 @@ __global__ __launch_bounds__(WK * 64) void spmm_bitmap_kernel(SpmmArgs a) {
         for (int j = 0; j < NPAD / 16; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const uint32_t rl = lane & 15, kq = lane >> 4;
-    for (int kt = kt0; kt < kt1; kt += 2) {
+    for (int kt = kt0; kt < kt1; kt += P) {
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
+        for (int q = 0; q < P; ++q) {
             const int k = kt + q;
             const u32x2 m = mk[q];
             const uint32_t units = nu[q];
-            fetch_masks(q, k + 2);
-            fetch_values(q ^ 1);  // tile k + 1
+            if (units > 0) bw.store(Bw, lane);
+            bw.load(bsrc, a.B, a.N, a.K, k + 1, lane, k + 1 < kt1);
+            fetch_masks(q, k + P);
+            fetch_values((q + P - 1) % P);  // tile k + P - 1
             if (units > 0) {
-                bf[q].store(Bw, lane);
                 // chunk g = 2i + ks, expanded right before its MFMAs (k step outer, so that
                 // consecutive MFMAs write different accumulators)
 #pragma unroll
@@ -990,14 +984,13 @@ __global__ __launch_bounds__(WK * 64) void spmm_bitmap_kernel(SpmmArgs a) {
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const half8 af =
-                            __builtin_bit_cast(half8, bitmap_chunk(xv[q], od[q], m[0], m[1], tbl, 2 * i + ks));
+                            __builtin_bit_cast(half8, bitmap_chunk(xv[q], vo[q], m[0], m[1], tbl, 2 * i + ks));
 #pragma unroll
                         for (int j = 0; j < NPAD / 16; ++j)
                             acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bfr[j], acc[i][j], 0, 0, 0);
                     }
                 }
             }
-            bf[q].load(bsrc, a.B, a.N, a.K, k + 2, lane, k + 2 < kt1);
         }
     }
 
@@ -1535,7 +1528,6 @@ __global__ __launch_bounds__(kThreads) void decode_bitmap_kernel(DecodeArgs a) {
     bitmap_group_offsets(m[0], m[1], voff);
     u32x3 x[16];
     bitmap_load_values(x, a.words, o0, units, voff);
-    const uint32_t odd = bitmap_odd_starts(voff);
     const int bm = (int)(t / a.KT), bk = (int)(t % a.KT);
 #pragma unroll
     for (int g = 0; g < 8; ++g) {
@@ -1543,7 +1535,7 @@ __global__ __launch_bounds__(kThreads) void decode_bitmap_kernel(DecodeArgs a) {
         const int gj = bk * kTileK + 32 * (g & 1) + 8 * (lane >> 4);
         if (gi >= a.M || gj >= a.K) continue;
         uint16_t* dst = a.A + (int64_t)gi * a.K + gj;
-        const u32x4 v = bitmap_chunk(x, odd, m[0], m[1], tbl, g);
+        const u32x4 v = bitmap_chunk(x, voff, m[0], m[1], tbl, g);
         if ((a.K & 7) == 0 && gj + 8 <= a.K) {
             *reinterpret_cast<u32x4*>(dst) = v;
         } else {
@@ -1715,8 +1707,9 @@ hipError_t launch_spmm_n(int kind, int R, const SpmmArgs& a, int grid, hipStream
 
 template <int NPAD, int WK>
 hipError_t launch_bitmap_n(const SpmmArgs& a, int grid, hipStream_t st, int* occ) {
-    if ((a.K & 7) != 0) return run(spmm_bitmap_kernel<NPAD, WK, false>, a, grid, st, occ, WK * 64);
-    return run(spmm_bitmap_kernel<NPAD, WK, true>, a, grid, st, occ, WK * 64);
+    constexpr int P = 2;  // three stages measured no faster
+    if ((a.K & 7) != 0) return run(spmm_bitmap_kernel<NPAD, WK, P, false>, a, grid, st, occ, WK * 64);
+    return run(spmm_bitmap_kernel<NPAD, WK, P, true>, a, grid, st, occ, WK * 64);
 }
 
 hipError_t launch_bitmap_any(int npad, const SpmmArgs& a, int grid, hipStream_t st, int* occ) {
