@@ -152,7 +152,7 @@ lscd_status_t lscd_encode_tiled(const uint16_t* A, const uint8_t* mask, int64_t 
  *   argument rules as lscd_pack; tiles are always 64 x 64) into caller arrays of nwords
  *   32-bit words and num_tiles + 1 offsets.
  * lscd_encode_bitmap -- pack and upload, like lscd_encode.  The handle works with every
- *   entry point taking a handle: lscd_spmm runs the bitmap kernel in launches of up to 32
+ *   entry point taking a handle: lscd_spmm runs the bitmap kernel in launches of up to 64
  *   columns; lscd_export returns the blob and its offsets; lscd_debug_decode and
  *   lscd_attach_dense decode it.
  */

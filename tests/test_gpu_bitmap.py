@@ -1,6 +1,7 @@
 """GPU parity of the bitmap-tile path (lscd_encode_bitmap + lscd_spmm / lscd_debug_decode).
 
-Bit-exact: the decoded matrix, the exported blob against the host encoder, fully dense tiles, integer-valued products for N across the 16 / 32-column launch
+Bit-exact: the decoded matrix, the exported blob against the host encoder, fully dense tiles,
+full chunks at odd starts, integer-valued products for N across the 16 / 32 / 64-column launch
 boundaries with forced K splits.  Tolerance gates (tests/_util.py) for Gaussian inputs on
 ragged shapes and, with sampled rows, at full OPT shapes.
 """
@@ -50,7 +51,7 @@ def test_bitmap_decode_and_export_bit_exact(M, K, keep):
     assert np.array_equal(words, ow) and np.array_equal(offs, oo)
 
 
-@pytest.mark.parametrize("N", [16, 32])
+@pytest.mark.parametrize("N", [16, 32, 64])
 def test_bitmap_full_tiles_bit_exact(N):
     # every position kept: all 16 groups of every lane hold 4 values
     case = syn.random_case(200, 300, N, 1.0, seed=2, values="int3")
@@ -116,3 +117,29 @@ def test_bitmap_linear_dense_path():
     L.lscd_linear(h, B, C)
     torch.cuda.synchronize()
     assert np.array_equal(C.cpu().numpy().view(np.uint16), osp.fp16_rne(osp.spmm_f64(case.A16, case.mask, case.B16)))
+
+
+def test_bitmap_full_chunk_at_odd_start():
+    # A full chunk (8 kept positions) whose run starts at an odd value needs one value past its
+    # 16-byte window: lane 5 and lane 62 take it from the next lane, lane 63 from a scalar load.
+    # Lane l, chunk g holds row 16*(g//2) + l%16, columns 32*(g%2) + 8*(l//16) .. +7.
+    M, K, N = 80, 100, 16
+    mask = np.zeros((M, K), dtype=np.uint8)
+    mask[0, 0] = 1                      # lane 0, chunk 0: one value, so later runs start odd
+    mask[5, 0:8] = 1                    # lane 5, chunk 0: full, start 1
+    mask[15, 24:32] = 1                 # lane 63, chunk 0: full, start 9
+    mask[32, 32:34] = 1                 # lane 0, chunk 5: two values (chunk 5 starts at 17)
+    mask[46, 56:64] = 1                 # lane 62, chunk 5: full, start 19
+    mask[47, 56:64] = 1                 # lane 63, chunk 5: full, start 27
+    mask[64:, 64:] = 1                  # a ragged, dense second-row tile
+    rng = np.random.default_rng(31)
+    A16 = syn.int_fp16(rng, M, K)
+    B16 = syn.int_fp16(rng, N, K)
+    for r, c in ((5, 0), (15, 24), (46, 56), (47, 56)):
+        assert ob.lane_bit(r, c)[1] % 8 == 0
+    h = L.lscd_encode_bitmap(A16, mask)
+    A = torch.empty((M, K), dtype=torch.float16, device="cuda")
+    L.lscd_debug_decode(h, A)
+    torch.cuda.synchronize()
+    assert np.array_equal(A.cpu().numpy().view(np.uint16), tc.masked(A16, mask))
+    assert np.array_equal(run(h, B16, M), osp.fp16_rne(osp.spmm_f64(A16, mask, B16)))

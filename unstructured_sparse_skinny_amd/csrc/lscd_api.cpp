@@ -151,9 +151,9 @@ lscd_status_t new_handle(const Grid& g, int64_t nnz, int64_t nwords, int32_t max
     const bool tall = g.tm != kTileM;
     int64_t part = 0;
     if (format == 1) {
-        // bitmap tiles: one kernel, launches of <= 32 columns
+        // bitmap tiles: one kernel, launches of <= 64 columns
         for (int i = 0; i < 3 && kernel_tile; ++i) {
-            const int npad = i == 0 ? 16 : 32;
+            const int npad = 16 << i;
             h->kind[i] = kKernelBitmap;
             const int occ = spmm_blocks_per_cu(kKernelBitmap, npad, 0, (int)std::min<int64_t>(g.K, 1 << 30));
             h->S[i] = plan_splits(g, h->cus, occ, g.MB, 4 * kBitmapWaves, false);  // fill the resident slots
@@ -623,10 +623,10 @@ lscd_status_t lscd_spmm(lscd_handle_t h, const void* B, void* C, int32_t N, void
     a.KT = (int32_t)h->g.KT;
     a.TM = h->g.tm;
     if (h->format == 1) {
-        // bitmap tiles: launches of up to 32 columns (the packed tile is read once per launch)
+        // bitmap tiles: launches of up to 64 columns (the packed tile is read once per launch)
         for (int32_t c0 = 0; c0 < N; c0 += lscd::kBitmapMaxN) {
             const int32_t n = std::min(N - c0, lscd::kBitmapMaxN);
-            const int npad = n <= 16 ? 16 : 32;
+            const int npad = n <= 16 ? 16 : (n <= 32 ? 32 : 64);
             a.B = (const uint16_t*)B + (int64_t)c0 * h->g.K;
             a.C = (uint16_t*)C + (int64_t)c0 * h->g.M;
             a.N = n;

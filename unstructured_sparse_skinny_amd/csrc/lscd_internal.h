@@ -120,11 +120,11 @@ constexpr int kKernelIndep8 = 2;  // 8 wavefronts per row block
 constexpr int kKernelWide = 3;
 constexpr int kWideMaxN = 256;
 // Bitmap-tile format: one row block per workgroup, kBitmapWaves wavefronts over its k range,
-// N padded to 16 or 32 per launch (wider N runs launches of 32 columns).  The allocation of a
+// N padded to 16, 32 or 64 per launch (wider N runs launches of 64 columns).  The allocation of a
 // bitmap blob carries kBitmapSlackBytes past its end: a tile's value loads may read up to that
 // far past its last value.
 constexpr int kKernelBitmap = 4;
-constexpr int kBitmapMaxN = 32;
+constexpr int kBitmapMaxN = 64;
 constexpr int kBitmapWaves = 4;
 constexpr int kBitmapSlackBytes = 16;
 // Three-level tiles (4:2 layer on the structured-sparse MFMA, slot filling, residual): one

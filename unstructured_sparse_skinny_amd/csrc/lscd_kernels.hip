@@ -770,14 +770,15 @@ __global__ __launch_bounds__(kThreads) void spmm_wide_kernel(SpmmArgs a) {
 // lane masks (512 bytes), then its values chunk by chunk (chunk g of lanes 0..63 in lane
 // order), padded to 16-byte vectors; offsets count 16-byte units.
 //
-// Decoding needs no LDS tile: a lane finds where each of its 4-bit groups starts in the value
+// Decoding needs no LDS tile: a lane finds where each of its 8 chunk runs starts in the value
 // stream (a prefix over the wavefront of its chunk counts, plus the chunk totals before it),
-// fetches the group's up to 4 values with one dword-aligned 12-byte load, shifts them down by
-// 16 bits when the group starts at an odd value, and spreads them to the group's positions
-// with two byte permutes (v_perm_b32) whose selectors come from a 16-entry table.  (Loads at
-// 2-byte alignment were measured at about 1000 CU cycles per tile whatever the density.)  In
-// chunk-major order the lanes of one load read neighbouring runs, a few cache lines per
-// instruction.
+// fetches each run with one dword-aligned 16-byte load, shifts each 4-bit group's values into
+// place (v_alignbit_b32) and spreads them to the group's positions with two byte permutes
+// (v_perm_b32) whose selectors come from a 16-entry table.  In chunk-major order the lanes of
+// one load read neighbouring runs, a few cache lines per instruction.  Measured: the product
+// is bound by the number of vector memory instructions per tile more than by their bytes (8-
+// and 12-byte loads at 2-byte alignment cost about 1000 and 650 CU cycles per tile at any
+// density; one 16-byte load per chunk instead of one 12-byte load per group took 17-25 % off).
 constexpr int kMaskUnits = kTileM * 8 / 16;     // 16-byte units of a tile's masks (32)
 constexpr int kMaskBytes = kMaskUnits * 16;     // 512
 constexpr int kBitmapTableBytes = 16 * 8;       // selector table: 16 groups x 2 dwords
@@ -819,11 +820,10 @@ __device__ __forceinline__ uint32_t wave_scan(uint32_t x) {
     return x;
 }
 
-// Byte offsets (from the tile's first value) of the 16 groups of lane masks (lo, hi): group
-// 2g + h is bits 8g + 4h .. +3.  Chunk counts are packed 10 bits a field, three fields a word,
-// so three wavefront scans give every chunk's lane prefix; the chunk totals (lane 63's
-// inclusive sums) are wave-uniform.
-__device__ __forceinline__ void bitmap_group_offsets(uint32_t lo, uint32_t hi, uint32_t (&voff)[16]) {
+// Value index (from the tile's first value) where each of the lane's 8 chunk runs starts.
+// Chunk counts are packed 10 bits a field, three fields a word, so three wavefront scans give
+// every chunk's lane prefix; the chunk totals (lane 63's inclusive sums) are wave-uniform.
+__device__ __forceinline__ void bitmap_chunk_starts(uint32_t lo, uint32_t hi, uint32_t (&first)[8]) {
     uint32_t c[8];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
@@ -843,24 +843,22 @@ __device__ __forceinline__ void bitmap_group_offsets(uint32_t lo, uint32_t hi, u
 #pragma unroll
     for (int g = 0; g < 8; ++g) {
         const int w = g / 3, f = 10 * (g % 3);
-        const uint32_t first = base + ((e[w] >> f) & 0x3FFu);
-        const uint32_t m = g < 4 ? lo : hi;
-        voff[2 * g] = 2u * first;
-        voff[2 * g + 1] = 2u * (first + (uint32_t)__popc((m >> (8 * (g & 3))) & 0xFu));
+        first[g] = base + ((e[w] >> f) & 0x3FFu);
         base += (t[w] >> f) & 0x3FFu;
     }
 }
 
-// The 16 value loads of a tile, each the dword-aligned 12 bytes around its group's run.  The
-// descriptor covers the values plus the slack, so a load that holds at least one of the
-// group's values lies wholly inside it (it ends at most 10 bytes past the group's last value).
-__device__ __forceinline__ void bitmap_load_values(u32x3 (&x)[16], const uint32_t* words, uint32_t first_unit,
-                                                   uint32_t units, const uint32_t (&voff)[16]) {
+// The 8 value loads of a tile: for each chunk, the dword-aligned 16 bytes from the start of
+// the lane's run.  The descriptor covers the values plus the slack, and every load lies
+// wholly inside it (it ends at most 16 bytes past the run's start, which is at most the
+// value count).
+__device__ __forceinline__ void bitmap_load_values(u32x4 (&x)[8], const uint32_t* words, uint32_t first_unit,
+                                                   uint32_t units, const uint32_t (&first)[8]) {
     const __amdgpu_buffer_rsrc_t vs = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(words + 4 * (size_t)first_unit + 4 * kMaskUnits), (short)0,
         units > (uint32_t)kMaskUnits ? (int)((units - kMaskUnits) * 16 + kBitmapSlack) : 0, kBufWord3);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) x[i] = __builtin_amdgcn_raw_buffer_load_b96(vs, voff[i] & ~3u, 0, 0);
+    for (int g = 0; g < 8; ++g) x[g] = __builtin_amdgcn_raw_buffer_load_b128(vs, (first[g] << 1) & ~3u, 0, 0);
 }
 
 // Lane masks of a tile (zero for an empty tile: the descriptor then covers nothing).
@@ -871,28 +869,53 @@ __device__ __forceinline__ u32x2 bitmap_load_masks(const uint32_t* words, uint32
     return __builtin_amdgcn_raw_buffer_load_b64(ms, lane * 8, 0, kStreamPolicy);
 }
 
-// A operand of lane `lane` for chunk g: 4 dwords, elements 8g .. 8g+7 of its mask.  voff are
-// the groups' byte offsets: v_alignbit_b32 reads bits 4:0 of voff << 3, i.e. 16 when the run
-// starts in the high half of its first dword, 0 otherwise.
-__device__ __forceinline__ u32x4 bitmap_chunk(const u32x3 (&x)[16], const uint32_t (&voff)[16], uint32_t lo,
-                                              uint32_t hi, const unsigned char* tbl, int g) {
+// A operand of lane `lane` for chunk g: 4 dwords, elements 8g .. 8g+7 of its mask, from the
+// chunk's 16-byte window w (8 halves from the run's start rounded down to even).  The low
+// group's values start at half F & 1, the high group's at o = (F & 1) + popc(low group), so
+// the high group reads dwords o/2 .. o/2 + 2 of the window.  Only a full chunk (8 values) at an
+// odd start needs a ninth half; it is the first half of the next lane's window (that lane's run
+// starts right after), moved over with a wavefront shift -- lane 63, which has no next lane,
+// reads it with a scalar load.  Every lane of the wavefront must call it (a shift from an
+// inactive lane reads 0).  v_alignbit_b32 reads bits 4:0 of its shift: 16 or 0 below.
+__device__ __forceinline__ u32x4 bitmap_chunk(const u32x4 (&x)[8], const uint32_t (&first)[8], uint32_t lo,
+                                              uint32_t hi, const unsigned char* tbl, const kconst_u32* vw,
+                                              int lane, int g) {
     const uint32_t m = g < 4 ? lo : hi;
-    u32x4 r;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const uint32_t q = (m >> (8 * (g & 3) + 4 * h)) & 0xFu;
-        const u32x2 s = *reinterpret_cast<const u32x2*>(tbl + q * 8);
-        const u32x3 v = x[2 * g + h];
-        const uint32_t sh = voff[2 * g + h] << 3;
-        const uint32_t v0 = __builtin_amdgcn_alignbit(v[1], v[0], sh);
-        const uint32_t v1 = __builtin_amdgcn_alignbit(v[2], v[1], sh);
-        r[2 * h] = __builtin_amdgcn_perm(v1, v0, s[0]);
-        r[2 * h + 1] = __builtin_amdgcn_perm(v1, v0, s[1]);
+    const uint32_t byte = (m >> (8 * (g & 3))) & 0xFFu;
+    const uint32_t q0 = byte & 0xFu, q1 = byte >> 4;
+    const u32x4 w = x[g];
+    const uint32_t F = first[g];
+    uint32_t w4 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)w[0], 0x130, 0xf, 0xf, false);  // wave_shl:1
+    // lane 63's chunk full (a wave-uniform test on its mask byte), then its start odd
+    if (((((uint32_t)__builtin_amdgcn_readlane((int)m, 63)) >> (8 * (g & 3))) & 0xFFu) == 0xFFu) {
+        const uint32_t f63 = (uint32_t)__builtin_amdgcn_readlane((int)F, 63);
+        if (f63 & 1u) {
+            const uint32_t sv = vw[(f63 + 7u) >> 1];
+            if (lane == 63) w4 = sv;
+        }
     }
+    const u32x2 s0 = *reinterpret_cast<const u32x2*>(tbl + q0 * 8);
+    const u32x2 s1 = *reinterpret_cast<const u32x2*>(tbl + q1 * 8);
+    u32x4 r;
+    const uint32_t sh0 = F << 4;
+    const uint32_t a0 = __builtin_amdgcn_alignbit(w[1], w[0], sh0);
+    const uint32_t a1 = __builtin_amdgcn_alignbit(w[2], w[1], sh0);
+    r[0] = __builtin_amdgcn_perm(a1, a0, s0[0]);
+    r[1] = __builtin_amdgcn_perm(a1, a0, s0[1]);
+    const uint32_t o = (F & 1u) + (uint32_t)__popc(q0);
+    const bool j1 = o >= 2u, j2 = o >= 4u;
+    const uint32_t y0 = j2 ? w[2] : (j1 ? w[1] : w[0]);
+    const uint32_t y1 = j2 ? w[3] : (j1 ? w[2] : w[1]);
+    const uint32_t y2 = j2 ? w4 : (j1 ? w[3] : w[2]);
+    const uint32_t sh1 = o << 4;
+    const uint32_t b0 = __builtin_amdgcn_alignbit(y1, y0, sh1);
+    const uint32_t b1 = __builtin_amdgcn_alignbit(y2, y1, sh1);
+    r[2] = __builtin_amdgcn_perm(b1, b0, s1[0]);
+    r[3] = __builtin_amdgcn_perm(b1, b0, s1[1]);
     return r;
 }
 
-// Bitmap-tile product for N <= 32 per launch: a workgroup owns one row block and its WK
+// Bitmap-tile product for N <= 64 per launch: a workgroup owns one row block and its WK
 // wavefronts split the k range; each wavefront keeps its own B tile in LDS and needs no
 // barrier until the final sum over wavefronts.  Pipeline of P stages: masks P tiles ahead,
 // values P - 1 tiles ahead (their offsets need the masks).  B is one tile ahead in one set of
@@ -929,8 +952,8 @@ __global__ __launch_bounds__(WK * 64) void spmm_bitmap_kernel(SpmmArgs a) {
     u32x2 mk[P];          // lane masks of the tile in each stage
     uint32_t fu[P];       // its first 16-byte unit
     uint32_t nu[P];       // its 16-byte units (0: empty)
-    u32x3 xv[P][16];      // its value loads
-    uint32_t vo[P][16];   // and their groups' byte offsets
+    u32x4 xv[P][8];       // its value windows, one per chunk
+    uint32_t vf[P][8];    // and the chunk runs' first values
     BWave<NPAD, VEC> bw;  // B tile of the current step's tile
     auto fetch_masks = [&](int q, int k) {
         uint32_t o0 = 0, o1 = 0;
@@ -943,8 +966,8 @@ __global__ __launch_bounds__(WK * 64) void spmm_bitmap_kernel(SpmmArgs a) {
         mk[q] = bitmap_load_masks(a.words, o0, o1 - o0, lane);
     };
     auto fetch_values = [&](int q) {
-        bitmap_group_offsets(mk[q][0], mk[q][1], vo[q]);
-        bitmap_load_values(xv[q], a.words, fu[q], nu[q], vo[q]);
+        bitmap_chunk_starts(mk[q][0], mk[q][1], vf[q]);
+        bitmap_load_values(xv[q], a.words, fu[q], nu[q], vf[q]);
     };
     bw.load(bsrc, a.B, a.N, a.K, kt0, lane, kt0 < kt1);
 #pragma unroll
@@ -968,6 +991,7 @@ __global__ __launch_bounds__(WK * 64) void spmm_bitmap_kernel(SpmmArgs a) {
             const int k = kt + q;
             const u32x2 m = mk[q];
             const uint32_t units = nu[q];
+            const kconst_u32* vw = (const kconst_u32*)(a.words) + 4 * (size_t)fu[q] + 4 * kMaskUnits;
             if (units > 0) bw.store(Bw, lane);
             bw.load(bsrc, a.B, a.N, a.K, k + 1, lane, k + 1 < kt1);
             fetch_masks(q, k + P);
@@ -984,7 +1008,7 @@ __global__ __launch_bounds__(WK * 64) void spmm_bitmap_kernel(SpmmArgs a) {
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const half8 af =
-                            __builtin_bit_cast(half8, bitmap_chunk(xv[q], vo[q], m[0], m[1], tbl, 2 * i + ks));
+                            __builtin_bit_cast(half8, bitmap_chunk(xv[q], vf[q], m[0], m[1], tbl, vw, lane, 2 * i + ks));
 #pragma unroll
                         for (int j = 0; j < NPAD / 16; ++j)
                             acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bfr[j], acc[i][j], 0, 0, 0);
@@ -1524,18 +1548,20 @@ __global__ __launch_bounds__(kThreads) void decode_bitmap_kernel(DecodeArgs a) {
     if (t >= a.T) return;
     const uint32_t o0 = a.offs[t], units = a.offs[t + 1] - o0;
     const u32x2 m = bitmap_load_masks(a.words, o0, units, lane);
-    uint32_t voff[16];
-    bitmap_group_offsets(m[0], m[1], voff);
-    u32x3 x[16];
-    bitmap_load_values(x, a.words, o0, units, voff);
+    uint32_t first[8];
+    bitmap_chunk_starts(m[0], m[1], first);
+    u32x4 x[8];
+    bitmap_load_values(x, a.words, o0, units, first);
+    const kconst_u32* vw = (const kconst_u32*)(a.words) + 4 * (size_t)o0 + 4 * kMaskUnits;
     const int bm = (int)(t / a.KT), bk = (int)(t % a.KT);
 #pragma unroll
     for (int g = 0; g < 8; ++g) {
+        // every lane expands (the wavefront shift inside reads the next lane), then stores
+        const u32x4 v = bitmap_chunk(x, first, m[0], m[1], tbl, vw, lane, g);
         const int gi = bm * kTileM + 16 * (g >> 1) + (lane & 15);
         const int gj = bk * kTileK + 32 * (g & 1) + 8 * (lane >> 4);
         if (gi >= a.M || gj >= a.K) continue;
         uint16_t* dst = a.A + (int64_t)gi * a.K + gj;
-        const u32x4 v = bitmap_chunk(x, voff, m[0], m[1], tbl, g);
         if ((a.K & 7) == 0 && gj + 8 <= a.K) {
             *reinterpret_cast<u32x4*>(dst) = v;
         } else {
@@ -1716,6 +1742,7 @@ hipError_t launch_bitmap_any(int npad, const SpmmArgs& a, int grid, hipStream_t 
     switch (npad) {
         case 16: return launch_bitmap_n<16, kBitmapWaves>(a, grid, st, occ);
         case 32: return launch_bitmap_n<32, kBitmapWaves>(a, grid, st, occ);
+        case 64: return launch_bitmap_n<64, kBitmapWaves>(a, grid, st, occ);
         default: return hipErrorInvalidValue;
     }
 }
