@@ -776,16 +776,16 @@ __global__ __launch_bounds__(kThreads) void spmm_wide_kernel(SpmmArgs a) {
 // place (v_alignbit_b32) and spreads them to the group's positions with two byte permutes
 // (v_perm_b32) whose selectors come from a 16-entry table.  In chunk-major order the lanes of
 // one load read neighbouring runs, a few cache lines per instruction.  Measured: the product
-// is bound by the number of vector memory instructions per tile more than by their bytes (8-
-// and 12-byte loads at 2-byte alignment cost about 1000 and 650 CU cycles per tile at any
-// density; one 16-byte load per chunk instead of one 12-byte load per group took 17-25 % off).
+// is bound by the number of vector memory instructions per tile more than by their bytes (one
+// 8-byte load per group at 2-byte alignment cost about 1000 CU cycles per tile at any density,
+// one dword-aligned 12-byte load per group about 650; one 16-byte load per chunk instead took
+// 17-25 % off that).
 constexpr int kMaskUnits = kTileM * 8 / 16;     // 16-byte units of a tile's masks (32)
 constexpr int kMaskBytes = kMaskUnits * 16;     // 512
 constexpr int kBitmapTableBytes = 16 * 8;       // selector table: 16 groups x 2 dwords
 constexpr int kBitmapSlack = kBitmapSlackBytes;  // readable bytes past a tile's values
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
 
 // Entry q: selectors of output dwords 0 (elements 0, 1) and 1 (elements 2, 3) of a 4-bit
 // group with mask q.  The group's values are packed at the front of an 8-byte load (value r
