@@ -782,29 +782,34 @@ __global__ __launch_bounds__(kThreads) void spmm_wide_kernel(SpmmArgs a) {
 // 17-25 % off that).
 constexpr int kMaskUnits = kTileM * 8 / 16;     // 16-byte units of a tile's masks (32)
 constexpr int kMaskBytes = kMaskUnits * 16;     // 512
-constexpr int kBitmapTableBytes = 16 * 8;       // selector table: 16 groups x 2 dwords
+constexpr int kBitmapTableBytes = 256 * 16;    // selector table: 256 chunk masks x 4 dwords
 constexpr int kBitmapSlack = kBitmapSlackBytes;  // readable bytes past a tile's values
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-// Entry q: selectors of output dwords 0 (elements 0, 1) and 1 (elements 2, 3) of a 4-bit
-// group with mask q.  The group's values are packed at the front of an 8-byte load (value r
-// in bytes 2r, 2r+1); element e takes value popc(q & ((1 << e) - 1)) when bit e is set, the
-// constant zero byte (selector 12) otherwise.
-__device__ __forceinline__ void bitmap_table(unsigned char* tbl, int lane) {
-    if (lane < 16) {
-        uint32_t sel[2] = {0u, 0u};
-        uint32_t r = 0;
+// Entry b (a chunk's 8 mask bits): v_perm_b32 selectors of the chunk's output dwords 0..3
+// (elements 0-1, 2-3 of the low 4-bit group, then of the high group).  A group's values sit
+// packed at the front of its 8 aligned bytes (value r in bytes 2r, 2r+1); element e of group q
+// takes value popc(q & ((1 << e) - 1)) when bit e is set, the constant zero byte (selector 12)
+// otherwise.  Built by the workgroup's first 256 threads, one entry each.
+__device__ __forceinline__ void bitmap_table(unsigned char* tbl, int tid) {
+    if (tid < 256) {
+        uint32_t sel[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            uint32_t s = 0x0C0Cu;
-            if ((lane >> e) & 1) {
-                s = (2u * r) | ((2u * r + 1u) << 8);
-                ++r;
+        for (int h = 0; h < 2; ++h) {
+            const uint32_t q = ((uint32_t)tid >> (4 * h)) & 0xFu;
+            uint32_t r = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                uint32_t v = 0x0C0Cu;
+                if ((q >> e) & 1u) {
+                    v = (2u * r) | ((2u * r + 1u) << 8);
+                    ++r;
+                }
+                sel[2 * h + (e >> 1)] |= v << (16 * (e & 1));
             }
-            sel[e >> 1] |= s << (16 * (e & 1));
         }
-        *reinterpret_cast<u32x2*>(tbl + lane * 8) = u32x2{sel[0], sel[1]};
+        *reinterpret_cast<u32x4*>(tbl + tid * 16) = u32x4{sel[0], sel[1], sel[2], sel[3]};
     }
 }
 
@@ -820,7 +825,8 @@ __device__ __forceinline__ uint32_t wave_scan(uint32_t x) {
     return x;
 }
 
-// Value index (from the tile's first value) where each of the lane's 8 chunk runs starts.
+// Value index (from the tile's first value) where each of the lane's 8 chunk runs starts,
+// times 16 (the form v_alignbit_b32 takes as a shift: bits 4:0 are 16 for an odd start).
 // Chunk counts are packed 10 bits a field, three fields a word, so three wavefront scans give
 // every chunk's lane prefix; the chunk totals (lane 63's inclusive sums) are wave-uniform.
 __device__ __forceinline__ void bitmap_chunk_starts(uint32_t lo, uint32_t hi, uint32_t (&first)[8]) {
@@ -843,7 +849,7 @@ __device__ __forceinline__ void bitmap_chunk_starts(uint32_t lo, uint32_t hi, ui
 #pragma unroll
     for (int g = 0; g < 8; ++g) {
         const int w = g / 3, f = 10 * (g % 3);
-        first[g] = base + ((e[w] >> f) & 0x3FFu);
+        first[g] = (base + ((e[w] >> f) & 0x3FFu)) << 4;
         base += (t[w] >> f) & 0x3FFu;
     }
 }
@@ -858,7 +864,7 @@ __device__ __forceinline__ void bitmap_load_values(u32x4 (&x)[8], const uint32_t
         (void*)(words + 4 * (size_t)first_unit + 4 * kMaskUnits), (short)0,
         units > (uint32_t)kMaskUnits ? (int)((units - kMaskUnits) * 16 + kBitmapSlack) : 0, kBufWord3);
 #pragma unroll
-    for (int g = 0; g < 8; ++g) x[g] = __builtin_amdgcn_raw_buffer_load_b128(vs, (first[g] << 1) & ~3u, 0, 0);
+    for (int g = 0; g < 8; ++g) x[g] = __builtin_amdgcn_raw_buffer_load_b128(vs, (first[g] >> 3) & ~3u, 0, 0);
 }
 
 // Lane masks of a tile (zero for an empty tile: the descriptor then covers nothing).
@@ -875,34 +881,31 @@ __device__ __forceinline__ u32x2 bitmap_load_masks(const uint32_t* words, uint32
 // the high group reads dwords o/2 .. o/2 + 2 of the window.  Only a full chunk (8 values) at an
 // odd start needs a ninth half; it is the first half of the next lane's window (that lane's run
 // starts right after), moved over with a wavefront shift -- lane 63, which has no next lane,
-// reads it with a scalar load.  Every lane of the wavefront must call it (a shift from an
-// inactive lane reads 0).  v_alignbit_b32 reads bits 4:0 of its shift: 16 or 0 below.
+// reads it with a scalar load (m63: lane 63's mask word of this chunk).  Every lane of the
+// wavefront must call it (a shift from an inactive lane reads nothing useful).  first[] holds
+// F << 4: v_alignbit_b32 reads bits 4:0 of its shift, 16 for an odd start.
 __device__ __forceinline__ u32x4 bitmap_chunk(const u32x4 (&x)[8], const uint32_t (&first)[8], uint32_t lo,
-                                              uint32_t hi, const unsigned char* tbl, const kconst_u32* vw,
-                                              int lane, int g) {
+                                              uint32_t hi, uint32_t m63, const unsigned char* tbl,
+                                              const kconst_u32* vw, int lane, int g) {
     const uint32_t m = g < 4 ? lo : hi;
-    const uint32_t byte = (m >> (8 * (g & 3))) & 0xFFu;
-    const uint32_t q0 = byte & 0xFu, q1 = byte >> 4;
+    const int bit = 8 * (g & 3);
     const u32x4 w = x[g];
-    const uint32_t F = first[g];
-    uint32_t w4 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)w[0], 0x130, 0xf, 0xf, false);  // wave_shl:1
-    // lane 63's chunk full (a wave-uniform test on its mask byte), then its start odd
-    if (((((uint32_t)__builtin_amdgcn_readlane((int)m, 63)) >> (8 * (g & 3))) & 0xFFu) == 0xFFu) {
-        const uint32_t f63 = (uint32_t)__builtin_amdgcn_readlane((int)F, 63);
+    const uint32_t F16 = first[g];
+    uint32_t w4 = (uint32_t)__builtin_amdgcn_mov_dpp((int)w[0], 0x130, 0xf, 0xf, false);  // wave_shl:1
+    if (((m63 >> bit) & 0xFFu) == 0xFFu) {  // lane 63's chunk is full
+        const uint32_t f63 = (uint32_t)__builtin_amdgcn_readlane((int)F16, 63) >> 4;
         if (f63 & 1u) {
             const uint32_t sv = vw[(f63 + 7u) >> 1];
             if (lane == 63) w4 = sv;
         }
     }
-    const u32x2 s0 = *reinterpret_cast<const u32x2*>(tbl + q0 * 8);
-    const u32x2 s1 = *reinterpret_cast<const u32x2*>(tbl + q1 * 8);
+    const u32x4 sel = *reinterpret_cast<const u32x4*>(tbl + (((m >> bit) & 0xFFu) << 4));
     u32x4 r;
-    const uint32_t sh0 = F << 4;
-    const uint32_t a0 = __builtin_amdgcn_alignbit(w[1], w[0], sh0);
-    const uint32_t a1 = __builtin_amdgcn_alignbit(w[2], w[1], sh0);
-    r[0] = __builtin_amdgcn_perm(a1, a0, s0[0]);
-    r[1] = __builtin_amdgcn_perm(a1, a0, s0[1]);
-    const uint32_t o = (F & 1u) + (uint32_t)__popc(q0);
+    const uint32_t a0 = __builtin_amdgcn_alignbit(w[1], w[0], F16);
+    const uint32_t a1 = __builtin_amdgcn_alignbit(w[2], w[1], F16);
+    r[0] = __builtin_amdgcn_perm(a1, a0, sel[0]);
+    r[1] = __builtin_amdgcn_perm(a1, a0, sel[1]);
+    const uint32_t o = ((F16 >> 4) & 1u) + (uint32_t)__popc((m >> bit) & 0xFu);
     const bool j1 = o >= 2u, j2 = o >= 4u;
     const uint32_t y0 = j2 ? w[2] : (j1 ? w[1] : w[0]);
     const uint32_t y1 = j2 ? w[3] : (j1 ? w[2] : w[1]);
@@ -910,8 +913,8 @@ __device__ __forceinline__ u32x4 bitmap_chunk(const u32x4 (&x)[8], const uint32_
     const uint32_t sh1 = o << 4;
     const uint32_t b0 = __builtin_amdgcn_alignbit(y1, y0, sh1);
     const uint32_t b1 = __builtin_amdgcn_alignbit(y2, y1, sh1);
-    r[2] = __builtin_amdgcn_perm(b1, b0, s1[0]);
-    r[3] = __builtin_amdgcn_perm(b1, b0, s1[1]);
+    r[2] = __builtin_amdgcn_perm(b1, b0, sel[2]);
+    r[3] = __builtin_amdgcn_perm(b1, b0, sel[3]);
     return r;
 }
 
@@ -925,6 +928,7 @@ __global__ __launch_bounds__(WK * 64) void spmm_bitmap_kernel(SpmmArgs a) {
     constexpr int kBBytes = NPAD * kRowBytes;
     constexpr int kRedBytes = NPAD * kTileM * 4;
     constexpr int kWaveBytes = kBBytes > kRedBytes ? kBBytes : kRedBytes;
+    static_assert(WK * 64 >= 256, "the workgroup builds the 256-entry selector table");
     __shared__ __attribute__((aligned(16))) unsigned char smem[kBitmapTableBytes + WK * kWaveBytes];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -936,7 +940,7 @@ __global__ __launch_bounds__(WK * 64) void spmm_bitmap_kernel(SpmmArgs a) {
     unsigned char* tbl = smem;
     unsigned char* area = smem + kBitmapTableBytes;
     unsigned char* Bw = area + wave * kWaveBytes;
-    if (wave == 0) bitmap_table(tbl, lane);
+    bitmap_table(tbl, tid);
     __syncthreads();
 
     const int s = item / a.G;
@@ -997,6 +1001,8 @@ __global__ __launch_bounds__(WK * 64) void spmm_bitmap_kernel(SpmmArgs a) {
             fetch_masks(q, k + P);
             fetch_values((q + P - 1) % P);  // tile k + P - 1
             if (units > 0) {
+                const uint32_t m63lo = (uint32_t)__builtin_amdgcn_readlane((int)m[0], 63);
+                const uint32_t m63hi = (uint32_t)__builtin_amdgcn_readlane((int)m[1], 63);
                 // chunk g = 2i + ks, expanded right before its MFMAs (k step outer, so that
                 // consecutive MFMAs write different accumulators)
 #pragma unroll
@@ -1008,7 +1014,7 @@ __global__ __launch_bounds__(WK * 64) void spmm_bitmap_kernel(SpmmArgs a) {
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const half8 af =
-                            __builtin_bit_cast(half8, bitmap_chunk(xv[q], vf[q], m[0], m[1], tbl, vw, lane, 2 * i + ks));
+                            __builtin_bit_cast(half8, bitmap_chunk(xv[q], vf[q], m[0], m[1], (2 * i + ks) < 4 ? m63lo : m63hi, tbl, vw, lane, 2 * i + ks));
 #pragma unroll
                         for (int j = 0; j < NPAD / 16; ++j)
                             acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bfr[j], acc[i][j], 0, 0, 0);
@@ -1542,7 +1548,7 @@ __global__ __launch_bounds__(kThreads) void decode_bitmap_kernel(DecodeArgs a) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    if (wave == 0) bitmap_table(tbl, lane);
+    bitmap_table(tbl, tid);
     __syncthreads();
     const int64_t t = (int64_t)blockIdx.x * kWaves + wave;
     if (t >= a.T) return;
@@ -1553,11 +1559,13 @@ __global__ __launch_bounds__(kThreads) void decode_bitmap_kernel(DecodeArgs a) {
     u32x4 x[8];
     bitmap_load_values(x, a.words, o0, units, first);
     const kconst_u32* vw = (const kconst_u32*)(a.words) + 4 * (size_t)o0 + 4 * kMaskUnits;
+    const uint32_t m63lo = (uint32_t)__builtin_amdgcn_readlane((int)m[0], 63);
+    const uint32_t m63hi = (uint32_t)__builtin_amdgcn_readlane((int)m[1], 63);
     const int bm = (int)(t / a.KT), bk = (int)(t % a.KT);
 #pragma unroll
     for (int g = 0; g < 8; ++g) {
         // every lane expands (the wavefront shift inside reads the next lane), then stores
-        const u32x4 v = bitmap_chunk(x, first, m[0], m[1], tbl, vw, lane, g);
+        const u32x4 v = bitmap_chunk(x, first, m[0], m[1], g < 4 ? m63lo : m63hi, tbl, vw, lane, g);
         const int gi = bm * kTileM + 16 * (g >> 1) + (lane & 15);
         const int gj = bk * kTileK + 32 * (g & 1) + 8 * (lane >> 4);
         if (gi >= a.M || gj >= a.K) continue;
