@@ -68,6 +68,27 @@ int plan_splits(const Grid& g, int cus, int blocks_per_cu, int64_t groups, int t
     return (int)S;
 }
 
+// K splits of the bitmap kernel: the load of the busiest CU, ceil(G*S / cus) / S row-block
+// ranges, times the start-up of each wavefront's pipeline (about 4 tiles against its KT / (S
+// * waves) tiles).  This picks the measured best of 1, 2 and 4 splits on the OPT shapes: 1 for
+// OPT-30B MLP1, OPT-66B QKV and OPT-175B MLP1; 2 for OPT-175B QKV; 4 for OutProj and MLP2.
+int plan_splits_bitmap(const Grid& g, int cus, int waves) {
+    if (const char* e = getenv("LSCD_SPLITK"); e && atoll(e) > 0)
+        return (int)std::max<int64_t>(1, std::min<int64_t>(atoll(e), g.KT));
+    const int64_t smax = std::max<int64_t>(1, std::min<int64_t>(g.KT / waves, 8));
+    int64_t S = 1;
+    double best = 0;
+    for (int64_t s = 1; s <= smax; ++s) {
+        const double load = (double)((g.MB * s + cus - 1) / cus) / (double)s;
+        const double cost = load * (1.0 + 4.0 * (double)(s * waves) / (double)g.KT);
+        if (s == 1 || cost < best) {
+            best = cost;
+            S = s;
+        }
+    }
+    return (int)S;
+}
+
 // Tile shapes with product kernels: 64 columns, 64 / 80 / 96 / 112 / 128 rows.
 bool kernel_shape(const Grid& g) {
     return g.tk == lscd::kTileK && (g.tm == 64 || g.tm == 80 || g.tm == 96 || g.tm == 112 || g.tm == 128);
@@ -155,8 +176,7 @@ lscd_status_t new_handle(const Grid& g, int64_t nnz, int64_t nwords, int32_t max
         for (int i = 0; i < 3 && kernel_tile; ++i) {
             const int npad = 16 << i;
             h->kind[i] = kKernelBitmap;
-            const int occ = spmm_blocks_per_cu(kKernelBitmap, npad, 0, (int)std::min<int64_t>(g.K, 1 << 30));
-            h->S[i] = plan_splits(g, h->cus, occ, g.MB, 4 * kBitmapWaves, false);  // fill the resident slots
+            h->S[i] = plan_splits_bitmap(g, h->cus, kBitmapWaves);
             if (h->S[i] > 1) part = std::max<int64_t>(part, (int64_t)h->S[i] * g.M * npad * 4);
         }
     }
