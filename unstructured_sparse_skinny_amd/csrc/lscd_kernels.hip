@@ -774,12 +774,12 @@ __global__ __launch_bounds__(kThreads) void spmm_wide_kernel(SpmmArgs a) {
 // stream (a prefix over the wavefront of its chunk counts, plus the chunk totals before it),
 // fetches each run with one dword-aligned 16-byte load, shifts each 4-bit group's values into
 // place (v_alignbit_b32) and spreads them to the group's positions with two byte permutes
-// (v_perm_b32) whose selectors come from a 16-entry table.  In chunk-major order the lanes of
-// one load read neighbouring runs, a few cache lines per instruction.  Measured: the product
-// is bound by the number of vector memory instructions per tile more than by their bytes (one
-// 8-byte load per group at 2-byte alignment cost about 1000 CU cycles per tile at any density,
-// one dword-aligned 12-byte load per group about 650; one 16-byte load per chunk instead took
-// 17-25 % off that).
+// (v_perm_b32) whose selectors come from a 256-entry table indexed by the chunk's mask byte.
+// In chunk-major order the lanes of one load read neighbouring runs, a few cache lines per
+// instruction.  Measured: the product is bound by the number of vector memory instructions
+// per tile more than by their bytes (one 8-byte load per group at 2-byte alignment cost about
+// 1000 CU cycles per tile at any density, one dword-aligned 12-byte load per group about 650;
+// one 16-byte load per chunk instead took 17-25 % off that), then by VALU issue.
 constexpr int kMaskUnits = kTileM * 8 / 16;     // 16-byte units of a tile's masks (32)
 constexpr int kMaskBytes = kMaskUnits * 16;     // 512
 constexpr int kBitmapTableBytes = 256 * 16;    // selector table: 256 chunk masks x 4 dwords
