@@ -772,10 +772,9 @@ __global__ __launch_bounds__(kThreads) void spmm_wide_kernel(SpmmArgs a) {
 //
 // Decoding needs no LDS tile: a lane finds where each of its 8 chunk runs starts in the value
 // stream (a prefix over the wavefront of its chunk counts, plus the chunk totals before it),
-// fetches each run with one dword-aligned 16-byte load, aligns the window to the run's start
-// (v_alignbit_b32) and spreads each 4-bit group's values to its positions with byte permutes
-// (v_perm_b32, two ORed per high-group dword) whose selectors come from a 256-entry table
-// indexed by the chunk's mask byte.
+// fetches each run with one dword-aligned 16-byte load, shifts each 4-bit group's values into
+// place (v_alignbit_b32) and spreads them to the group's positions with two byte permutes
+// (v_perm_b32) whose selectors come from a 256-entry table indexed by the chunk's mask byte.
 // In chunk-major order the lanes of one load read neighbouring runs, a few cache lines per
 // instruction.  Measured: the product is bound by the number of vector memory instructions
 // per tile more than by their bytes (one 8-byte load per group at 2-byte alignment cost about
@@ -783,49 +782,34 @@ __global__ __launch_bounds__(kThreads) void spmm_wide_kernel(SpmmArgs a) {
 // one 16-byte load per chunk instead took 17-25 % off that), then by VALU issue.
 constexpr int kMaskUnits = kTileM * 8 / 16;     // 16-byte units of a tile's masks (32)
 constexpr int kMaskBytes = kMaskUnits * 16;     // 512
-constexpr int kBitmapTableBytes = 256 * 32;    // selector table: 256 chunk masks x 8 dwords
+constexpr int kBitmapTableBytes = 256 * 16;    // selector table: 256 chunk masks x 4 dwords
 constexpr int kBitmapSlack = kBitmapSlackBytes;  // readable bytes past a tile's values
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-// Entry b (a chunk's 8 mask bits, low group q0 = b & 15, high group q1 = b >> 4): v_perm_b32
-// selectors that build the chunk's 4 output dwords from its values, which sit packed in the
-// halves 0..7 of the aligned window A0..A3 (value r at half r).  Output dwords 0 and 1 (low
-// group) read (A1, A0): element e takes half popc(q0 & ((1 << e) - 1)).  Output dwords 2 and 3
-// (high group) take half popc(q0) + popc(q1 & ((1 << e) - 1)), anywhere in 0..7: each is the OR
-// of a select from (A1, A0) and one from (A3, A2).  An unset element, or a half outside the
-// pair, selects the constant zero byte (selector 12).  Dwords: low 0, low 1, high 0 from A0-A1,
-// high 0 from A2-A3, high 1 from A0-A1, high 1 from A2-A3, then two unused.  Built by the
-// workgroup's first 256 threads, one entry each.
+// Entry b (a chunk's 8 mask bits): v_perm_b32 selectors of the chunk's output dwords 0..3
+// (elements 0-1, 2-3 of the low 4-bit group, then of the high group).  A group's values sit
+// packed at the front of its 8 aligned bytes (value r in bytes 2r, 2r+1); element e of group q
+// takes value popc(q & ((1 << e) - 1)) when bit e is set, the constant zero byte (selector 12)
+// otherwise.  Built by the workgroup's first 256 threads, one entry each.
 __device__ __forceinline__ void bitmap_table(unsigned char* tbl, int tid) {
     if (tid < 256) {
-        const uint32_t q0 = (uint32_t)tid & 0xFu, q1 = ((uint32_t)tid >> 4) & 0xFu;
-        uint32_t sel[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
-        uint32_t r = 0;
+        uint32_t sel[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {  // low group
-            uint32_t v = 0x0C0Cu;
-            if ((q0 >> e) & 1u) {
-                v = (2u * r) | ((2u * r + 1u) << 8);
-                ++r;
-            }
-            sel[e >> 1] |= v << (16 * (e & 1));
-        }
+        for (int h = 0; h < 2; ++h) {
+            const uint32_t q = ((uint32_t)tid >> (4 * h)) & 0xFu;
+            uint32_t r = 0;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {  // high group: half r continues after the low group's
-            uint32_t lo = 0x0C0Cu, hi = 0x0C0Cu;
-            if ((q1 >> e) & 1u) {
-                if (r < 4u)
-                    lo = (2u * r) | ((2u * r + 1u) << 8);
-                else
-                    hi = (2u * (r - 4u)) | ((2u * (r - 4u) + 1u) << 8);
-                ++r;
+            for (int e = 0; e < 4; ++e) {
+                uint32_t v = 0x0C0Cu;
+                if ((q >> e) & 1u) {
+                    v = (2u * r) | ((2u * r + 1u) << 8);
+                    ++r;
+                }
+                sel[2 * h + (e >> 1)] |= v << (16 * (e & 1));
             }
-            sel[2 + 2 * (e >> 1)] |= lo << (16 * (e & 1));
-            sel[3 + 2 * (e >> 1)] |= hi << (16 * (e & 1));
         }
-        *reinterpret_cast<u32x4*>(tbl + tid * 32) = u32x4{sel[0], sel[1], sel[2], sel[3]};
-        *reinterpret_cast<u32x4*>(tbl + tid * 32 + 16) = u32x4{sel[4], sel[5], sel[6], sel[7]};
+        *reinterpret_cast<u32x4*>(tbl + tid * 16) = u32x4{sel[0], sel[1], sel[2], sel[3]};
     }
 }
 
@@ -892,15 +876,14 @@ __device__ __forceinline__ u32x2 bitmap_load_masks(const uint32_t* words, uint32
 }
 
 // A operand of lane `lane` for chunk g: 4 dwords, elements 8g .. 8g+7 of its mask, from the
-// chunk's 16-byte window w (8 halves from the run's start rounded down to even).  Shifted by
-// one half when the run starts at an odd value (F & 1), the window holds the chunk's values at
-// halves 0..7 (A0..A3), and the selector table places both groups.  Only a full chunk (8
-// values) at an odd start needs a ninth window half; it is the first half of the next lane's
-// window (that lane's run starts right after), moved over with a wavefront shift -- lane 63,
-// which has no next lane, reads it with a scalar load (m63: lane 63's mask word of this
-// chunk).  Every lane of the wavefront must call it (a shift from an inactive lane reads
-// nothing useful).  first[] holds F << 4: v_alignbit_b32 reads bits 4:0 of its shift, 16 for
-// an odd start.
+// chunk's 16-byte window w (8 halves from the run's start rounded down to even).  The low
+// group's values start at half F & 1, the high group's at o = (F & 1) + popc(low group), so
+// the high group reads dwords o/2 .. o/2 + 2 of the window.  Only a full chunk (8 values) at an
+// odd start needs a ninth half; it is the first half of the next lane's window (that lane's run
+// starts right after), moved over with a wavefront shift -- lane 63, which has no next lane,
+// reads it with a scalar load (m63: lane 63's mask word of this chunk).  Every lane of the
+// wavefront must call it (a shift from an inactive lane reads nothing useful).  first[] holds
+// F << 4: v_alignbit_b32 reads bits 4:0 of its shift, 16 for an odd start.
 __device__ __forceinline__ u32x4 bitmap_chunk(const u32x4 (&x)[8], const uint32_t (&first)[8], uint32_t lo,
                                               uint32_t hi, uint32_t m63, const unsigned char* tbl,
                                               const kconst_u32* vw, int lane, int g) {
@@ -916,18 +899,22 @@ __device__ __forceinline__ u32x4 bitmap_chunk(const u32x4 (&x)[8], const uint32_
             if (lane == 63) w4 = sv;
         }
     }
-    const unsigned char* e = tbl + (((m >> bit) & 0xFFu) << 5);
-    const u32x4 s0 = *reinterpret_cast<const u32x4*>(e);
-    const u32x2 s1 = *reinterpret_cast<const u32x2*>(e + 16);
+    const u32x4 sel = *reinterpret_cast<const u32x4*>(tbl + (((m >> bit) & 0xFFu) << 4));
+    u32x4 r;
     const uint32_t a0 = __builtin_amdgcn_alignbit(w[1], w[0], F16);
     const uint32_t a1 = __builtin_amdgcn_alignbit(w[2], w[1], F16);
-    const uint32_t a2 = __builtin_amdgcn_alignbit(w[3], w[2], F16);
-    const uint32_t a3 = __builtin_amdgcn_alignbit(w4, w[3], F16);
-    u32x4 r;
-    r[0] = __builtin_amdgcn_perm(a1, a0, s0[0]);
-    r[1] = __builtin_amdgcn_perm(a1, a0, s0[1]);
-    r[2] = __builtin_amdgcn_perm(a1, a0, s0[2]) | __builtin_amdgcn_perm(a3, a2, s0[3]);
-    r[3] = __builtin_amdgcn_perm(a1, a0, s1[0]) | __builtin_amdgcn_perm(a3, a2, s1[1]);
+    r[0] = __builtin_amdgcn_perm(a1, a0, sel[0]);
+    r[1] = __builtin_amdgcn_perm(a1, a0, sel[1]);
+    const uint32_t o = ((F16 >> 4) & 1u) + (uint32_t)__popc((m >> bit) & 0xFu);
+    const bool j1 = o >= 2u, j2 = o >= 4u;
+    const uint32_t y0 = j2 ? w[2] : (j1 ? w[1] : w[0]);
+    const uint32_t y1 = j2 ? w[3] : (j1 ? w[2] : w[1]);
+    const uint32_t y2 = j2 ? w4 : (j1 ? w[3] : w[2]);
+    const uint32_t sh1 = o << 4;
+    const uint32_t b0 = __builtin_amdgcn_alignbit(y1, y0, sh1);
+    const uint32_t b1 = __builtin_amdgcn_alignbit(y2, y1, sh1);
+    r[2] = __builtin_amdgcn_perm(b1, b0, sel[2]);
+    r[3] = __builtin_amdgcn_perm(b1, b0, sel[3]);
     return r;
 }
 
@@ -1754,7 +1741,7 @@ hipError_t launch_spmm_n(int kind, int R, const SpmmArgs& a, int grid, hipStream
 
 template <int NPAD, int WK>
 hipError_t launch_bitmap_n(const SpmmArgs& a, int grid, hipStream_t st, int* occ) {
-    constexpr int P = 2;  // three stages measured slower (fewer resident wavefronts)
+    constexpr int P = 2;  // three stages measured no faster
     if ((a.K & 7) != 0) return run(spmm_bitmap_kernel<NPAD, WK, P, false>, a, grid, st, occ, WK * 64);
     return run(spmm_bitmap_kernel<NPAD, WK, P, true>, a, grid, st, occ, WK * 64);
 }
