@@ -82,7 +82,7 @@ def test_bitmap_gaussian_within_tolerance(M, K, keep, N):
     assert_gates(run(h, case.B16, M), osp.spmm_f64(case.A16, case.mask, case.B16), f"M={M} K={K} N={N}")
 
 
-@pytest.mark.parametrize("cfg,shape", [(2, 0), (5, 1), (5, 0)])
+@pytest.mark.parametrize("cfg,shape", [(2, 0), (5, 1), (5, 0), (4, 0)])
 def test_bitmap_full_size_sampled_rows(cfg, shape):
     case = syn.make_config(cfg, shape)
     say(f"bitmap full {case.name}")
