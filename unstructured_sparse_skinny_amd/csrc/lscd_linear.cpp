@@ -114,6 +114,24 @@ lscd_status_t on_device(const lscd_handle_s* h) {
     return dev == h->device ? LSCD_SUCCESS : LSCD_ERROR_INVALID_VALUE;
 }
 
+// Sparse time of the handle's product: the model's for Tiled-CSL; bitmap and three-level
+// handles run one skinny launch per 64 columns (each reading the whole blob), costed launch
+// by launch.
+double sparse_time(const lscd_handle_s* h, int32_t N) {
+    double ts = 0, td = 0;
+    if (h->format == 0) {
+        model(h->g.M, h->g.K, h->nnz_padded, h->g.T, N, &ts, &td);
+        return ts;
+    }
+    const int32_t per = h->format == 1 ? lscd::kBitmapMaxN : lscd::kThreeLevelMaxN;
+    double sum = 0;
+    for (int32_t c0 = 0; c0 < N; c0 += per) {
+        model(h->g.M, h->g.K, h->nnz_padded, h->g.T, std::min(N - c0, per), &ts, &td);
+        sum += ts;
+    }
+    return sum;
+}
+
 // Dense iff the dense time is lower: the time lscd_tune_dense measured for this N when there
 // is one, the cost model's otherwise; the sparse time is always the model's.
 bool use_dense(const lscd_handle_s* h, int32_t N) {
@@ -121,6 +139,7 @@ bool use_dense(const lscd_handle_s* h, int32_t N) {
     if (h->crossover >= 0) return N > h->crossover;
     double ts, td;
     model(h->g.M, h->g.K, h->nnz_padded, h->g.T, N, &ts, &td);
+    ts = sparse_time(h, N);
     if (const LtState* lt = (const LtState*)h->lt)
         for (const auto& t : lt->tuned)
             if (t.N == N) td = t.us;
