@@ -301,10 +301,11 @@ lscd_status_t lscd_tune_dense(lscd_handle_t h, const void* B, void* C, int32_t N
 /* lscd_linear_path -- the path lscd_linear takes for N: *path = 0 sparse, 1 dense (dense
  * only with a dense copy attached): dense iff its time is below the sparse product's, taking
  * the time lscd_tune_dense measured for this N when there is one and lscd_linear_model's
- * prediction otherwise.  The sparse time is lscd_linear_model's for a Tiled-CSL handle; a
- * bitmap or three-level handle runs one launch per 64 columns, so its sparse time is the sum
- * of lscd_linear_model's times for those launches (N = 64 each, then the remainder), with the
- * handle's nnz_padded and num_tiles.  No device work. */
+ * prediction otherwise.  The sparse time is lscd_linear_model's for a Tiled-CSL handle.  A
+ * bitmap or three-level handle runs one launch per 64 columns whose kernels cost about the
+ * same per tile at any density: its sparse time is a fixed part plus a time per tile for each
+ * launch (bitmap about 0.9, 1.0 and 1.2 ns per tile for N padded to 16, 32 and 64;
+ * three-level 1.0, 1.2 and 1.5).  No device work. */
 lscd_status_t lscd_linear_path(lscd_handle_t h, int32_t N, int32_t* path);
 
 /* lscd_set_linear_crossover -- fix the choice: sparse iff N <= n_max_sparse; -1 returns
