@@ -174,13 +174,20 @@ def sweep_n(args, case, L, torch, np):
     choice, and the library's dense path with hipBLASLt tuned for N) and lscd_linear's own
     choice on the attached dense copy, for every N of --sweep-n."""
     M, K = case.M, case.K
-    tm = L.lscd_default_tile_m(M, K)
-    words, offs = L.lscd_pack(case.A16, case.mask, tm, 64)
-    h0 = L.lscd_import(words, offs, M, K, tm, 64)
-    info = h0.info
-    copies = max(1, min(8, math.ceil(3 * MALL_BYTES / info["format_bytes"])))
-    hs = [h0] + [L.lscd_import(words, offs, M, K, tm, 64) for _ in range(copies - 1)]
-    del words, offs
+    if args.format == "tiled-csl":
+        tm = L.lscd_default_tile_m(M, K)
+        words, offs = L.lscd_pack(case.A16, case.mask, tm, 64)
+        h0 = L.lscd_import(words, offs, M, K, tm, 64)
+        info = h0.info
+        copies = max(1, min(8, math.ceil(3 * MALL_BYTES / info["format_bytes"])))
+        hs = [h0] + [L.lscd_import(words, offs, M, K, tm, 64) for _ in range(copies - 1)]
+        del words, offs
+    else:
+        enc = L.lscd_encode_bitmap if args.format == "bitmap" else L.lscd_encode_three_level
+        h0 = enc(case.A16, case.mask)
+        info = h0.info
+        copies = max(1, min(8, math.ceil(3 * MALL_BYTES / info["format_bytes"])))
+        hs = [h0] + [enc(case.A16, case.mask) for _ in range(copies - 1)]
     Ad = torch.from_numpy(np.where(case.mask.astype(bool), case.A16, 0).astype(np.uint16).view(np.float16))
     dcopies = max(1, min(4, math.ceil(3 * MALL_BYTES / (2 * M * K))))
     Ads = [Ad.to("cuda") for _ in range(dcopies)]
@@ -200,14 +207,16 @@ def sweep_n(args, case, L, torch, np):
         L.lscd_set_linear_crossover(h0, -1)
         _, tl, *_ = time_calls([(L.lscd_linear, (h0, B, C))], args.steps, args.warmup, torch, graph=False)
         ms, md = L.lscd_linear_model(M, K, info["nnz_padded"], info["num_tiles"], N)
+        if args.format != "tiled-csl":
+            ms = None  # the variant formats are costed per tile, not by this model
         if ts < min(td, tt):
             last_sparse_win = N
-        print(json.dumps({"sweep": "n", "workload": case.name, "M": M, "K": K, "N": N,
+        print(json.dumps({"sweep": "n", "workload": case.name, "format": args.format, "M": M, "K": K, "N": N,
                           "sparsity": round(case.sparsity, 4), "sparse_us": round(ts * 1e3, 1),
                           "dense_hipblaslt_us": round(td * 1e3, 1), "dense_tuned_us": round(tt * 1e3, 1),
                           "tune_us": round(tune_us, 1), "linear_us": round(tl * 1e3, 1),
                           "linear_path": ["sparse", "dense"][L.lscd_linear_path(h0, N)],
-                          "model_sparse_us": round(ms, 1), "model_dense_us": round(md, 1),
+                          "model_sparse_us": None if ms is None else round(ms, 1), "model_dense_us": round(md, 1),
                           "sparse_tflops": round(2 * M * N * K / (ts * 1e-3) / 1e12, 1)}), flush=True)
     print(json.dumps({"sweep": "n", "workload": case.name, "largest_n_sparse_wins": last_sparse_win}), flush=True)
 
