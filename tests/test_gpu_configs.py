@@ -81,3 +81,25 @@ def test_full_size_decode_cfg2():
     got = A.cpu().numpy().view(np.uint16)
     assert np.array_equal(got, tc.masked(case.A16, case.mask))
     assert h.info["nnz"] == int(case.mask.sum())
+
+
+@pytest.mark.parametrize("sparsity", [0.5, 0.6])
+def test_full_size_cfg2_shape_dense_tiles_n64(sparsity):
+    """OPT-30B MLP1 shape at 50-60 % sparsity, N = 16 and 64: 112-row tiles of 2900-3600
+    words, past the 12-vector register stage at 50 % (the rest is loaded inside the scatter);
+    integer-valued inputs, sampled rows bit-exact against fp16_rne of the oracle."""
+    case = syn.make_config(2, sparsity=sparsity)
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([977, int(sparsity * 100)])))
+    A16 = syn.int_fp16(rng, case.M, case.K)
+    say(f"int {case.name} sparsity={sparsity}")
+    h = L.lscd_encode(A16, case.mask)
+    assert h.info["tile_m"] == 112
+    if sparsity == 0.5:
+        assert h.info["max_tile_words"] > 12 * 64 * 4
+    rows = _rows(case.M, seed=2)
+    for N in (16, 64):
+        B16 = syn.int_fp16(rng, N, case.K)
+        C = _run(h, B16, case.M)
+        C64 = osp.spmm_f64(A16, case.mask, B16, rows=rows)
+        assert np.abs(C64).max() < 65504
+        assert np.array_equal(C[:, rows], osp.fp16_rne(C64)), f"N={N}"
