@@ -6,7 +6,9 @@ row blocks and 256 random rows):
   * Gaussian inputs: the sampled rows pass the tolerance gates (tests/_util.py);
   * integer-valued inputs with the configuration's own mask: the sampled rows are
     bit-exact against fp16_rne of the oracle (every fp32 partial sum is an exact integer);
-  * for configuration 2 the decoded matrix (lscd_debug_decode) is compared bit for bit.
+  * for configuration 2 the decoded matrix (lscd_debug_decode) is compared bit for bit;
+  * the OPT-30B MLP1 shape at 50 and 60 % sparsity, N = 16 and 64 (dense tall tiles),
+    integer-valued and bit-exact on the sampled rows.
 """
 import numpy as np
 import pytest
