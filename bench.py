@@ -302,7 +302,11 @@ def main():
         f"max_tile_words={info['max_tile_words']}")
 
     nnz, tiles = info["nnz"], info["num_tiles"]
-    split = info["splits"][L.npad_index(N)]
+    if N <= 64:
+        split, variant_id = info["splits"][L.npad_index(N)], info["variant"][L.npad_index(N)]
+    else:  # the N > 64 kernel; the first launch's plan when N > 256 takes several
+        npw = 128 if N <= 128 else (192 if N <= 192 else 256)
+        split, variant_id = info["splits_wide"][(npw - 128) // 64], 3
     # Tiled-CSL: one 4-byte word per nonzero; bitmap and three-level tiles: the blob as stored
     stored = 4 * info["nnz_padded"] if args.format != "tiled-csl" else 4 * nnz
     alg_bytes = stored + 4 * (tiles + 1) + 2 * K * N + 2 * M * N
@@ -407,7 +411,7 @@ def main():
         "config": {"workload": case.name, "format": args.format, "M": M, "K": K, "N": N,
                    "sparsity": round(case.sparsity, 4),
                    "nnz": nnz, "tile": f"{info['tile_m']}x{info['tile_k']}", "splits": split,
-                   "variant": ["shared-B", "independent-4", "independent-8", "wide", "bitmap", "three-level"][info["variant"][L.npad_index(N)]],
+                   "variant": ["shared-B", "independent-4", "independent-8", "wide", "bitmap", "three-level"][variant_id],
                    "copies_rotated": copies, "gpu": props.name, "cus": props.multi_processor_count},
         "tflops": round(flops / (ms_step * 1e-3) / 1e12, 2),
         "pct_roofline": round(100 * value / HBM_PEAK_GBS, 1),

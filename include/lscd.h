@@ -68,7 +68,10 @@ typedef struct {
                                    16, 32 and 64 (1: no second pass)                        */
     int32_t variant[3];         /* product kernel variant for N padded to 16, 32, 64:
                                    0 shared B tile, 1 / 2 independent wavefronts (4 / 8),
-                                   4 bitmap tiles, 5 three-level tiles                      */
+                                   3 the N > 64 kernel with N padded to 128 (tiles taller
+                                   than 64 rows that overflow the shared-B register stage;
+                                   splits[2] then equals splits_wide[0]), 4 bitmap tiles,
+                                   5 three-level tiles                                      */
     int32_t splits_wide[3];     /* K-splits for N > 64, per launch of N padded to 128, 192,
                                    256 (N > 256 runs one launch per 256 columns)            */
     int32_t reg_vectors_wide;   /* 128-bit staging registers per thread, N > 64 kernel      */

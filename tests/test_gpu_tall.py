@@ -108,3 +108,34 @@ def test_tall_device_encoder_matches_host():
         words, offs = L.lscd_export(h)
         pw, po = L.lscd_pack(case.A16, case.mask, tm, 64)
         assert np.array_equal(offs, po) and np.array_equal(words, pw), tm
+
+
+@pytest.mark.parametrize("tm,keep", [(112, 0.6), (80, 1.0)])
+@pytest.mark.parametrize("splits", [None, "3"])
+def test_tall_overflow_n64_runs_wide_kernel(tm, keep, splits):
+    """Tall tiles denser than the shared-B register stage: N = 33..64 runs the N > 64 kernel
+    (variant 3, N padded to 128, splits of its first launch width); N <= 32 keeps the
+    8-wavefront kernel.  Integer products bit-exact for N on both sides of the boundaries."""
+    case = syn.random_case(300, 700, 64, keep, seed=tm, values="int3")
+    with env(LSCD_SPLITK=splits):
+        h = encode(case.A16, case.mask, tm)
+    info = h.info
+    say(f"overflow tm={tm} keep={keep} maxw={info['max_tile_words']} R={info['reg_vectors']} "
+        f"variant={info['variant']} S={info['splits']} Sw={info['splits_wide']}")
+    assert info["max_tile_words"] > info["reg_vectors"] * 64 * 4
+    assert info["variant"][:2] == [2, 2] and info["variant"][2] == 3
+    assert info["splits"][2] == info["splits_wide"][0]
+    for N in (16, 32, 33, 48, 64):
+        B16 = case.B16[:N]
+        C64 = osp.spmm_f64(case.A16, case.mask, B16)
+        assert np.abs(C64).max() < 2048
+        assert np.array_equal(run(h, B16, case.M), osp.fp16_rne(C64)), f"N={N}"
+
+
+def test_tall_fitting_tiles_keep_shared_b():
+    """Tall tiles that fit the register stage keep the shared-B kernel at N = 64."""
+    case = syn.random_case(300, 700, 64, 0.35, seed=5, values="int3")
+    h = encode(case.A16, case.mask, 112)
+    assert h.info["max_tile_words"] <= h.info["reg_vectors"] * 64 * 4
+    assert h.info["variant"][2] == 0
+    assert np.array_equal(run(h, case.B16, case.M), osp.fp16_rne(osp.spmm_f64(case.A16, case.mask, case.B16)))

@@ -211,6 +211,14 @@ lscd_status_t new_handle(const Grid& g, int64_t nnz, int64_t nwords, int32_t max
         h->Sw[i] = plan_splits(g, h->cus, occ, g.MB, 4, false);
         if (h->Sw[i] > 1) part = std::max<int64_t>(part, (int64_t)h->Sw[i] * g.M * npad * 4);
     }
+    // Tall tiles denser than the shared-B kernel's register stage (R vectors of 4 words per
+    // lane of each wavefront): N = 33..64 runs the N > 64 kernel instead, whose workgroup
+    // decodes each tile together, with N padded to 128.  OPT-30B MLP1 at 50 % sparsity and
+    // N = 64: 122 -> 93 us.  Where the tiles fit (60 %) the two tie; at 80 % shared-B is faster.
+    if (tall && kernel_tile && format == 0 && (int64_t)maxw > (int64_t)h->R * 64 * 4) {
+        h->kind[2] = kKernelWide;
+        h->S[2] = h->Sw[0];
+    }
     if (const char* fa = getenv("LSCD_TEST_FAIL_ALLOC"); fa && fa[0] == '1') {
         free_handle(h);
         return LSCD_ERROR_OUT_OF_MEMORY;
@@ -690,7 +698,7 @@ lscd_status_t lscd_spmm(lscd_handle_t h, const void* B, void* C, int32_t N, void
     for (int32_t c0 = 0; c0 < N; c0 += lscd::kWideMaxN) {
         const int32_t n = std::min(N - c0, lscd::kWideMaxN);
         int kind, npad, R, S;
-        if (n <= LSCD_NARROW_MAX_N) {
+        if (n <= LSCD_NARROW_MAX_N && h->kind[npad_index(n)] != lscd::kKernelWide) {
             kind = h->kind[npad_index(n)];
             npad = n <= 16 ? 16 : (n <= 32 ? 32 : 64);
             R = h->R;
