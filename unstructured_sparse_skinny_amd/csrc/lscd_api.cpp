@@ -42,7 +42,8 @@ void free_handle(lscd_handle_s* h) {
 //
 // Shared-B variant: as many workgroups as the GPU holds at once (CUs x resident workgroups
 // per CU, from the kernel's real occupancy), so the whole grid runs in a single wave.
-int plan_splits(const Grid& g, int cus, int blocks_per_cu, int64_t groups, int tiles_per_split_min, bool indep) {
+int plan_splits(const Grid& g, int cus, int blocks_per_cu, int64_t groups, int tiles_per_split_min, bool indep,
+                bool widen_low_fill = false) {
     int64_t S = 1;
     const int64_t smax = std::max<int64_t>(1, std::min<int64_t>(g.KT / tiles_per_split_min, 64));
     const char* e = getenv("LSCD_SPLITK");
@@ -63,6 +64,13 @@ int plan_splits(const Grid& g, int cus, int blocks_per_cu, int64_t groups, int t
     } else {
         const int64_t slots = (int64_t)cus * std::max(1, blocks_per_cu);
         S = std::min<int64_t>(slots / groups, smax);
+        // Slots less than 80 % full: twice the splits, i.e. a second, partial round of
+        // workgroups.  Measured on the Tiled-CSL shared-B and N > 64 kernels: 192 row blocks
+        // (OPT-175B OutProj, MLP2, config 4) at N = 128 go 105 -> 99, 381 -> 341 and 339 ->
+        // 301 us, and OPT-175B MLP1 at N = 64 (192 groups of 4) 248 -> 232 us.  Fills of 90 %
+        // and more (config 2, OPT-175B QKV and MLP1 at N = 128, config 4 at N = 64) were
+        // already the fastest count.
+        if (widen_low_fill && S * groups * 5 < slots * 4) S = std::min<int64_t>(2 * S, smax);
     }
     S = std::max<int64_t>(1, std::min<int64_t>(S, g.KT));
     return (int)S;
@@ -201,14 +209,14 @@ lscd_status_t new_handle(const Grid& g, int64_t nnz, int64_t nwords, int32_t max
         h->kind[i] = tall ? (i < 2 ? kKernelIndep8 : kKernelShared) : pick_kind(16 << i);
         const int occ = spmm_blocks_per_cu(h->kind[i], 16 << i, h->R, (int)std::min<int64_t>(g.K, 1 << 30), g.tm);
         const int min_tiles = h->kind[i] == kKernelIndep ? 8 : (h->kind[i] == kKernelIndep8 ? 16 : 2);
-        h->S[i] = plan_splits(g, h->cus, occ, row_groups(g, h->kind[i]), min_tiles, h->kind[i] != kKernelShared);
+        h->S[i] = plan_splits(g, h->cus, occ, row_groups(g, h->kind[i]), min_tiles, h->kind[i] != kKernelShared, true);
         if (h->S[i] > 1) part = std::max<int64_t>(part, (int64_t)h->S[i] * g.M * (16 << i) * 4);
     }
     h->Rw = pick_reg_vectors_wide(maxw);
     for (int i = 0; i < 3 && kernel_tile && format == 0; ++i) {
         const int npad = 128 + 64 * i;
         const int occ = spmm_blocks_per_cu(kKernelWide, npad, h->Rw, (int)std::min<int64_t>(g.K, 1 << 30), g.tm);
-        h->Sw[i] = plan_splits(g, h->cus, occ, g.MB, 4, false);
+        h->Sw[i] = plan_splits(g, h->cus, occ, g.MB, 4, false, true);
         if (h->Sw[i] > 1) part = std::max<int64_t>(part, (int64_t)h->Sw[i] * g.M * npad * 4);
     }
     // Tall tiles denser than the shared-B kernel's register stage (R vectors of 4 words per
