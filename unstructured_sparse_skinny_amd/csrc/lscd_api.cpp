@@ -69,7 +69,8 @@ int plan_splits(const Grid& g, int cus, int blocks_per_cu, int64_t groups, int t
         // (OPT-175B OutProj, MLP2, config 4) at N = 128 go 105 -> 99, 381 -> 341 and 339 ->
         // 301 us, and OPT-175B MLP1 at N = 64 (192 groups of 4) 248 -> 232 us.  Fills of 90 %
         // and more (config 2, OPT-175B QKV and MLP1 at N = 128, config 4 at N = 64) were
-        // already the fastest count.
+        // already the fastest count.  Three-level tiles at N = 64 likewise: OPT-175B MLP1
+        // 240 -> 224 us.
         if (widen_low_fill && S * groups * 5 < slots * 4) S = std::min<int64_t>(2 * S, smax);
     }
     S = std::max<int64_t>(1, std::min<int64_t>(S, g.KT));
@@ -198,7 +199,7 @@ lscd_status_t new_handle(const Grid& g, int64_t nnz, int64_t nwords, int32_t max
             // the resident slots; N <= 32: one row block per workgroup, splits that balance the
             // busiest CU (OPT-175B QKV at N = 16: 145 -> 131 us with 4 splits)
             const int64_t groups = npad == 64 ? (g.MB + kWaves - 1) / kWaves : g.MB;
-            h->S[i] = plan_splits(g, h->cus, occ, groups, 8, npad != 64);
+            h->S[i] = plan_splits(g, h->cus, occ, groups, 8, npad != 64, true);
             if (h->S[i] > 1) part = std::max<int64_t>(part, (int64_t)h->S[i] * g.M * npad * 4);
         }
     }
