@@ -125,3 +125,32 @@ def test_wide_limits():
                           L.ctypes.c_void_p(C.data_ptr()), L.LSCD_MAX_N + 1, None)
     assert st == L.LSCD_ERROR_NOT_SUPPORTED
     torch.cuda.synchronize()
+
+
+def test_split_plan_low_fill_doubles():
+    """192 row blocks of 64 rows at 50 % sparsity: the N > 64 kernel's slot-filling count (2,
+    75 % of the resident slots on 256 CUs) is doubled to 4, while the shared-B launch at
+    N = 64 (10 splits, 94 % of the slots) keeps its count.  The product at N = 128 with the
+    doubled plan is bit-exact on integer inputs (sampled rows)."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([31337, 128])))
+    M, K, N = 12288, 2048, 128
+    A16 = syn.int_fp16(rng, M, K)
+    mask = (rng.random((M, K), dtype=np.float32) < 0.5).astype(np.uint8)
+    h = L.lscd_encode(A16, mask)
+    info = h.info
+    say(f"plan cus={cus} tile={info['tile_m']} S={info['splits']} Sw={info['splits_wide']} variant={info['variant']}")
+    if cus == 256:
+        assert info["tile_m"] == 64
+        assert info["splits_wide"][0] == 4
+        assert info["splits"][2] == 10
+    B16 = syn.int_fp16(rng, N, K)
+    B = torch.from_numpy(B16.view(np.float16)).to("cuda")
+    C = torch.full((N, M), float("nan"), dtype=torch.float16, device="cuda")
+    L.lscd_spmm(h, B, C)
+    torch.cuda.synchronize()
+    rows = np.array(sorted(set(range(64)) | set(range(M - 64, M)) |
+                           set(rng.choice(M, size=256, replace=False).tolist())), dtype=np.int64)
+    C64 = osp.spmm_f64(A16, mask, B16, rows=rows)
+    assert np.abs(C64).max() < 65504
+    assert np.array_equal(C.cpu().numpy().view(np.uint16)[:, rows], osp.fp16_rne(C64))
