@@ -1,29 +1,38 @@
 #!/usr/bin/env python3
 """Throughput of lscd_spmm (Load-as-Sparse, Compute-as-Dense skinny SpMM) on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--config 2] [--shape 0] [--n N] [--sparsity S]
+    python bench.py [--steps K] [--warmup W] [--config 4] [--shape 0] [--n N] [--sparsity S]
 
 A step is one lscd_spmm call, C[N][M] = A_sparse[M][K] . B[N][K]^T, over inputs already
 resident in HBM; the format is encoded once before timing (ahead of time, as the method
-prescribes).  To keep the 256 MB Infinity Cache from serving A, the timed loop rotates over
-several device copies of the encoded matrix whose total exceeds three times that cache.
+prescribes).  The default workload is the largest configuration, the OPT-175B-shaped MLP2
+(12288 x 49152, 60 % unstructured sparsity, N = 64).  To keep the 256 MB Infinity Cache from
+serving A, the timed loop rotates over several device copies of the encoded matrix whose
+total exceeds three times that cache.
 
 Printed (one JSON line on stdout):
   value         effective GB/s = (4*nnz + 4*(tiles+1) + 2*K*N + 2*M*N) / wall time per step
   tflops        dense-equivalent 2*M*N*K / wall time per step
-  roofline      the product kernel's algorithmic bytes / its average duration from a HIP
-                event pair around the timed steps (one graph replay), against 8 TB/s HBM
+  roofline      the product's algorithmic bytes / its average device time per step, from a HIP
+                event pair on the launch stream around the timed steps (one graph replay),
+                against 8 TB/s HBM; stream_frac = the same against the streaming-read reference
+  stream_ref    a plain streaming read of the same byte count with the product's own loads
+                (lscd_stream_read), rotated over as many buffers and timed the same way: how
+                fast this GPU streams that many bytes, the ceiling of a memory-bound kernel
   dense_hipblaslt  the same product as a dense fp16 GEMM: hipBLASLt with the fastest of its
                 heuristic's candidates (lscd_tune_dense, through lscd_linear), timed the same way;
                 torch.mm's default choice beside it
-  cpu_baseline  the CPU oracle on a bounded row sample (reported baseline only)
+  cpu_baseline  the plain C oracle (decode + fp64 triple loop, OpenMP over rows) on a bounded
+                row sample, and single-threaded on the tiny configuration (reported baseline only)
 """
 import argparse
 import ctypes
 import hashlib
+import importlib.util
 import json
 import math
 import os
+import platform
 import sys
 import time
 
@@ -33,6 +42,8 @@ sys.path.insert(0, ROOT)
 MALL_BYTES = 256 << 20
 HBM_PEAK_GBS = 8000.0
 METRIC = "dense-equiv TFLOPS & effective HBM GB/s (% of roofline) per skinny SpMM, 1 GPU"
+DEFAULT_CONFIG = 4          # the largest configuration: OPT-175B MLP2, 12288 x 49152, 60 %, N = 64
+WARM_S = 0.3                # untimed graph replays before the timed one, seconds
 
 
 def parse():
@@ -40,8 +51,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", type=int, default=2, help="1..5: tiny, OPT-30B MLP1, OPT-66B QKV, "
-                                                           "OPT-175B MLP2, OPT-175B layer at 50%%")
+    ap.add_argument("--config", type=int, default=DEFAULT_CONFIG,
+                    help="1..5: tiny, OPT-30B MLP1, OPT-66B QKV, OPT-175B MLP2 (default), OPT-175B layer at 50%%")
     ap.add_argument("--shape", type=int, default=0, help="config 5 only: 0 QKV, 1 OutProj, 2 MLP1, 3 MLP2")
     ap.add_argument("--n", type=int, default=None, help="batch width N (default: the config's)")
     ap.add_argument("--sparsity", type=float, default=None, help="override the config's sparsity")
@@ -51,12 +62,13 @@ def parse():
     ap.add_argument("--copies", type=int, default=0, help="encoded copies rotated in the timed loop (0: auto)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-dense", action="store_true", help="skip the dense hipBLASLt baseline")
+    ap.add_argument("--no-stream-ref", action="store_true", help="skip the streaming-read reference")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU baseline sample budget")
     ap.add_argument("--eager", action="store_true",
                     help="time eager calls with an event pair around each (default: one HIP graph replay)")
     ap.add_argument("--sweep-n", default=None, metavar="N1,N2,...",
-                    help="instead of the benchmark line: time the sparse product, the dense GEMM and "
-                         "lscd_linear (cost-model choice) for each N on the config's matrix, one JSON line each")
+                    help="instead of the benchmark line: time the sparse product, the tuned dense GEMM and "
+                         "lscd_linear's choice for each N on the config's matrix, one JSON line each")
     ap.add_argument("--encode", action="store_true",
                     help="instead of the benchmark line: time the device encoder (lscd_encode_device) and "
                          "the host encoder (lscd_pack) on the config's matrix, one JSON line")
@@ -70,9 +82,16 @@ def log(*a):
 
 
 def kernel_source_hash():
-    """Short hash of the device source: committed counter figures are valid only for it."""
-    with open(os.path.join(ROOT, "unstructured_sparse_skinny_amd/csrc/lscd_kernels.hip"), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Short hash of the device sources: committed counter figures are valid only for them."""
+    spec = importlib.util.spec_from_file_location("_lscd_build", os.path.join(ROOT, "unstructured_sparse_skinny_amd",
+                                                                               "build.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    h = hashlib.sha256()
+    for rel in mod.DEVICE_SOURCES:
+        with open(os.path.join(ROOT, "unstructured_sparse_skinny_amd", rel), "rb") as f:
+            h.update(rel.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
 
 
 def calibrate():
@@ -90,14 +109,24 @@ def calibrate():
                       "bytes_read_per_dispatch": n, "bytes_written_per_dispatch": n, "dispatches": 5}))
 
 
-def time_calls(fn_args, steps, warmup, torch, graph=True):
+class Timing:
+    """Result of time_calls (all times in ms per step)."""
+
+    def __init__(self, wall, dev_mean, spread=None, pct=None):
+        self.wall, self.dev_mean, self.spread, self.pct = wall, dev_mean, spread, pct
+
+
+def time_calls(fn_args, steps, warmup, torch, graph=True, spread_replays=5):
     """Time `steps` calls rotating over fn_args, after `warmup` eager calls.
 
-    graph=True: the steps are captured once into a HIP graph on a side stream and the timed
-    region is one replay (how a serving loop would launch them; no Python in between).  A
-    HIP event pair on that stream around the replay gives the average device time per
-    step.  graph=False: eager calls with an event pair around each one.
-    Returns (wall ms per step, mean device ms per step, median, p10, p90).
+    graph=True: the steps are captured once into a HIP graph on a side stream and, after
+    untimed replays for WARM_S seconds, the timed region is one replay (how a serving loop
+    would launch them; no Python in between).  A
+    HIP event pair on that stream around the replay gives the average device time per step.
+    Then `spread_replays` further replays, each between its own event pair, give the spread
+    of that average from replay to replay (a graph replay has no per-step events, so no
+    per-step percentiles are claimed).  graph=False: eager calls with an event pair around
+    each one; p10 / p50 / p90 over the calls.
     """
     k = len(fn_args)
     for i in range(warmup):
@@ -112,8 +141,15 @@ def time_calls(fn_args, steps, warmup, torch, graph=True):
                 for i in range(steps):
                     f, a = fn_args[i % k]
                     f(*a)
-        g.replay()                                    # untimed: first replay uploads the graph
-        torch.cuda.synchronize()
+        # untimed replays: the first uploads the graph; the rest, for at least WARM_S seconds,
+        # bring the GPU to its steady clocks (a first replay right after a cold start measured
+        # up to 8 % slower than the ones after it)
+        t_w = time.perf_counter()
+        while True:
+            g.replay()
+            torch.cuda.synchronize()
+            if time.perf_counter() - t_w >= WARM_S:
+                break
         t_s, t_e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t0 = time.perf_counter()
         with torch.cuda.stream(side):
@@ -123,7 +159,16 @@ def time_calls(fn_args, steps, warmup, torch, graph=True):
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         dev = t_s.elapsed_time(t_e) / steps
-        return wall / steps * 1e3, dev, dev, dev, dev
+        spread = []
+        for _ in range(spread_replays):
+            with torch.cuda.stream(side):
+                t_s.record(side)
+                g.replay()
+                t_e.record(side)
+            torch.cuda.synchronize()
+            spread.append(t_s.elapsed_time(t_e) / steps)
+        del g
+        return Timing(wall / steps * 1e3, dev, spread=spread)
     stream = torch.cuda.current_stream()
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
@@ -137,75 +182,171 @@ def time_calls(fn_args, steps, warmup, torch, graph=True):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ev = sorted(s_.elapsed_time(e) for s_, e in zip(starts, ends))
-    return wall / steps * 1e3, sum(ev) / len(ev), ev[len(ev) // 2], ev[len(ev) // 10], ev[(len(ev) * 9) // 10]
+    return Timing(wall / steps * 1e3, sum(ev) / len(ev),
+                  pct=(ev[len(ev) // 10], ev[len(ev) // 2], ev[(len(ev) * 9) // 10]))
 
 
-def cpu_baseline(case, alg_bytes, flops, budget_s):
-    """The oracle's fp64 product on a bounded sample of rows, scaled to the same units as `value`."""
-    import numpy as np
-    from oracle import spmm as osp
+def cpu_model():
     try:
-        from threadpoolctl import threadpool_info
-        threads = max((p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"), default=1)
-    except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def cpu_baseline(case, tile_m, alg_bytes, flops, budget_s):
+    """The plain C oracle on a bounded sample of the same matrices, scaled to the whole product:
+    the Tiled-CSL decode of a few whole row blocks (encoded by the oracle's own encoder, untimed,
+    ahead of time as the method prescribes) and the fp64 triple loop over a random sample of rows
+    sized to the budget, both with every OpenMP thread of the host.  Also the tiny configuration,
+    whole and single-threaded."""
+    import numpy as np
+    import lscd_synth as syn
+    from oracle import loop, tiled_csl
+    threads = loop.max_threads()
     rng = np.random.default_rng(0)
-    probe = np.sort(rng.choice(case.M, size=min(case.M, 256), replace=False))
+    MB = -(-case.M // tile_m)
+    # decode leg: 8 random row blocks
+    blocks = np.sort(rng.choice(MB, size=min(MB, 8), replace=False))
+    rows_d = np.concatenate([np.arange(b * tile_m, min(case.M, (b + 1) * tile_m)) for b in blocks])
+    w, o = tiled_csl.encode_canonical(case.A16[rows_d], case.mask[rows_d], tile_m, 64)
     t0 = time.perf_counter()
-    osp.spmm_f64(case.A16, case.mask, case.B16, rows=probe)
+    loop.decode(w, o, rows_d.size, case.K, tile_m, 64)
+    t_dec = (time.perf_counter() - t0) * MB / blocks.size
+    # loop leg: rows of the decoded matrix (the masked weights), sized from a probe to the budget
+    probe = np.sort(rng.choice(case.M, size=min(case.M, 4 * threads), replace=False))
+    dp = tiled_csl.masked(case.A16[probe], case.mask[probe])
+    t0 = time.perf_counter()
+    loop.spmm(dp, case.B16)
     t_probe = time.perf_counter() - t0
-    rows_n = int(min(case.M, max(len(probe), len(probe) * budget_s / max(t_probe, 1e-6))))
+    rows_n = int(min(case.M, max(probe.size, probe.size * budget_s / max(t_probe, 1e-6))))
     rows = np.sort(rng.choice(case.M, size=rows_n, replace=False))
-    passes, dt = 0, 0.0
-    while passes == 0 or dt < budget_s:       # repeat a fast sample until the budget is used
-        t0 = time.perf_counter()
-        osp.spmm_f64(case.A16, case.mask, case.B16, rows=rows)
-        dt += time.perf_counter() - t0
-        passes += 1
-    frac = rows_n * passes / case.M
-    return {"value": round(alg_bytes * frac / dt / 1e9, 3), "unit": "GB/s", "cores": int(threads),
-            "kind": "oracle", "tflops": round(flops * frac / dt / 1e12, 5), "seconds": round(dt, 2),
-            "sample": f"{passes} pass(es) over {rows_n} of {case.M} rows (random, seed 0) of the same matrices; "
-                      f"fp64 numpy/BLAS product of the masked rows; bytes and flops scaled by rows computed / M"}
+    dense = tiled_csl.masked(case.A16[rows], case.mask[rows])
+    t0 = time.perf_counter()
+    loop.spmm(dense, case.B16)
+    t_loop = time.perf_counter() - t0
+    del dense
+    t_full = t_dec + t_loop * case.M / rows_n
+    # the tiny configuration (1024 x 1024, 80 %, N = 8), whole, on one thread
+    tiny = syn.make_config(1)
+    tw, to = tiled_csl.encode_canonical(tiny.A16, tiny.mask, 64, 64)
+    t0 = time.perf_counter()
+    d1 = loop.decode(tw, to, tiny.M, tiny.K, 64, 64)
+    loop.spmm(d1, tiny.B16, threads=1)
+    t1 = time.perf_counter() - t0
+    nnz1 = int(np.count_nonzero(tiny.mask))
+    b1 = 4 * nnz1 + 4 * to.size + 2 * tiny.K * tiny.N + 2 * tiny.M * tiny.N
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        affinity = os.cpu_count()
+    return {"value": round(alg_bytes / t_full / 1e9, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "tflops": round(flops / t_full / 1e12, 6), "seconds_full_matrix": round(t_full, 2),
+            "nproc": os.cpu_count(), "affinity_cpus": affinity, "cpu": cpu_model(),
+            "sample": f"C oracle (oracle/spmm_loop.c) with {threads} OpenMP threads: Tiled-CSL decode of {blocks.size} "
+                      f"random row blocks of {tile_m} rows (scaled by {MB} / {blocks.size}) plus the fp64 triple loop "
+                      f"over {rows_n} random rows of the decoded weights ({t_loop:.2f} s, scaled by M / {rows_n}); "
+                      f"seed 0",
+            "tiny_single_thread": {"workload": tiny.name, "value": round(b1 / t1 / 1e9, 4), "unit": "GB/s",
+                                   "seconds": round(t1, 4), "cores": 1,
+                                   "what": "decode + triple loop of the whole tiny product on one thread"}}
+
+
+def stream_reference(L, torch, nbytes, copies, steps, warmup, eager):
+    """lscd_stream_read over `nbytes` rotated over `copies` buffers, timed like the product; the
+    best of 1, 2, 4 and 8 workgroups per CU."""
+    nb = (int(nbytes) + 15) // 16 * 16
+    bufs = [torch.empty(nb, dtype=torch.uint8, device="cuda") for _ in range(copies)]
+    for b in bufs:
+        b.random_(0, 255)
+    sink = torch.zeros(4, dtype=torch.uint8, device="cuda")
+    fn = L._lib.lscd_stream_read
+
+    def checked(*a):
+        st = fn(*a)
+        if st != 0:
+            raise L.LSCDError(st, "lscd_stream_read")
+
+    res = {}
+    for bpc in (1, 2, 4, 8):
+        calls = [(checked, (ctypes.c_void_p(b.data_ptr()), nb, bpc, ctypes.c_void_p(sink.data_ptr()), _Cur(torch)))
+                 for b in bufs]
+        t = time_calls(calls, steps, warmup, torch, graph=not eager, spread_replays=0)
+        res[bpc] = t.dev_mean
+    del bufs
+    best = min(res, key=res.get)
+    return {"gbs": round(nbytes / (res[best] * 1e-3) / 1e9, 1), "us": round(res[best] * 1e3, 2),
+            "bytes": int(nbytes), "workgroups_per_cu": best, "copies": copies,
+            "us_by_workgroups_per_cu": {str(k): round(v * 1e3, 2) for k, v in res.items()},
+            "frac_of_peak": round(nbytes / (res[best] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "kernel": "lscd_stream_read (128-bit non-temporal buffer loads, one contiguous range per workgroup)"}
+
+
+class _Cur:
+    """ctypes stream argument read at call time, so captured calls land on the capture stream."""
+
+    def __init__(self, torch):
+        self.torch = torch
+
+    @property
+    def _as_parameter_(self):
+        return ctypes.c_void_p(self.torch.cuda.current_stream().cuda_stream)
+
+
+def dense_copies(M, K):
+    return max(2, min(16, math.ceil(3 * MALL_BYTES / (2 * M * K)) + 1))
 
 
 def sweep_n(args, case, L, torch, np):
-    """N sweep to the dense crossover: sparse (lscd_spmm), dense (torch.mm -> hipBLASLt's default
-    choice, and the library's dense path with hipBLASLt tuned for N) and lscd_linear's own
-    choice on the attached dense copy, for every N of --sweep-n."""
+    """N sweep to the dense crossover: the sparse product (lscd_spmm), the dense GEMM (torch.mm, i.e.
+    hipBLASLt's default choice, and the library's dense path with hipBLASLt tuned for N) and
+    lscd_linear's own choice, for every N of --sweep-n.  Every leg rotates over copies of its
+    matrix (sparse: encoded copies; dense: decoded copies) whose total exceeds three times the
+    Infinity Cache, and runs as one graph replay (lscd_linear eagerly when its dense path cannot
+    be captured)."""
     M, K = case.M, case.K
     if args.format == "tiled-csl":
         tm = L.lscd_default_tile_m(M, K)
         words, offs = L.lscd_pack(case.A16, case.mask, tm, 64)
         h0 = L.lscd_import(words, offs, M, K, tm, 64)
         info = h0.info
-        copies = max(1, min(8, math.ceil(3 * MALL_BYTES / info["format_bytes"])))
+        copies = max(2, min(8, math.ceil(3 * MALL_BYTES / info["format_bytes"]) + 1))
         hs = [h0] + [L.lscd_import(words, offs, M, K, tm, 64) for _ in range(copies - 1)]
         del words, offs
     else:
         enc = L.lscd_encode_bitmap if args.format == "bitmap" else L.lscd_encode_three_level
         h0 = enc(case.A16, case.mask)
         info = h0.info
-        copies = max(1, min(8, math.ceil(3 * MALL_BYTES / info["format_bytes"])))
+        copies = max(2, min(8, math.ceil(3 * MALL_BYTES / info["format_bytes"]) + 1))
         hs = [h0] + [enc(case.A16, case.mask) for _ in range(copies - 1)]
+    nd = min(len(hs), dense_copies(M, K))
+    for h in hs[:nd]:
+        L.lscd_attach_dense(h)
     Ad = torch.from_numpy(np.where(case.mask.astype(bool), case.A16, 0).astype(np.uint16).view(np.float16))
-    dcopies = max(1, min(4, math.ceil(3 * MALL_BYTES / (2 * M * K))))
-    Ads = [Ad.to("cuda") for _ in range(dcopies)]
+    Ads = [Ad.to("cuda") for _ in range(nd)]
     del Ad
-    L.lscd_attach_dense(h0)
     gen = torch.Generator().manual_seed(1234)
     last_sparse_win = None
     for N in [int(x) for x in args.sweep_n.split(",")]:
         B = torch.randn(N, K, generator=gen).half().to("cuda")
         C = torch.empty(N, M, dtype=torch.float16, device="cuda")
-        _, ts, *_ = time_calls([(L.lscd_spmm, (h, B, C)) for h in hs], args.steps, args.warmup, torch)
-        _, td, *_ = time_calls([(torch.mm, (B, a.t())) for a in Ads], args.steps, args.warmup, torch)
-        # the library's dense path with hipBLASLt tuned for this N, then lscd_linear's own choice
-        tune_us, _ = L.lscd_tune_dense(h0, B, C)
-        L.lscd_set_linear_crossover(h0, 0)
-        _, tt, *_ = time_calls([(L.lscd_linear, (h0, B, C))], args.steps, args.warmup, torch, graph=False)
-        L.lscd_set_linear_crossover(h0, -1)
-        _, tl, *_ = time_calls([(L.lscd_linear, (h0, B, C))], args.steps, args.warmup, torch, graph=False)
+        ts = time_calls([(L.lscd_spmm, (h, B, C)) for h in hs], args.steps, args.warmup, torch).dev_mean
+        td = time_calls([(torch.mm, (B, a.t())) for a in Ads], args.steps, args.warmup, torch).dev_mean
+        tune = [L.lscd_tune_dense(h, B, C)[0] for h in hs[:nd]]
+        for h in hs[:nd]:
+            L.lscd_set_linear_crossover(h, 0)
+        try:
+            tt = time_calls([(L.lscd_linear, (h, B, C)) for h in hs[:nd]], args.steps, args.warmup, torch).dev_mean
+        except RuntimeError:
+            tt = time_calls([(L.lscd_linear, (h, B, C)) for h in hs[:nd]], args.steps, args.warmup, torch,
+                            graph=False).dev_mean
+        for h in hs[:nd]:
+            L.lscd_set_linear_crossover(h, -1)
+        path = L.lscd_linear_path(hs[0], N)
+        tl = ts if path == 0 else tt
         ms, md = L.lscd_linear_model(M, K, info["nnz_padded"], info["num_tiles"], N)
         if args.format != "tiled-csl":
             ms = None  # the variant formats are costed per tile, not by this model
@@ -213,10 +354,15 @@ def sweep_n(args, case, L, torch, np):
             last_sparse_win = N
         print(json.dumps({"sweep": "n", "workload": case.name, "format": args.format, "M": M, "K": K, "N": N,
                           "sparsity": round(case.sparsity, 4), "sparse_us": round(ts * 1e3, 1),
-                          "dense_hipblaslt_us": round(td * 1e3, 1), "dense_tuned_us": round(tt * 1e3, 1),
-                          "tune_us": round(tune_us, 1), "linear_us": round(tl * 1e3, 1),
-                          "linear_path": ["sparse", "dense"][L.lscd_linear_path(h0, N)],
+                          "dense_torch_mm_us": round(td * 1e3, 1), "dense_tuned_us": round(tt * 1e3, 1),
+                          "tune_us": [round(t, 1) for t in tune], "linear_us": round(tl * 1e3, 1),
+                          "linear_path": ["sparse", "dense"][path],
+                          "linear_picks_faster": (path == 0) == (ts <= tt),
                           "model_sparse_us": None if ms is None else round(ms, 1), "model_dense_us": round(md, 1),
+                          "sparse_pct_roofline": round(100 * (4 * info["nnz"] + 4 * (info["num_tiles"] + 1) +
+                                                              2 * K * N + 2 * M * N) / (ts * 1e-3) / 1e9 /
+                                                       HBM_PEAK_GBS, 1) if args.format == "tiled-csl" else None,
+                          "speedup_vs_tuned_dense": round(tt / ts, 3),
                           "sparse_tflops": round(2 * M * N * K / (ts * 1e-3) / 1e12, 1)}), flush=True)
     print(json.dumps({"sweep": "n", "workload": case.name, "largest_n_sparse_wins": last_sparse_win}), flush=True)
 
@@ -244,6 +390,9 @@ def bench_encode(args, case, L, torch, np):
                       "host_ms": round(t_host * 1e3, 1), "host_threads": os.cpu_count(),
                       "speedup": round(t_host / t_dev, 1),
                       "note": "wall time per synchronous call, allocations included"}), flush=True)
+
+
+VARIANTS = ["shared-B", "independent-4", "independent-8", "wide", "bitmap", "three-level"]
 
 
 def main():
@@ -277,14 +426,12 @@ def main():
         return
 
     t_enc = time.perf_counter()
+    tm = L.lscd_default_tile_m(M, K)           # the tile height lscd_encode would use
     if args.format == "bitmap":
-        words, offs = L.lscd_pack_bitmap(case.A16, case.mask)
         h0 = L.lscd_encode_bitmap(case.A16, case.mask)
     elif args.format == "three-level":
-        words, offs = L.lscd_pack_three_level(case.A16, case.mask)
         h0 = L.lscd_encode_three_level(case.A16, case.mask)
     else:
-        tm = L.lscd_default_tile_m(M, K)       # the tile height lscd_encode would use
         words, offs = L.lscd_pack(case.A16, case.mask, tm, 64)
         h0 = L.lscd_import(words, offs, M, K, tm, 64)
     info = h0.info
@@ -296,7 +443,7 @@ def main():
         handles = [h0] + [L.lscd_encode_three_level(case.A16, case.mask) for _ in range(copies - 1)]
     else:
         handles = [h0] + [L.lscd_import(words, offs, M, K, tm, 64) for _ in range(copies - 1)]
-    del words, offs
+        del words, offs
     log(f"[bench] encoded {copies} copies of {fmt_bytes / 1e6:.1f} MB in {time.perf_counter() - t_enc:.1f}s; "
         f"splits={info['splits']} variants={info['variant']} reg_vectors={info['reg_vectors']} "
         f"max_tile_words={info['max_tile_words']}")
@@ -321,27 +468,34 @@ def main():
         if st != 0:
             raise L.LSCDError(st, "lscd_spmm")
 
-    # the stream argument is read at call time, so captured calls land on the capture stream
-    class _Cur:
-        @property
-        def _as_parameter_(self):
-            return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-
     calls = [(checked, (ctypes.c_void_p(h.ptr), ctypes.c_void_p(B.data_ptr()), ctypes.c_void_p(C.data_ptr()),
-                        N, _Cur())) for h in handles]
-    log("[bench] timing lscd_spmm (HIP graph of the timed steps)")
-    ms_step, ev_mean, ev_med, ev_p10, ev_p90 = time_calls(calls, args.steps, args.warmup, torch, graph=not args.eager)
+                        N, _Cur(torch))) for h in handles]
+    log("[bench] timing lscd_spmm (HIP graph of the timed steps)" if not args.eager else "[bench] timing lscd_spmm")
+    ts = time_calls(calls, args.steps, args.warmup, torch, graph=not args.eager)
     if not torch.isfinite(C.float()).all():
         raise RuntimeError("non-finite output")
-    value = alg_bytes / (ms_step * 1e-3) / 1e9
-    achieved = alg_bytes / (ev_mean * 1e-3) / 1e9
-    log(f"[bench] lscd: {ms_step * 1e3:.1f} us/step wall, device events {ev_mean * 1e3:.1f} us/step "
-        f"(p10 {ev_p10 * 1e3:.1f}, p50 {ev_med * 1e3:.1f}, p90 {ev_p90 * 1e3:.1f}) -> {achieved:.0f} GB/s")
+    value = alg_bytes / (ts.wall * 1e-3) / 1e9
+    achieved = alg_bytes / (ts.dev_mean * 1e-3) / 1e9
+    if ts.pct:
+        log(f"[bench] lscd: {ts.wall * 1e3:.1f} us/step wall, device events {ts.dev_mean * 1e3:.1f} us/step "
+            f"(p10 {ts.pct[0] * 1e3:.1f}, p50 {ts.pct[1] * 1e3:.1f}, p90 {ts.pct[2] * 1e3:.1f}) -> {achieved:.0f} GB/s")
+    else:
+        log(f"[bench] lscd: {ts.wall * 1e3:.1f} us/step wall, device events {ts.dev_mean * 1e3:.1f} us/step "
+            f"(mean of {args.steps} steps in one replay; further replays "
+            f"{', '.join(f'{x * 1e3:.1f}' for x in ts.spread)}) -> {achieved:.0f} GB/s")
+
+    stream = None
+    if not args.no_stream_ref:
+        log("[bench] streaming-read reference of the same byte count")
+        stream = stream_reference(L, torch, alg_bytes, copies, args.steps, args.warmup, args.eager)
+        log(f"[bench] stream read: {stream['us']:.1f} us -> {stream['gbs']:.0f} GB/s "
+            f"({stream['workgroups_per_cu']} workgroups per CU); product at "
+            f"{100 * achieved / stream['gbs']:.1f} % of it")
 
     dense = None
     if not args.no_dense:
         dense_bytes = 2 * M * K + 2 * K * N + 2 * M * N
-        ncopy = min(len(handles), max(2, min(16, math.ceil(3 * MALL_BYTES / (2 * M * K)) + 1)))
+        ncopy = min(len(handles), dense_copies(M, K))
         Cd = torch.empty((N, M), dtype=torch.float16, device="cuda")
         # hipBLASLt with the fastest of its heuristic's candidates for this N (lscd_tune_dense),
         # run through lscd_linear's dense path on dense copies decoded from the encoding and
@@ -360,68 +514,79 @@ def main():
                 raise L.LSCDError(st, "lscd_linear")
 
         dcalls = [(lin_checked, (ctypes.c_void_p(h.ptr), ctypes.c_void_p(B.data_ptr()), ctypes.c_void_p(Cd.data_ptr()),
-                                 N, _Cur())) for h in handles[:ncopy]]
+                                 N, _Cur(torch))) for h in handles[:ncopy]]
         d_graph = not args.eager
         try:
-            d_ms, d_mean, _, _, _ = time_calls(dcalls, args.steps, args.warmup, torch, graph=d_graph)
+            td = time_calls(dcalls, args.steps, args.warmup, torch, graph=d_graph, spread_replays=0)
         except RuntimeError:
             d_graph = False
-            d_ms, d_mean, _, _, _ = time_calls(dcalls, args.steps, args.warmup, torch, graph=False)
+            td = time_calls(dcalls, args.steps, args.warmup, torch, graph=False)
         # torch.mm on the masked matrix (hipBLASLt through PyTorch, its default choice), eager
         log("[bench] timing dense fp16 GEMM: torch.mm (default algorithm)")
         Ad = torch.from_numpy(np.where(case.mask.astype(bool), case.A16, 0).astype(np.uint16).view(np.float16))
         Ads = [Ad.to("cuda") for _ in range(ncopy)]
         del Ad
         tcalls = [(lambda x, y: torch.mm(x, y, out=Cd), (B, a.t())) for a in Ads]
-        t_ms, _, _, _, _ = time_calls(tcalls, args.steps, args.warmup, torch, graph=False)
+        tt = time_calls(tcalls, args.steps, args.warmup, torch, graph=False)
         del Ads
-        dense = {"ms_per_step": round(d_ms, 5), "kernel_ms_mean": round(d_mean, 5),
-                 "effective_gbs": round(dense_bytes / (d_ms * 1e-3) / 1e9, 1),
-                 "tflops": round(flops / (d_ms * 1e-3) / 1e12, 2), "copies": ncopy,
-                 "lscd_speedup": round(d_ms / ms_step, 3),
+        dense = {"ms_per_step": round(td.wall, 5), "kernel_ms_mean": round(td.dev_mean, 5),
+                 "effective_gbs": round(dense_bytes / (td.wall * 1e-3) / 1e9, 1),
+                 "tflops": round(flops / (td.wall * 1e-3) / 1e12, 2), "copies": ncopy,
+                 "lscd_speedup": round(td.wall / ts.wall, 3),
+                 "lscd_speedup_device": round(td.dev_mean / ts.dev_mean, 3),
                  "library": "hipBLASLt, fastest of %d heuristic candidates (lscd_tune_dense)" % tuned[0][1],
                  "timing": "one HIP graph replay" if d_graph else "eager, event pair per call",
-                 "tune_us_back_to_back": [round(t[0], 2) for t in tuned],
-                 "torch_mm_ms_per_step": round(t_ms, 5), "lscd_speedup_vs_torch_mm": round(t_ms / ms_step, 3),
+                 "tune_us_flushed_median": [round(t[0], 2) for t in tuned],
+                 "torch_mm_ms_per_step": round(tt.wall, 5), "lscd_speedup_vs_torch_mm": round(tt.wall / ts.wall, 3),
                  "blas": str(torch.backends.cuda.preferred_blas_library())}
-        log(f"[bench] dense (tuned hipBLASLt): {d_ms * 1e3:.1f} us/step -> speedup of lscd {d_ms / ms_step:.2f}x; "
-            f"torch.mm {t_ms * 1e3:.1f} us/step ({t_ms / ms_step:.2f}x)")
+        log(f"[bench] dense (tuned hipBLASLt): {td.wall * 1e3:.1f} us/step -> speedup of lscd "
+            f"{td.wall / ts.wall:.2f}x; torch.mm {tt.wall * 1e3:.1f} us/step ({tt.wall / ts.wall:.2f}x)")
 
     cpu = None
     if not args.no_cpu:
         log("[bench] CPU oracle baseline")
-        cpu = cpu_baseline(case, alg_bytes, flops, args.cpu_seconds)
+        cpu = cpu_baseline(case, info["tile_m"], alg_bytes, flops, args.cpu_seconds)
+        log(f"[bench] CPU oracle: {cpu['value']} GB/s on {cpu['cores']} threads ({cpu['cpu']})")
 
     # HBM bytes per launch from the committed counter summary of this workload, valid only
-    # while the kernel sources are the ones the counters were taken with.
+    # while the kernel sources and launch plan are the ones the counters were taken with.
     traffic = None
     tpath = os.path.join(ROOT, "profiles", f"traffic_{case.name}.json")
+    src_hash = kernel_source_hash()
     if os.path.exists(tpath):
         with open(tpath) as f:
             t = json.load(f)
         launch = t.get("launch", {})
-        if (args.format == "tiled-csl" and t.get("kernel_source_hash") == kernel_source_hash() and launch.get("splits") == split
+        if (args.format == "tiled-csl" and t.get("kernel_source_hash") == src_hash and launch.get("splits") == split
                 and launch.get("reg_vectors") == info["reg_vectors"]):
             traffic = t.get("hbm_bytes_per_launch")
 
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "stream_frac": round(achieved / stream["gbs"], 4) if stream else None,
+                "kernel": "lscd_spmm" + (" (product kernel + split-K pass)" if split > 1 else " (product kernel)"),
+                "bytes_per_launch": alg_bytes, "kernel_source_hash": src_hash,
+                "kernel_us_mean": round(ts.dev_mean * 1e3, 2),
+                "timing": "eager, event pair per call" if args.eager else
+                          "one HIP graph replay of the timed steps, event pair on its stream around it"}
+    if ts.pct:
+        roofline.update({"kernel_us_p10": round(ts.pct[0] * 1e3, 2), "kernel_us_p50": round(ts.pct[1] * 1e3, 2),
+                         "kernel_us_p90": round(ts.pct[2] * 1e3, 2)})
+    else:
+        roofline["replay_means_us"] = [round(x * 1e3, 2) for x in ts.spread]
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
+        "warmup": args.warmup, "ms_per_step": round(ts.wall, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f16", "data": "synthetic",
         "config": {"workload": case.name, "format": args.format, "M": M, "K": K, "N": N,
                    "sparsity": round(case.sparsity, 4),
                    "nnz": nnz, "tile": f"{info['tile_m']}x{info['tile_k']}", "splits": split,
-                   "variant": ["shared-B", "independent-4", "independent-8", "wide", "bitmap", "three-level"][variant_id],
+                   "variant": VARIANTS[variant_id],
                    "copies_rotated": copies, "gpu": props.name, "cus": props.multi_processor_count},
-        "tflops": round(flops / (ms_step * 1e-3) / 1e12, 2),
+        "tflops": round(flops / (ts.wall * 1e-3) / 1e12, 2),
         "pct_roofline": round(100 * value / HBM_PEAK_GBS, 1),
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": "lscd_spmm" + (" (product kernel + split-K pass)" if split > 1 else " (product kernel)"),
-                     "bytes_per_launch": alg_bytes, "kernel_source_hash": kernel_source_hash(),
-                     "kernel_us_mean": round(ev_mean * 1e3, 2), "kernel_us_p50": round(ev_med * 1e3, 2),
-                     "timing": "eager, event pair per call" if args.eager else
-                               "one HIP graph replay of the timed steps, event pair around it"},
+        "roofline": roofline,
+        "stream_ref": stream,
         "dense_hipblaslt": dense,
         "cpu_baseline": cpu,
     }

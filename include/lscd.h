@@ -293,10 +293,13 @@ lscd_status_t lscd_linear(lscd_handle_t h, const void* B, void* C, int32_t N, vo
  * this handle at width N (the comparison the pages make against the vendor dense library,
  * Flash-LLM review section 6) and keep the fastest for lscd_linear's dense path.  B (N x K)
  * and C (N x M) are caller device buffers as for lscd_spmm; C is overwritten.  Each candidate
- * runs 3 times untimed and 20 times back to back between two events on the default stream;
- * *best_us receives the fastest mean time per GEMM, *candidates how many were timed.
- * Synchronous.  Needs lscd_attach_dense first (NOT_SUPPORTED otherwise); allocates a 64 MiB
- * workspace on its first call, freed by lscd_destroy.
+ * runs twice untimed, then 7 times, each run alone between two events on the default stream
+ * after a 768 MiB buffer has been overwritten (three times the Infinity Cache, so the dense
+ * weights come from HBM as in a model's layer loop, not from the cache); its time is the
+ * median of the 7.  *best_us receives the fastest candidate's time per GEMM, *candidates how
+ * many were timed.  Synchronous.  Needs lscd_attach_dense first (NOT_SUPPORTED otherwise);
+ * allocates a 64 MiB workspace on its first call, freed by lscd_destroy, and the 768 MiB
+ * buffer for the duration of the call.
  */
 lscd_status_t lscd_tune_dense(lscd_handle_t h, const void* B, void* C, int32_t N, double* best_us,
                               int32_t* candidates);
@@ -325,6 +328,20 @@ lscd_status_t lscd_set_linear_crossover(lscd_handle_t h, int32_t n_max_sparse);
  */
 lscd_status_t lscd_linear_model(int64_t M, int64_t K, int64_t nnz_padded, int64_t num_tiles, int32_t N,
                                 double* t_sparse_us, double* t_dense_us);
+
+/*
+ * lscd_stream_read -- measurement reference, not part of the product: read `bytes` bytes of
+ * device memory at `src` (16-byte aligned; bytes rounded down to a multiple of 16) with the
+ * product kernels' own 128-bit non-temporal buffer loads and no other work, in
+ * `blocks_per_cu` x CUs workgroups of 256 threads, each streaming one contiguous range.  It
+ * tells how fast this GPU streams a buffer of that size from HBM -- the ceiling a memory-bound
+ * kernel of the same byte count can approach (Flash-LLM review, section 4: the skinny product
+ * is bound by global-memory bandwidth).  `sink` is a 4-byte device buffer that is written only
+ * in the rare case the XOR of everything read equals a fixed key.  Asynchronous on `stream`;
+ * no allocation.  INVALID_VALUE for a null or misaligned pointer or blocks_per_cu outside
+ * 1..64.
+ */
+lscd_status_t lscd_stream_read(const void* src, int64_t bytes, int32_t blocks_per_cu, void* sink, void* stream);
 
 /* lscd_destroy -- free the handle and its device buffers; NULL is a no-op.  The caller
  * must make sure no work using the handle is still running. */

@@ -24,10 +24,13 @@ What it computes, from the Flash-LLM pages:
   section "Problematica": one bit per position instead of per-entry positions): per
   tile, 64 lane masks whose bits follow the matrix-core operand layout, then the kept
   values chunk by chunk.
+* `loop` -- the same decode and product written again as plain C loops
+  (`spmm_loop.c`: the fp64 triple loop with k ascending, OpenMP over rows), pinned
+  to the modules above and timed as the CPU baseline.
 * `accounting` -- the compute-intensity formula and the byte/flop counts used
   for effective bandwidth (same review, section 3 "core formulas").
 
 Readings of points the pages leave open (bit order of a word, offset units,
 padding, output rounding) are stated in the module that takes them.
 """
-from . import accounting, bitmap, spmm, tiled_csl  # noqa: F401
+from . import accounting, bitmap, loop, spmm, tiled_csl  # noqa: F401

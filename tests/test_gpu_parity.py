@@ -168,6 +168,20 @@ def test_edge_cases():
     assert ei.value.status == L.LSCD_ERROR_NOT_SUPPORTED
 
 
+def test_allocation_failure_is_a_status():
+    """The allocation-failure hook makes handle creation report OUT_OF_MEMORY (nothing is left
+    allocated: the sanitizer build of the host code checks the same path for leaks), and a
+    later encode succeeds."""
+    case = syn.random_case(130, 200, 8, 0.3, seed=15)
+    for enc in (L.lscd_encode, L.lscd_encode_bitmap, L.lscd_encode_three_level):
+        with env(LSCD_TEST_FAIL_ALLOC="1"):
+            with pytest.raises(L.LSCDError) as ei:
+                enc(case.A16, case.mask)
+        assert ei.value.status == L.LSCD_ERROR_OUT_OF_MEMORY
+    h = L.lscd_encode(case.A16, case.mask)
+    assert_gates(run_spmm(h, case.B16, 130), osp.spmm_f64(case.A16, case.mask, case.B16), "after the failures")
+
+
 def test_other_stream_and_graph_replay():
     case = syn.random_case(900, 1500, 24, 0.3, seed=14)
     h = L.lscd_encode(case.A16, case.mask)

@@ -154,3 +154,31 @@ def test_split_plan_low_fill_doubles():
     C64 = osp.spmm_f64(A16, mask, B16, rows=rows)
     assert np.abs(C64).max() < 65504
     assert np.array_equal(C.cpu().numpy().view(np.uint16)[:, rows], osp.fp16_rne(C64))
+
+
+def _inflate(words, offs, reps):
+    """Every tile's words repeated `reps` times: duplicates with the same bits are valid padding
+    (a word placed twice lands on the same position with the same value)."""
+    w2, o2 = [], [0]
+    for t in range(len(offs) - 1):
+        tile = words[offs[t]:offs[t + 1]]
+        w2.append(np.tile(tile, reps))
+        o2.append(o2[-1] + reps * len(tile))
+    return np.concatenate(w2).astype(np.uint32), np.array(o2, dtype=np.uint32)
+
+
+@pytest.mark.parametrize("tm", [64, 128])
+@pytest.mark.parametrize("N", [16, 64, 128, 256])
+def test_words_past_every_register_stage(tm, N):
+    """Dense tiles whose words are repeated so that a tile holds more words than any register
+    stage (64-row tiles: 8192 words; 128-row tiles: 16384 words): the tail loops of the skinny
+    and N > 64 kernels place the rest, and the integer product stays bit-exact."""
+    case = syn.random_case(200, 150, N, 1.0, seed=77 + tm + N, values="int3")
+    w, o = L.lscd_pack(case.A16, case.mask, tm, 64)
+    w2, o2 = _inflate(w, o, 2)
+    assert int(np.diff(o2).max()) > 4 * 256 * (4 if tm == 64 else 8)
+    h = L.lscd_import(w2, o2, case.M, case.K, tm, 64)
+    say(f"inflated tm={tm} N={N} max_tile_words={h.info['max_tile_words']} variant={h.info['variant']} "
+        f"Rw={h.info['reg_vectors_wide']}")
+    C = run(L.lscd_spmm, h, case.B16, case.M)
+    assert np.array_equal(C, osp.fp16_rne(osp.spmm_f64(case.A16, case.mask, case.B16)))

@@ -38,7 +38,7 @@ EXPORTS = ("lscd_pack_size", "lscd_pack", "lscd_default_tile_m", "lscd_encode", 
            "lscd_import", "lscd_export",
            "lscd_get_info", "lscd_spmm", "lscd_debug_decode", "lscd_attach_dense", "lscd_linear",
            "lscd_linear_path", "lscd_set_linear_crossover", "lscd_linear_model", "lscd_tune_dense", "lscd_destroy",
-           "lscd_status_string")
+           "lscd_status_string", "lscd_stream_read")
 
 
 class lscd_info_t(ctypes.Structure):
@@ -89,6 +89,7 @@ def _load():
         "lscd_linear_model": [I64, I64, I64, I64, I32, P(ctypes.c_double), P(ctypes.c_double)],
         "lscd_tune_dense": [VP, VP, VP, I32, P(ctypes.c_double), P(I32)],
         "lscd_destroy": [VP],
+        "lscd_stream_read": [VP, I64, I32, VP, VP],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -346,6 +347,17 @@ def lscd_debug_decode(h: Handle, A_dense, stream=None):
     pa = _device_fp16(A_dense, "A_dense", (info["M"], info["K"]))
     _check(_lib.lscd_debug_decode(ctypes.c_void_p(h.ptr), pa, _stream(stream)), "lscd_debug_decode")
     return A_dense
+
+
+def lscd_stream_read(src, nbytes: int, blocks_per_cu: int, sink, stream=None):
+    """Measurement reference: stream `nbytes` of the device tensor `src` with the product's loads
+    (see include/lscd.h); `sink` is a device tensor of at least 4 bytes."""
+    if not (isinstance(src, torch.Tensor) and src.is_cuda and isinstance(sink, torch.Tensor) and sink.is_cuda):
+        raise ValueError("src and sink must be CUDA tensors")
+    if nbytes > src.numel() * src.element_size() or sink.numel() * sink.element_size() < 4:
+        raise ValueError("buffer too small")
+    _check(_lib.lscd_stream_read(ctypes.c_void_p(src.data_ptr()), int(nbytes), int(blocks_per_cu),
+                                 ctypes.c_void_p(sink.data_ptr()), _stream(stream)), "lscd_stream_read")
 
 
 def lscd_destroy(h: Handle):

@@ -19,8 +19,14 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "liblscd.so")
 BUILD_DIR = os.path.join(HERE, "_build")
-SOURCES = ["csrc/lscd_api.cpp", "csrc/lscd_linear.cpp", "csrc/lscd_pack.cpp", "csrc/lscd_kernels.hip",
-           "csrc/lscd_encode_dev.hip"]
+# The kernel families are separate translation units so that they compile in parallel.
+SOURCES = ["csrc/lscd_skinny64.hip", "csrc/lscd_skinny32.hip", "csrc/lscd_skinny16.hip", "csrc/lscd_three_level.hip",
+           "csrc/lscd_bitmap.hip", "csrc/lscd_wide.hip", "csrc/lscd_kernels.hip", "csrc/lscd_encode_dev.hip",
+           "csrc/lscd_api.cpp", "csrc/lscd_linear.cpp", "csrc/lscd_pack.cpp"]
+# Device sources (their hash identifies the kernels that produced a committed measurement).
+DEVICE_SOURCES = ["csrc/lscd_device.h", "csrc/lscd_skinny.h", "csrc/lscd_skinny16.hip", "csrc/lscd_skinny32.hip",
+                  "csrc/lscd_skinny64.hip", "csrc/lscd_wide.hip", "csrc/lscd_bitmap.hip", "csrc/lscd_three_level.hip",
+                  "csrc/lscd_kernels.hip", "csrc/lscd_internal.h"]
 ARCH = os.environ.get("LSCD_OFFLOAD_ARCH", "gfx950")
 
 
@@ -39,20 +45,16 @@ def _flags():
                 "-I", os.path.join(ROOT, "include")]
 
 
-def build(verbose: bool = False, pkg_dir: str = HERE, defines=()) -> str:
-    """Compile the sources of `pkg_dir` (default: this package) into `pkg_dir`/liblscd.so.
-
-    `defines` are extra -D options for tuning builds (tile-loop knobs such as LSCD_WAVES).
-    """
+def build(verbose: bool = False, pkg_dir: str = HERE) -> str:
+    """Compile the sources of `pkg_dir` (default: this package) into `pkg_dir`/liblscd.so."""
     hipcc = _hipcc()
     build_dir = os.path.join(pkg_dir, "_build")
     lib = os.path.join(pkg_dir, "liblscd.so")
     os.makedirs(build_dir, exist_ok=True)
-    extra = [f"-D{d}" for d in defines]
 
     def compile_one(src):
         obj = os.path.join(build_dir, os.path.basename(src) + ".o")
-        cmd = [hipcc, *_flags(), "-I", os.path.join(pkg_dir, "csrc"), *extra, "-c", os.path.join(pkg_dir, src),
+        cmd = [hipcc, *_flags(), "-I", os.path.join(pkg_dir, "csrc"), "-c", os.path.join(pkg_dir, src),
                "-o", obj]
         if src.endswith(".cpp"):
             cmd[1:1] = ["-x", "hip"]
@@ -63,7 +65,7 @@ def build(verbose: bool = False, pkg_dir: str = HERE, defines=()) -> str:
             print(" ".join(cmd))
         return obj
 
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+    with ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
         objs = list(ex.map(compile_one, SOURCES))
     tmp = lib + ".tmp"
     rocm_lib = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "lib")

@@ -159,6 +159,33 @@ int npad_index(int N) { return N <= 16 ? 0 : (N <= 32 ? 1 : 2); }
 
 namespace lscd {
 
+// Staging registers per lane (vectors of 4 words) of the register stage, from the instantiated
+// choices; LSCD_MAX_R caps it (tests use it to force the path past the stage).
+static const int kRegChoices[] = {2, 3, 4, 5, 6, 8, 10, 12, 16};
+
+int pick_reg_vectors(int32_t max_tile_words) {
+    const int need = ((max_tile_words / 4) + 63) / 64;
+    int cap = 16;
+    if (const char* e = getenv("LSCD_MAX_R")) cap = atoi(e) > 0 ? atoi(e) : 16;
+    int best = 2;
+    for (int r : kRegChoices) {
+        if (r > cap) break;
+        best = r;
+        if (r >= need) break;
+    }
+    return best;
+}
+
+int pick_reg_vectors_tall(int32_t max_tile_words) {
+    const int r = pick_reg_vectors(max_tile_words);
+    return r <= 4 ? 4 : (r <= 6 ? 6 : (r >= 12 ? 12 : r));
+}
+
+int pick_reg_vectors_wide(int32_t max_tile_words) {
+    const int need = ((max_tile_words / 4) + kThreads - 1) / kThreads;
+    return need <= 1 ? 1 : (need <= 2 ? 2 : (need <= 4 ? 4 : 8));
+}
+
 // A handle for grid g with its kernel plan (variants, K splits) and split-K workspace; the
 // caller supplies the encoding buffers.
 lscd_status_t new_handle(const Grid& g, int64_t nnz, int64_t nwords, int32_t maxw, lscd_handle_s** out, int format) {
@@ -210,7 +237,8 @@ lscd_status_t new_handle(const Grid& g, int64_t nnz, int64_t nwords, int32_t max
         h->kind[i] = tall ? (i < 2 ? kKernelIndep8 : kKernelShared) : pick_kind(16 << i);
         const int occ = spmm_blocks_per_cu(h->kind[i], 16 << i, h->R, (int)std::min<int64_t>(g.K, 1 << 30), g.tm);
         const int min_tiles = h->kind[i] == kKernelIndep ? 8 : (h->kind[i] == kKernelIndep8 ? 16 : 2);
-        h->S[i] = plan_splits(g, h->cus, occ, row_groups(g, h->kind[i]), min_tiles, h->kind[i] != kKernelShared, true);
+        const bool indep = h->kind[i] == kKernelIndep || h->kind[i] == kKernelIndep8;
+        h->S[i] = plan_splits(g, h->cus, occ, row_groups(g, h->kind[i]), min_tiles, indep, true);
         if (h->S[i] > 1) part = std::max<int64_t>(part, (int64_t)h->S[i] * g.M * (16 << i) * 4);
     }
     h->Rw = pick_reg_vectors_wide(maxw);
@@ -639,7 +667,15 @@ lscd_status_t lscd_get_info(lscd_handle_t h, lscd_info_t* info) {
     return LSCD_SUCCESS;
 }
 
-lscd_status_t lscd_spmm(lscd_handle_t h, const void* B, void* C, int32_t N, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The product behind lscd_spmm: `part` receives the fp32 partial sums of
+// K-split launches and holds `part_bytes`; a launch whose partials would not fit is refused
+// with NOT_SUPPORTED before anything is launched.
+lscd_status_t spmm_impl(lscd_handle_t h, const void* B, void* C, int32_t N, void* stream, float* part,
+                        int64_t part_bytes) {
     if (!h || N < 0) return LSCD_ERROR_INVALID_VALUE;
     if (N == 0) return LSCD_SUCCESS;
     if (!B || !C || !aligned16(B) || !aligned16(C)) return LSCD_ERROR_INVALID_VALUE;
@@ -653,7 +689,7 @@ lscd_status_t lscd_spmm(lscd_handle_t h, const void* B, void* C, int32_t N, void
     lscd::SpmmArgs a;
     a.words = h->d_words;
     a.offs = h->d_offs;
-    a.part = h->d_part;
+    a.part = part;
     a.M = (int32_t)h->g.M;
     a.K = (int32_t)h->g.K;
     a.MB = (int32_t)h->g.MB;
@@ -671,6 +707,7 @@ lscd_status_t lscd_spmm(lscd_handle_t h, const void* B, void* C, int32_t N, void
             a.S = h->S[npad_index(n)];
             a.items = a.G * a.S;
             a.per_xcd = (a.items + 7) / 8;
+            if (a.S > 1 && (int64_t)a.S * a.N * h->g.M * 4 > part_bytes) return LSCD_ERROR_NOT_SUPPORTED;
             hipError_t e = lscd::launch_spmm(lscd::kKernelBitmap, npad, 0, a, 8 * a.per_xcd, s);
             if (e != hipSuccess) return hip_status(e);
             if (a.S > 1) {
@@ -692,6 +729,7 @@ lscd_status_t lscd_spmm(lscd_handle_t h, const void* B, void* C, int32_t N, void
             a.S = h->S[npad_index(n)];
             a.items = a.G * a.S;
             a.per_xcd = (a.items + 7) / 8;
+            if (a.S > 1 && (int64_t)a.S * a.N * h->g.M * 4 > part_bytes) return LSCD_ERROR_NOT_SUPPORTED;
             hipError_t e = lscd::launch_spmm(lscd::kKernelThreeLevel, npad, 0, a, 8 * a.per_xcd, s);
             if (e != hipSuccess) return hip_status(e);
             if (a.S > 1) {
@@ -725,6 +763,7 @@ lscd_status_t lscd_spmm(lscd_handle_t h, const void* B, void* C, int32_t N, void
         a.S = S;
         a.items = a.G * a.S;
         a.per_xcd = (a.items + 7) / 8;
+        if (a.S > 1 && (int64_t)a.S * a.N * h->g.M * 4 > part_bytes) return LSCD_ERROR_NOT_SUPPORTED;
         hipError_t e = lscd::launch_spmm(kind, npad, R, a, 8 * a.per_xcd, s);
         if (e != hipSuccess) return hip_status(e);
         if (S > 1) {
@@ -733,6 +772,14 @@ lscd_status_t lscd_spmm(lscd_handle_t h, const void* B, void* C, int32_t N, void
         }
     }
     return LSCD_SUCCESS;
+}
+
+}  // namespace
+
+extern "C" {
+
+lscd_status_t lscd_spmm(lscd_handle_t h, const void* B, void* C, int32_t N, void* stream) {
+    return spmm_impl(h, B, C, N, stream, h ? h->d_part : nullptr, h ? h->part_bytes : 0);
 }
 
 lscd_status_t lscd_debug_decode(lscd_handle_t h, void* A_dense, void* stream) {
@@ -754,6 +801,16 @@ lscd_status_t lscd_debug_decode(lscd_handle_t h, void* A_dense, void* stream) {
     if (h->format == 1) return hip_status(lscd::launch_decode_bitmap(a, (int)grid, (hipStream_t)stream));
     if (h->format == 2) return hip_status(lscd::launch_decode_three_level(a, (int)grid, (hipStream_t)stream));
     return hip_status(lscd::launch_decode(h->R, a, (int)grid, (hipStream_t)stream));
+}
+
+lscd_status_t lscd_stream_read(const void* src, int64_t bytes, int32_t blocks_per_cu, void* sink, void* stream) {
+    if (!src || !sink || !aligned16(src) || ((uintptr_t)sink & 3u) || bytes < 0 || blocks_per_cu < 1 ||
+        blocks_per_cu > 64)
+        return LSCD_ERROR_INVALID_VALUE;
+    const int cus = current_cus();
+    if (cus < 0) return LSCD_ERROR_HIP;
+    return hip_status(lscd::launch_stream_read(src, bytes & ~(int64_t)15, cus * blocks_per_cu, (uint32_t*)sink,
+                                               (hipStream_t)stream));
 }
 
 lscd_status_t lscd_destroy(lscd_handle_t h) {

@@ -16,10 +16,7 @@ namespace lscd {
 constexpr int kTileM = 64;
 constexpr int kTileK = 64;
 // Wavefronts per workgroup; each owns one row block, all share the staged B tile.
-#ifndef LSCD_WAVES
-#define LSCD_WAVES 4
-#endif
-constexpr int kWaves = LSCD_WAVES;
+constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 
 // ---------------------------------------------------------------- host encoder
@@ -136,10 +133,20 @@ hipError_t launch_decode_bitmap(const DecodeArgs& a, int grid, hipStream_t s);
 // Staging registers per thread and tile of the wide variant (1, 2 or 4).
 int pick_reg_vectors_wide(int32_t max_tile_words);
 hipError_t launch_spmm(int kind, int npad, int R, const SpmmArgs& a, int grid, hipStream_t s);
+// Per-family launch tables (one source file each, compiled in parallel).  occ != nullptr:
+// report resident workgroups per CU in *occ instead of launching.
+hipError_t launch_kind_skinny16(int kind, int R, const SpmmArgs& a, int grid, hipStream_t s, int* occ);
+hipError_t launch_kind_skinny32(int kind, int R, const SpmmArgs& a, int grid, hipStream_t s, int* occ);
+hipError_t launch_kind_skinny64(int kind, int R, const SpmmArgs& a, int grid, hipStream_t s, int* occ);
+hipError_t launch_kind_wide(int npad, int R, const SpmmArgs& a, int grid, hipStream_t s, int* occ);
+hipError_t launch_kind_bitmap(int npad, const SpmmArgs& a, int grid, hipStream_t s, int* occ);
+hipError_t launch_kind_three_level(int npad, const SpmmArgs& a, int grid, hipStream_t s, int* occ);
 // Workgroups of a product kernel (variant, N padding, stage size) resident per CU.
 int spmm_blocks_per_cu(int kind, int npad, int R, int K, int TM = kTileM);
 hipError_t launch_reduce(const float* part, uint16_t* C, int S, int64_t NM, hipStream_t s);
 hipError_t launch_decode(int R, const DecodeArgs& a, int grid, hipStream_t s);
+// Streaming-read reference over `bytes` (a multiple of 16) with `blocks` workgroups.
+hipError_t launch_stream_read(const void* src, int64_t bytes, int blocks, uint32_t* sink, hipStream_t s);
 
 // A new handle for grid g: kernel plan, split-K workspace; d_words / d_offs left null for
 // the caller to fill.  delete_handle frees a handle and every buffer it holds.
