@@ -260,6 +260,22 @@ lscd_status_t lscd_get_info(lscd_handle_t h, lscd_info_t* info);
 lscd_status_t lscd_spmm(lscd_handle_t h, const void* B, void* C, int32_t N, void* stream);
 
 /*
+ * lscd_spmm_noalloc -- lscd_spmm for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same arguments,
+ * layouts, kernels, plan and result (bit-identical to lscd_spmm on the same handle), but the
+ * fp32 partial sums of K-split launches go to a static device array of the library, 64 MiB
+ * per GPU (allocated with the library's code on each device it runs on and held until the
+ * process ends), not to the handle's workspace.  Allocates nothing and calls no allocating
+ * routine; the first call on a device looks up that device's copy of the array.
+ * Errors: those of lscd_spmm, plus NOT_SUPPORTED when one launch's partials (splits x N x M x
+ * 4 bytes, at most 256 columns per launch) exceed 64 MiB.  The array is shared by every call
+ * on that GPU and keeps the last call's contents (each launch writes every partial it reads,
+ * so nothing needs clearing): calls that overlap on one GPU -- on different streams, or from
+ * different threads -- race and must be serialized by the caller.
+ */
+lscd_status_t lscd_spmm_noalloc(lscd_handle_t h, const void* B, void* C, int32_t N, void* stream);
+
+/*
  * lscd_debug_decode -- write the dense M x K fp16 matrix the handle encodes into the
  * device buffer A_dense (row-major, 16-byte aligned), on `stream`.  Uses the same
  * load-and-extract device code as lscd_spmm, so it shows exactly what the product

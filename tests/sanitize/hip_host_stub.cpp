@@ -64,6 +64,7 @@ hipError_t encode_device_fill(const uint16_t*, const uint8_t*, const Grid&, cons
     return hipErrorNoDevice;
 }
 int spmm_blocks_per_cu(int, int, int, int, int) { return 2; }
+hipError_t scratch_partials(int, float**) { return hipErrorNoDevice; }
 void release_dense(struct ::lscd_handle_s*) {}
 
 }  // namespace lscd

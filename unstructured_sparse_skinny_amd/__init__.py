@@ -38,7 +38,7 @@ EXPORTS = ("lscd_pack_size", "lscd_pack", "lscd_default_tile_m", "lscd_encode", 
            "lscd_import", "lscd_export",
            "lscd_get_info", "lscd_spmm", "lscd_debug_decode", "lscd_attach_dense", "lscd_linear",
            "lscd_linear_path", "lscd_set_linear_crossover", "lscd_linear_model", "lscd_tune_dense", "lscd_destroy",
-           "lscd_status_string", "lscd_stream_read")
+           "lscd_status_string", "lscd_stream_read", "lscd_spmm_noalloc")
 
 
 class lscd_info_t(ctypes.Structure):
@@ -90,6 +90,7 @@ def _load():
         "lscd_tune_dense": [VP, VP, VP, I32, P(ctypes.c_double), P(I32)],
         "lscd_destroy": [VP],
         "lscd_stream_read": [VP, I64, I32, VP, VP],
+        "lscd_spmm_noalloc": [VP, VP, VP, I32, VP],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -294,6 +295,17 @@ def lscd_spmm(h: Handle, B, C, stream=None):
     pb = _device_fp16(B, "B", (N, info["K"]))
     pc = _device_fp16(C, "C", (N, info["M"]))
     _check(_lib.lscd_spmm(ctypes.c_void_p(h.ptr), pb, pc, N, _stream(stream)), "lscd_spmm")
+    return C
+
+
+def lscd_spmm_noalloc(h: Handle, B, C, stream=None):
+    """lscd_spmm with its split-K partial sums in the library's static per-GPU array instead of
+    the handle's workspace (for callers that cannot allocate; calls on one GPU must not overlap)."""
+    info = lscd_get_info(h)
+    N = int(B.shape[0]) if isinstance(B, torch.Tensor) and B.dim() == 2 else -1
+    pb = _device_fp16(B, "B", (N, info["K"]))
+    pc = _device_fp16(C, "C", (N, info["M"]))
+    _check(_lib.lscd_spmm_noalloc(ctypes.c_void_p(h.ptr), pb, pc, N, _stream(stream)), "lscd_spmm_noalloc")
     return C
 
 

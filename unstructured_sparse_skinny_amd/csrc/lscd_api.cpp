@@ -671,7 +671,7 @@ lscd_status_t lscd_get_info(lscd_handle_t h, lscd_info_t* info) {
 
 namespace {
 
-// The product behind lscd_spmm: `part` receives the fp32 partial sums of
+// The product behind lscd_spmm and lscd_spmm_noalloc: `part` receives the fp32 partial sums of
 // K-split launches and holds `part_bytes`; a launch whose partials would not fit is refused
 // with NOT_SUPPORTED before anything is launched.
 lscd_status_t spmm_impl(lscd_handle_t h, const void* B, void* C, int32_t N, void* stream, float* part,
@@ -780,6 +780,17 @@ extern "C" {
 
 lscd_status_t lscd_spmm(lscd_handle_t h, const void* B, void* C, int32_t N, void* stream) {
     return spmm_impl(h, B, C, N, stream, h ? h->d_part : nullptr, h ? h->part_bytes : 0);
+}
+
+lscd_status_t lscd_spmm_noalloc(lscd_handle_t h, const void* B, void* C, int32_t N, void* stream) {
+    if (!h || N < 0) return LSCD_ERROR_INVALID_VALUE;
+    if (N == 0) return LSCD_SUCCESS;
+    lscd_status_t st = check_device(h);
+    if (st != LSCD_SUCCESS) return st;
+    float* part = nullptr;
+    hipError_t e = lscd::scratch_partials(h->device, &part);
+    if (e != hipSuccess) return hip_status(e);
+    return spmm_impl(h, B, C, N, stream, part, lscd::kScratchBytes);
 }
 
 lscd_status_t lscd_debug_decode(lscd_handle_t h, void* A_dense, void* stream) {

@@ -145,6 +145,11 @@ hipError_t launch_kind_three_level(int npad, const SpmmArgs& a, int grid, hipStr
 int spmm_blocks_per_cu(int kind, int npad, int R, int K, int TM = kTileM);
 hipError_t launch_reduce(const float* part, uint16_t* C, int S, int64_t NM, hipStream_t s);
 hipError_t launch_decode(int R, const DecodeArgs& a, int grid, hipStream_t s);
+// Partial-sum scratch of lscd_spmm_noalloc: a file-scope device array of kScratchBytes, one
+// per GPU, held until the process ends.  scratch_partials returns its address on `device`
+// (looked up once per device, then cached).
+constexpr int64_t kScratchBytes = (int64_t)64 << 20;
+hipError_t scratch_partials(int device, float** ptr);
 // Streaming-read reference over `bytes` (a multiple of 16) with `blocks` workgroups.
 hipError_t launch_stream_read(const void* src, int64_t bytes, int blocks, uint32_t* sink, hipStream_t s);
 

@@ -4,6 +4,9 @@
 
 #include <stdlib.h>
 
+#include <mutex>
+#include <vector>
+
 #include "lscd_device.h"
 
 namespace lscd {
@@ -172,6 +175,31 @@ hipError_t launch_reduce(const float* part, uint16_t* C, int S, int64_t NM, hipS
     if (blocks < 1) blocks = 1;
     hipLaunchKernelGGL(reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, st, part, C, S, NM);
     return hipGetLastError();
+}
+
+// The partial sums of lscd_spmm_noalloc live here instead of in a handle's workspace.  In host
+// code `scratch` names a host-side stand-in, not device memory: only the address that
+// hipGetSymbolAddress returns for the current device may be handed to kernels or copies.
+static __device__ __align__(256) float scratch[kScratchBytes / 4];
+
+hipError_t scratch_partials(int device, float** ptr) {
+    static std::mutex mu;
+    static std::vector<float*> addr;  // per device, filled on first use
+    std::lock_guard<std::mutex> lock(mu);
+    if (device < 0) return hipErrorInvalidDevice;
+    if ((size_t)device >= addr.size()) addr.resize((size_t)device + 1, nullptr);
+    if (!addr[(size_t)device]) {
+        int cur = -1;
+        hipError_t e = hipGetDevice(&cur);
+        if (e != hipSuccess) return e;
+        if (cur != device) return hipErrorInvalidDevice;
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        addr[(size_t)device] = (float*)p;
+    }
+    *ptr = addr[(size_t)device];
+    return hipSuccess;
 }
 
 hipError_t launch_stream_read(const void* src, int64_t bytes, int blocks, uint32_t* sink, hipStream_t st) {
