@@ -309,13 +309,13 @@ lscd_status_t lscd_linear(lscd_handle_t h, const void* B, void* C, int32_t N, vo
  * this handle at width N (the comparison the pages make against the vendor dense library,
  * Flash-LLM review section 6) and keep the fastest for lscd_linear's dense path.  B (N x K)
  * and C (N x M) are caller device buffers as for lscd_spmm; C is overwritten.  Each candidate
- * runs twice untimed, then 7 times, each run alone between two events on the default stream
- * after a 768 MiB buffer has been overwritten (three times the Infinity Cache, so the dense
- * weights come from HBM as in a model's layer loop, not from the cache); its time is the
- * median of the 7.  *best_us receives the fastest candidate's time per GEMM, *candidates how
- * many were timed.  Synchronous.  Needs lscd_attach_dense first (NOT_SUPPORTED otherwise);
- * allocates a 64 MiB workspace on its first call, freed by lscd_destroy, and the 768 MiB
- * buffer for the duration of the call.
+ * runs twice untimed, then 20 times back to back between two events on the default stream,
+ * rotating over copies of the dense matrix whose total exceeds three times the 256 MiB
+ * Infinity Cache (2 to 8 copies), so the weights come from HBM as in a model's layer loop
+ * rather than from the cache.  *best_us receives the fastest candidate's mean time per GEMM,
+ * *candidates how many were timed.  Synchronous.  Needs lscd_attach_dense first (NOT_SUPPORTED
+ * otherwise); allocates a 64 MiB workspace on its first call, freed by lscd_destroy, and the
+ * extra copies (1 to 7 times M*K*2 bytes) for the duration of the call.
  */
 lscd_status_t lscd_tune_dense(lscd_handle_t h, const void* B, void* C, int32_t N, double* best_us,
                               int32_t* candidates);

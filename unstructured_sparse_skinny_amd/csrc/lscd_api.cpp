@@ -30,7 +30,10 @@ void free_handle(lscd_handle_s* h) {
     delete h;
 }
 
-// Number of K splits for one N padding.  LSCD_SPLITK overrides (tuning only).
+// Encodings below this size run without K splits (one launch; see plan_splits).
+constexpr int64_t kSmallFormatBytes = (int64_t)16 << 20;
+
+// Number of K splits for one N padding.  LSCD_SPLITK overrides (tests and tuning).
 //
 // Independent-wavefront variants (one workgroup per row block and split): each work item is
 // 1/S of a row block's k range, and a CU ends up with ceil(groups * S / CUs) of them, so the
@@ -43,12 +46,17 @@ void free_handle(lscd_handle_s* h) {
 // Shared-B variant: as many workgroups as the GPU holds at once (CUs x resident workgroups
 // per CU, from the kernel's real occupancy), so the whole grid runs in a single wave.
 int plan_splits(const Grid& g, int cus, int blocks_per_cu, int64_t groups, int tiles_per_split_min, bool indep,
-                bool widen_low_fill = false) {
+                bool widen_low_fill = false, int64_t format_bytes = -1) {
     int64_t S = 1;
     const int64_t smax = std::max<int64_t>(1, std::min<int64_t>(g.KT / tiles_per_split_min, 64));
     const char* e = getenv("LSCD_SPLITK");
     if (e && atoll(e) > 0) {
         S = atoll(e);
+    } else if (format_bytes >= 0 && format_bytes < kSmallFormatBytes) {
+        // A product this small is bound by launch latency, not by how its tiles spread over the
+        // CUs: a second (reduction) launch costs more than a split can save.  Measured on
+        // 1024 x 1024 at 80 % sparsity, N = 8: 6.7 us with 2 splits, 6.2 us with one launch.
+        S = 1;
     } else if (indep) {
         // at most 4: measured on OPT-175B QKV (80-row tiles), 6 splits cost 22 % over 1
         // although the count above favours them -- each split adds a pipeline start-up and
@@ -238,7 +246,7 @@ lscd_status_t new_handle(const Grid& g, int64_t nnz, int64_t nwords, int32_t max
         const int occ = spmm_blocks_per_cu(h->kind[i], 16 << i, h->R, (int)std::min<int64_t>(g.K, 1 << 30), g.tm);
         const int min_tiles = h->kind[i] == kKernelIndep ? 8 : (h->kind[i] == kKernelIndep8 ? 16 : 2);
         const bool indep = h->kind[i] == kKernelIndep || h->kind[i] == kKernelIndep8;
-        h->S[i] = plan_splits(g, h->cus, occ, row_groups(g, h->kind[i]), min_tiles, indep, true);
+        h->S[i] = plan_splits(g, h->cus, occ, row_groups(g, h->kind[i]), min_tiles, indep, true, 4 * nwords);
         if (h->S[i] > 1) part = std::max<int64_t>(part, (int64_t)h->S[i] * g.M * (16 << i) * 4);
     }
     h->Rw = pick_reg_vectors_wide(maxw);

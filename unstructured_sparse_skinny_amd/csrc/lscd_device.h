@@ -289,6 +289,37 @@ __device__ __forceinline__ void mma_rows(f32x4 (&acc)[RG][NPAD / 16], const unsi
     }
 }
 
+// The same product with every operand read issued before the first MFMA: all 2 * (RG + NPAD/16)
+// 16-byte LDS reads of the tile are in flight together and the MFMAs then run back to back,
+// instead of each MFMA waiting out the latency of its own A read (the compiler, left to
+// itself, keeps one or two reads ahead).  Costs 8 * (RG + NPAD/16) VGPRs; for kernels whose
+// occupancy the LDS already bounds.
+template <int NPAD, int RG>
+__device__ __forceinline__ void mma_rows_prefetched(f32x4 (&acc)[RG][NPAD / 16], const unsigned char* As,
+                                                    const unsigned char* Bs, int lane) {
+    const uint32_t rl = lane & 15, kq = lane >> 4;
+    half8 bf[2][NPAD / 16];
+    half8 af[2][RG];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+        for (int j = 0; j < NPAD / 16; ++j)
+            bf[ks][j] = *reinterpret_cast<const half8*>(Bs + lds_chunk(j * 16 + rl, ks * 4 + kq));
+#pragma unroll
+        for (int i = 0; i < RG; ++i)
+            af[ks][i] = *reinterpret_cast<const half8*>(As + lds_chunk(i * 16 + rl, ks * 4 + kq));
+    }
+    // nothing moves across this point: the scheduler would otherwise sink each read to its MFMA
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int i = 0; i < RG; ++i)
+#pragma unroll
+            for (int j = 0; j < NPAD / 16; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[ks][i], bf[ks][j], acc[i][j], 0, 0, 0);
+}
+
 // acc[i][j] += A rows 16i..16i+15 (x 64 k) times B columns 16j..16j+15.
 template <int NPAD>
 __device__ __forceinline__ void mma_tile(f32x4 (&acc)[4][NPAD / 16], const unsigned char* As,

@@ -96,11 +96,11 @@ struct LtProblem {
     }
 };
 
-hipblasStatus_t lt_run(const lscd_handle_s* h, LtState* lt, LtProblem& pb, const hipblasLtMatmulAlgo_t* algo,
-                       const void* B, void* C, hipStream_t s) {
+hipblasStatus_t lt_run(const void* A, LtState* lt, LtProblem& pb, const hipblasLtMatmulAlgo_t* algo, const void* B,
+                       void* C, hipStream_t s) {
     const float alpha = 1.0f, beta = 0.0f;
-    return hipblasLtMatmul(lt->handle, pb.desc, &alpha, h->d_dense, pb.a, B, pb.b, &beta, C, pb.c, C, pb.c, algo,
-                           lt->ws, lt->ws_bytes, s);
+    return hipblasLtMatmul(lt->handle, pb.desc, &alpha, A, pb.a, B, pb.b, &beta, C, pb.c, C, pb.c, algo, lt->ws,
+                           lt->ws_bytes, s);
 }
 
 lscd_status_t hip_st(hipError_t e) {
@@ -235,7 +235,7 @@ lscd_status_t lscd_linear(lscd_handle_t h, const void* B, void* C, int32_t N, vo
             if (t.N != N) continue;
             LtProblem pb;
             if (!pb.make(h->g.M, h->g.K, N)) return LSCD_ERROR_HIP;
-            return lt_run(h, lt, pb, &t.algo, B, C, (hipStream_t)stream) == HIPBLAS_STATUS_SUCCESS ? LSCD_SUCCESS
+            return lt_run(h->d_dense, lt, pb, &t.algo, B, C, (hipStream_t)stream) == HIPBLAS_STATUS_SUCCESS ? LSCD_SUCCESS
                                                                                                  : LSCD_ERROR_HIP;
         }
     }
@@ -284,63 +284,68 @@ lscd_status_t lscd_tune_dense(lscd_handle_t h, const void* B, void* C, int32_t N
                                                          kLtCandidates, res, &got);
     (void)hipblasLtMatmulPreferenceDestroy(pref);
     if (hs != HIPBLAS_STATUS_SUCCESS || got < 1) return LSCD_ERROR_NOT_SUPPORTED;
-    // Timed as the GEMM runs in a model's layer loop, with its weights coming from HBM: before
-    // every timed run a 768 MiB buffer (three times the 256 MiB Infinity Cache) is overwritten,
-    // which evicts the dense copy from the cache, and the run alone sits between two events.
-    // Back-to-back runs on one copy would be served partly from the cache and flatter the GEMM.
-    // Each candidate: 2 untimed runs, then kLtTimedRuns flushed runs; its time is their median.
-    constexpr size_t kFlushBytes = (size_t)768 << 20;
-    constexpr int kLtTimedRuns = 7;
-    void* flush = nullptr;
-    hipError_t fe = hipMalloc(&flush, kFlushBytes);
-    if (fe != hipSuccess) return hip_st(fe);
-    hipEvent_t e0[kLtTimedRuns], e1[kLtTimedRuns];
-    int made = 0;
-    bool ev_ok = true;
-    for (; made < kLtTimedRuns && ev_ok; ++made) {
-        if (hipEventCreate(&e0[made]) != hipSuccess) {
-            ev_ok = false;
-            break;
+    // Timed as the GEMM runs in a model's layer loop, with its weights coming from HBM rather than
+    // from the 256 MiB Infinity Cache: back to back over rotating copies of the dense matrix
+    // (made here and freed before returning) whose total exceeds three times that cache.  One
+    // copy run back to back would be served partly from the cache and flatter the GEMM.  Each
+    // candidate: 2 untimed runs, then kLtTimedRuns between one event pair on the default stream.
+    constexpr int kLtTimedRuns = 20;
+    const size_t dense_bytes = (size_t)h->g.M * (size_t)h->g.K * 2;
+    const size_t mall = (size_t)256 << 20;
+    const int ncopies = (int)std::max<size_t>(2, std::min<size_t>(8, (3 * mall + dense_bytes - 1) / dense_bytes + 1));
+    std::vector<void*> copies(1, (void*)h->d_dense);
+    hipError_t ce = hipSuccess;
+    for (int c = 1; c < ncopies && ce == hipSuccess; ++c) {
+        void* p = nullptr;
+        ce = hipMalloc(&p, dense_bytes);
+        if (ce == hipSuccess) {
+            copies.push_back(p);
+            ce = hipMemcpy(p, h->d_dense, dense_bytes, hipMemcpyDeviceToDevice);
         }
-        if (hipEventCreate(&e1[made]) != hipSuccess) {
-            (void)hipEventDestroy(e0[made]);
-            ev_ok = false;
-            break;
-        }
+    }
+    auto free_copies = [&]() {
+        for (size_t c = 1; c < copies.size(); ++c) (void)hipFree(copies[c]);
+    };
+    if (ce != hipSuccess) {
+        free_copies();
+        return hip_st(ce);
+    }
+    hipEvent_t e0, e1;
+    if (hipEventCreate(&e0) != hipSuccess) {
+        free_copies();
+        return LSCD_ERROR_HIP;
+    }
+    if (hipEventCreate(&e1) != hipSuccess) {
+        (void)hipEventDestroy(e0);
+        free_copies();
+        return LSCD_ERROR_HIP;
     }
     double best = -1;
     int best_i = -1, tried = 0;
-    for (int i = 0; i < got && ev_ok; ++i) {
+    const int nc = (int)copies.size();
+    for (int i = 0; i < got; ++i) {
         if (res[i].state != HIPBLAS_STATUS_SUCCESS || res[i].workspaceSize > lt->ws_bytes) continue;
         bool ok = true;
-        for (int r = 0; r < 2 && ok; ++r) ok = lt_run(h, lt, pb, &res[i].algo, B, C, nullptr) == HIPBLAS_STATUS_SUCCESS;
-        for (int r = 0; r < kLtTimedRuns && ok; ++r) {
-            ok = hipMemsetAsync(flush, r & 0xFF, kFlushBytes, nullptr) == hipSuccess &&
-                 hipEventRecord(e0[r], nullptr) == hipSuccess &&
-                 lt_run(h, lt, pb, &res[i].algo, B, C, nullptr) == HIPBLAS_STATUS_SUCCESS &&
-                 hipEventRecord(e1[r], nullptr) == hipSuccess;
-        }
-        if (hipDeviceSynchronize() != hipSuccess || !ok) continue;
-        double t[kLtTimedRuns];
-        for (int r = 0; r < kLtTimedRuns; ++r) {
-            float ms = 0;
-            (void)hipEventElapsedTime(&ms, e0[r], e1[r]);
-            t[r] = 1e3 * (double)ms;
-        }
-        std::sort(t, t + kLtTimedRuns);
+        for (int r = 0; r < 2 && ok; ++r)
+            ok = lt_run(copies[r % nc], lt, pb, &res[i].algo, B, C, nullptr) == HIPBLAS_STATUS_SUCCESS;
+        if (!ok) continue;
+        (void)hipEventRecord(e0, nullptr);
+        for (int r = 0; r < kLtTimedRuns && ok; ++r)
+            ok = lt_run(copies[r % nc], lt, pb, &res[i].algo, B, C, nullptr) == HIPBLAS_STATUS_SUCCESS;
+        (void)hipEventRecord(e1, nullptr);
+        if (hipEventSynchronize(e1) != hipSuccess || !ok) continue;
+        float ms = 0;
+        (void)hipEventElapsedTime(&ms, e0, e1);
         ++tried;
-        const double us = t[kLtTimedRuns / 2];
+        const double us = 1e3 * (double)ms / kLtTimedRuns;
         if (best < 0 || us < best) {
             best = us;
             best_i = i;
         }
     }
-    for (int r = 0; r < made; ++r) {
-        (void)hipEventDestroy(e0[r]);
-        (void)hipEventDestroy(e1[r]);
-    }
-    (void)hipFree(flush);
-    if (!ev_ok) return LSCD_ERROR_HIP;
+    (void)hipEventDestroy(e0);
+    (void)hipEventDestroy(e1);
+    free_copies();
     if (best_i < 0) return LSCD_ERROR_NOT_SUPPORTED;
     bool found = false;
     for (auto& t : lt->tuned)

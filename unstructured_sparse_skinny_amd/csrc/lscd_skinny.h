@@ -227,7 +227,10 @@ __global__ __launch_bounds__(WK * 64) void spmm_indep_kernel(SpmmArgs a) {
                 scatter_keep<R>(wb[q], n, As, lane);
                 if (n > R * 64) scatter_rest<R>(n, As, a.words + first[q], lane);
                 bf[q].store(Bw, lane);
-                mma_rows<NPAD, RG>(acc, As, Bw, lane);
+                if constexpr (WK == 8)
+                    mma_rows_prefetched<NPAD, RG>(acc, As, Bw, lane);  // LDS holds one workgroup per CU
+                else
+                    mma_rows<NPAD, RG>(acc, As, Bw, lane);
                 // Reset: rewriting the scattered positions costs one 2-byte store per word,
                 // clearing the tile TM / 8 16-byte stores per lane; the former wins only for
                 // sparse tiles (at most a quarter of the tile's positions).
