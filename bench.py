@@ -81,14 +81,15 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash():
-    """Short hash of the device sources: committed counter figures are valid only for them."""
+def kernel_source_hash(fmt="tiled-csl"):
+    """Short hash of the device sources behind one format's product: committed counter figures
+    are valid only for them."""
     spec = importlib.util.spec_from_file_location("_lscd_build", os.path.join(ROOT, "unstructured_sparse_skinny_amd",
                                                                                "build.py"))
     mod = importlib.util.module_from_spec(spec)
     spec.loader.exec_module(mod)
     h = hashlib.sha256()
-    for rel in mod.DEVICE_SOURCES:
+    for rel in mod.DEVICE_SOURCES_BY_FORMAT[fmt]:
         with open(os.path.join(ROOT, "unstructured_sparse_skinny_amd", rel), "rb") as f:
             h.update(rel.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
@@ -151,6 +152,11 @@ def time_calls(fn_args, steps, warmup, torch, graph=True, spread_replays=5):
             if time.perf_counter() - t_w >= WARM_S:
                 break
         t_s, t_e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(side):            # one more untimed replay, with the timing events
+            t_s.record(side)                       # themselves already in use
+            g.replay()
+            t_e.record(side)
+        torch.cuda.synchronize()
         t0 = time.perf_counter()
         with torch.cuda.stream(side):
             t_s.record(side)
@@ -554,7 +560,7 @@ def main():
     # while the kernel sources and launch plan are the ones the counters were taken with.
     traffic = None
     tpath = os.path.join(ROOT, "profiles", f"traffic_{case.name}.json")
-    src_hash = kernel_source_hash()
+    src_hash = kernel_source_hash(args.format)
     if os.path.exists(tpath):
         with open(tpath) as f:
             t = json.load(f)

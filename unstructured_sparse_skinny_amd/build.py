@@ -23,10 +23,16 @@ BUILD_DIR = os.path.join(HERE, "_build")
 SOURCES = ["csrc/lscd_skinny64.hip", "csrc/lscd_skinny32.hip", "csrc/lscd_skinny16.hip", "csrc/lscd_three_level.hip",
            "csrc/lscd_bitmap.hip", "csrc/lscd_wide.hip", "csrc/lscd_kernels.hip", "csrc/lscd_encode_dev.hip",
            "csrc/lscd_api.cpp", "csrc/lscd_linear.cpp", "csrc/lscd_pack.cpp"]
-# Device sources (their hash identifies the kernels that produced a committed measurement).
-DEVICE_SOURCES = ["csrc/lscd_device.h", "csrc/lscd_skinny.h", "csrc/lscd_skinny16.hip", "csrc/lscd_skinny32.hip",
-                  "csrc/lscd_skinny64.hip", "csrc/lscd_wide.hip", "csrc/lscd_bitmap.hip", "csrc/lscd_three_level.hip",
-                  "csrc/lscd_kernels.hip", "csrc/lscd_internal.h"]
+# Device sources of each format's product (their hash identifies the kernels behind a committed
+# measurement of that format; the split-K reduction and the shared helpers belong to all).
+_COMMON_DEVICE = ["csrc/lscd_internal.h", "csrc/lscd_device.h", "csrc/lscd_kernels.hip"]
+DEVICE_SOURCES_BY_FORMAT = {
+    "tiled-csl": _COMMON_DEVICE + ["csrc/lscd_skinny.h", "csrc/lscd_skinny16.hip", "csrc/lscd_skinny32.hip",
+                                   "csrc/lscd_skinny64.hip", "csrc/lscd_wide.hip"],
+    "bitmap": _COMMON_DEVICE + ["csrc/lscd_bitmap.hip"],
+    "three-level": _COMMON_DEVICE + ["csrc/lscd_three_level.hip"],
+}
+DEVICE_SOURCES = sorted({f for v in DEVICE_SOURCES_BY_FORMAT.values() for f in v})
 ARCH = os.environ.get("LSCD_OFFLOAD_ARCH", "gfx950")
 
 
