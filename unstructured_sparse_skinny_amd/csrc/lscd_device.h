@@ -385,6 +385,60 @@ struct BWave {
     }
 };
 
+// Write one wavefront's results: RG x NCB blocks of 16 x 16 fp32 sums in the MFMA layout
+// (lane l holds column l & 15, rows 4 * (l >> 4) + 0..3 of each block) for rows m0 .. m0 + 16 RG - 1
+// and columns n0 .. n0 + 16 NCB - 1; fp16 to C (N x M) when a.S == 1, else the fp32 partial sums
+// of split s.  They leave through `red`, LDS private to the wavefront (16 * LD floats), 16
+// columns at a time, transposed so that each store writes whole 128-byte lines: a column's rows
+// are contiguous in C and in the partial sums.  (Stored straight from the MFMA layout, a store
+// instruction would write 16 columns x 4 rows, a 64-byte piece of 16 different lines.)  The
+// wavefront's LDS operations run in order, so no barrier is needed.
+template <int RG, int NCB, int LD>
+__device__ __forceinline__ void store_results(const f32x4 (&acc)[RG][NCB], float* red, const SpmmArgs& a, int s,
+                                              int m0, int n0, int lane) {
+    constexpr int TM = 16 * RG;
+    static_assert(LD >= TM, "a column of the block fits its stride");
+    const int ncol = lane & 15;
+    const int mq = (lane >> 4) * 4;
+    const bool vec_m = (a.M & 3) == 0;
+#pragma unroll
+    for (int j = 0; j < NCB; ++j) {
+#pragma unroll
+        for (int i = 0; i < RG; ++i) *reinterpret_cast<f32x4*>(red + ncol * LD + i * 16 + mq) = acc[i][j];
+#pragma unroll
+        for (int it = lane; it < 16 * (TM / 4); it += 64) {
+            const int c = it / (TM / 4);
+            const int ml = (it - c * (TM / 4)) * 4;
+            const int n = n0 + j * 16 + c;
+            const int m = m0 + ml;
+            if (n >= a.N || m >= a.M) continue;
+            const f32x4 v = *reinterpret_cast<const f32x4*>(red + c * LD + ml);
+            if (a.S == 1) {
+                uint16_t* dst = a.C + (int64_t)n * a.M + m;
+                if (vec_m && m + 3 < a.M) {
+                    uint2 pk;
+                    pk.x = (uint32_t)f16_bits(v[0]) | ((uint32_t)f16_bits(v[1]) << 16);
+                    pk.y = (uint32_t)f16_bits(v[2]) | ((uint32_t)f16_bits(v[3]) << 16);
+                    *reinterpret_cast<uint2*>(dst) = pk;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (m + e < a.M) dst[e] = f16_bits(v[e]);
+                }
+            } else {
+                float* dst = a.part + ((int64_t)s * a.N + n) * a.M + m;
+                if (vec_m && m + 3 < a.M) {
+                    *reinterpret_cast<f32x4*>(dst) = v;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (m + e < a.M) dst[e] = v[e];
+                }
+            }
+        }
+    }
+}
+
 template <typename Kern>
 hipError_t run(Kern k, const SpmmArgs& a, int grid, hipStream_t st, int* occ, int threads = kThreads) {
     if (occ) return hipOccupancyMaxActiveBlocksPerMultiprocessor(occ, k, threads, 0);

@@ -113,44 +113,8 @@ __global__ __launch_bounds__(kThreads) void spmm_kernel(SpmmArgs a) {
             }
         }
     }
-    // MFMA 16x16 result layout: lane holds column (lane & 15), rows 4*(lane >> 4) + 0..3.
-    const int ncol = lane & 15;
-    const int mrow = rb * TM + (lane >> 4) * 4;
-    const bool vec_m = (a.M & 3) == 0;
-    if (active) {
-#pragma unroll
-        for (int i = 0; i < RG; ++i) {
-#pragma unroll
-            for (int j = 0; j < NPAD / 16; ++j) {
-                const int n = j * 16 + ncol;
-                const int m = mrow + i * 16;
-                if (n >= a.N || m >= a.M) continue;
-                const f32x4 v = acc[i][j];
-                if (a.S == 1) {
-                    uint16_t* dst = a.C + (int64_t)n * a.M + m;
-                    if (vec_m && m + 3 < a.M) {
-                        uint2 pk;
-                        pk.x = (uint32_t)f16_bits(v[0]) | ((uint32_t)f16_bits(v[1]) << 16);
-                        pk.y = (uint32_t)f16_bits(v[2]) | ((uint32_t)f16_bits(v[3]) << 16);
-                        *reinterpret_cast<uint2*>(dst) = pk;
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            if (m + e < a.M) dst[e] = f16_bits(v[e]);
-                    }
-                } else {
-                    float* dst = a.part + ((int64_t)s * a.N + n) * a.M + m;
-                    if (vec_m && m + 3 < a.M) {
-                        *reinterpret_cast<f32x4*>(dst) = v;
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            if (m + e < a.M) dst[e] = v[e];
-                    }
-                }
-            }
-        }
-    }
+    // padded column stride: the 16 columns of a block start on different LDS banks
+    if (active) store_results<RG, NPAD / 16, TM + 4>(acc, reinterpret_cast<float*>(As), a, s, rb * TM, 0, lane);
 }
 
 
@@ -227,8 +191,11 @@ __global__ __launch_bounds__(WK * 64) void spmm_indep_kernel(SpmmArgs a) {
                 scatter_keep<R>(wb[q], n, As, lane);
                 if (n > R * 64) scatter_rest<R>(n, As, a.words + first[q], lane);
                 bf[q].store(Bw, lane);
-                if constexpr (WK == 8)
-                    mma_rows_prefetched<NPAD, RG>(acc, As, Bw, lane);  // LDS holds one workgroup per CU
+                // Operand prefetch where the LDS already holds one workgroup per CU and its
+                // registers fit beside the accumulators and stages (OPT-66B QKV shape, 112-row
+                // tiles at N = 32: 55.2 us with it and 2 spilled registers, 54.8 without).
+                if constexpr (WK == 8 && (NPAD == 16 || R + RG <= 16))
+                    mma_rows_prefetched<NPAD, RG>(acc, As, Bw, lane);
                 else
                     mma_rows<NPAD, RG>(acc, As, Bw, lane);
                 // Reset: rewriting the scattered positions costs one 2-byte store per word,

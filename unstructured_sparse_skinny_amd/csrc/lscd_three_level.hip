@@ -372,44 +372,7 @@ __global__ __launch_bounds__(kThreads) void spmm_three_level_shared_kernel(SpmmA
                 three_level_reset(As, dst, npts, res, lane < nr);
         }
     }
-    // MFMA 16x16 result layout: lane holds column (lane & 15), rows 4*(lane >> 4) + 0..3.
-    const int ncol = lane & 15;
-    const int mrow = rb * kTileM + (lane >> 4) * 4;
-    const bool vec_m = (a.M & 3) == 0;
-    if (active) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-#pragma unroll
-            for (int j = 0; j < NPAD / 16; ++j) {
-                const int n = j * 16 + ncol;
-                const int m = mrow + i * 16;
-                if (n >= a.N || m >= a.M) continue;
-                const f32x4 v = acc[i][j];
-                if (a.S == 1) {
-                    uint16_t* dst = a.C + (int64_t)n * a.M + m;
-                    if (vec_m && m + 3 < a.M) {
-                        uint2 pk;
-                        pk.x = (uint32_t)f16_bits(v[0]) | ((uint32_t)f16_bits(v[1]) << 16);
-                        pk.y = (uint32_t)f16_bits(v[2]) | ((uint32_t)f16_bits(v[3]) << 16);
-                        *reinterpret_cast<uint2*>(dst) = pk;
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            if (m + e < a.M) dst[e] = f16_bits(v[e]);
-                    }
-                } else {
-                    float* dst = a.part + ((int64_t)s * a.N + n) * a.M + m;
-                    if (vec_m && m + 3 < a.M) {
-                        *reinterpret_cast<f32x4*>(dst) = v;
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            if (m + e < a.M) dst[e] = v[e];
-                    }
-                }
-            }
-        }
-    }
+    if (active) store_results<4, NPAD / 16, kTileM + 4>(acc, reinterpret_cast<float*>(As), a, s, rb * kTileM, 0, lane);
 }
 
 // Dense view of a three-level encoding: slot filling and residual through the product

@@ -107,6 +107,9 @@ __global__ __launch_bounds__(kThreads) void spmm_wide_kernel(SpmmArgs a) {
         }
     }
     if (wave >= NW) return;
+    // Stored straight from the MFMA layout: the whole-line stores through LDS of the other
+    // kernels (store_results) measured 1-2 % slower here (OPT-30B MLP1 and OPT-175B OutProj
+    // shapes at N = 128).
     const int ncol = lane & 15;
     const int mrow = rb * TM + (lane >> 4) * 4;
     const bool vec_m = (a.M & 3) == 0;
