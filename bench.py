@@ -399,7 +399,7 @@ def bench_encode(args, case, L, torch, np):
                       "note": "wall time per synchronous call, allocations included"}), flush=True)
 
 
-VARIANTS = ["shared-B", "independent-4", "independent-8", "wide", "bitmap", "three-level"]
+VARIANTS = ["shared-B", "independent-4", "independent-8", "wide", "bitmap", "three-level", "shared-B-3"]
 
 
 def main():

@@ -71,7 +71,8 @@ typedef struct {
                                    3 the N > 64 kernel with N padded to 128 (tiles taller
                                    than 64 rows that overflow the shared-B register stage;
                                    splits[2] then equals splits_wide[0]), 4 bitmap tiles,
-                                   5 three-level tiles                                      */
+                                   5 three-level tiles, 6 shared B tile with three row
+                                   blocks per workgroup instead of four (N padded to 64)    */
     int32_t splits_wide[3];     /* K-splits for N > 64, per launch of N padded to 128, 192,
                                    256 (N > 256 runs one launch per 256 columns)            */
     int32_t reg_vectors_wide;   /* 128-bit staging registers per thread, N > 64 kernel      */

@@ -67,12 +67,13 @@ def test_decode_dense_and_overflow_paths():
 
 @pytest.mark.parametrize("N", [1, 7, 8, 16, 17, 32, 33, 48, 64])
 @pytest.mark.parametrize("splits", [None, "1", "3"])
-@pytest.mark.parametrize("variant", ["indep", "shared"])
+@pytest.mark.parametrize("variant", ["indep", "shared", "shared3"])
 def test_integer_bit_exact(N, splits, variant):
     """Integer inputs: every partial sum is exact in fp32, so C must equal fp16_rne(C_oracle) bit for bit.
 
-    Runs both product kernel variants (the independent-wavefront one exists for N <= 32; above
-    that the shared-B kernel runs whatever is asked).
+    Runs the product kernel variants: the independent-wavefront one exists for N <= 32; above
+    that the shared-B kernel runs, with four row blocks per workgroup ("indep", "shared") or
+    three ("shared3"; at N <= 32 that setting leaves the default kernel).
     """
     case = syn.random_case(333, 1000 + 8 * N, N, 0.35, seed=N, values="int3")
     with env(LSCD_SPLITK=splits, LSCD_KERNEL=variant):
@@ -86,7 +87,7 @@ def test_integer_bit_exact(N, splits, variant):
 
 @pytest.mark.parametrize("M,K,keep", SHAPES)
 @pytest.mark.parametrize("N", [8, 16, 32, 64])
-@pytest.mark.parametrize("variant", ["indep", "shared"])
+@pytest.mark.parametrize("variant", ["indep", "shared", "shared3"])
 def test_gaussian_within_tolerance(M, K, keep, N, variant):
     case = syn.random_case(M, K, N, keep, seed=M + N)
     with env(LSCD_KERNEL=variant):

@@ -137,5 +137,5 @@ def test_tall_fitting_tiles_keep_shared_b():
     case = syn.random_case(300, 700, 64, 0.35, seed=5, values="int3")
     h = encode(case.A16, case.mask, 112)
     assert h.info["max_tile_words"] <= h.info["reg_vectors"] * 64 * 4
-    assert h.info["variant"][2] == 0
+    assert h.info["variant"][2] in (0, 6)   # shared B, four or three row blocks per workgroup
     assert np.array_equal(run(h, case.B16, case.M), osp.fp16_rne(osp.spmm_f64(case.A16, case.mask, case.B16)))

@@ -143,7 +143,9 @@ def test_split_plan_low_fill_doubles():
     if cus == 256:
         assert info["tile_m"] == 64
         assert info["splits_wide"][0] == 4
-        assert info["splits"][2] == 10
+        # N = 64 fills the resident slots: groups of three row blocks x 8 splits (512), or of
+        # four x 10 (480) where the three-wavefront kernel has no instantiation for the stage
+        assert (info["variant"][2], info["splits"][2]) in ((6, 8), (0, 10))
     B16 = syn.int_fp16(rng, N, K)
     B = torch.from_numpy(B16.view(np.float16)).to("cuda")
     C = torch.full((N, M), float("nan"), dtype=torch.float16, device="cuda")

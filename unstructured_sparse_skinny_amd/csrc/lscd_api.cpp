@@ -145,6 +145,7 @@ int current_cus() {
 }
 
 int64_t row_groups(const Grid& g, int kind) {
+    if (kind == lscd::kKernelShared3) return (g.MB + 2) / 3;
     return kind == lscd::kKernelShared ? (g.MB + lscd::kWaves - 1) / lscd::kWaves : g.MB;
 }
 
@@ -163,13 +164,48 @@ int pick_kind(int npad) {
 
 int npad_index(int N) { return N <= 16 ? 0 : (N <= 32 ? 1 : 2); }
 
+// Shared-B kernel at N padded to 64: four or three row blocks per workgroup.  The planner
+// fills the resident slots in one wave of workgroups, and slots left over land on some CUs
+// only: 192 row blocks in groups of four give 48 x 10 = 480 workgroups for 512 slots, and the
+// 32 CUs that get one workgroup idle for the last quarter of the kernel while the other 224
+// run two.  Groups of three give 64 x 8 = 512, two on every CU.  The cost compared is the
+// busiest CU's work (its workgroups times row blocks times k tiles each).  Measured on the
+// OPT-175B shapes at N = 64 (us, four -> three row blocks):
+//   - a tie with fewer splits: MLP1 230.5 -> 199.8 (50 % sparsity) and 189.2 -> 174.1 (60 %)
+//     (four: 4 splits, 1.5 waves of workgroups; three: 2 splits, one wave), QKV 169.6 -> 162.3;
+//   - 6 % less work on the busiest CU with short K ranges: OutProj 57.7 -> 55.3 (60 %);
+//   - the same with long ones (96 k tiles per workgroup): the OPT-175B MLP2 shape at 60 %,
+//     172.4 -> 173.7 -- with fewer wavefronts per CU (six, not eight) its deeper pipelines lose
+//     what the balance gains, so four stay.
+// LSCD_KERNEL=shared keeps four, =shared3 forces three.
+void plan_shared_rows(const Grid& g, lscd_handle_s* h, int64_t format_bytes) {
+    const char* e = getenv("LSCD_KERNEL");
+    const bool force3 = e && strcmp(e, "shared3") == 0;
+    if (e && !force3) return;
+    const int occ3 = lscd::spmm_blocks_per_cu(lscd::kKernelShared3, 64, h->R, (int)std::min<int64_t>(g.K, 1 << 30), g.tm);
+    const int64_t g3 = row_groups(g, lscd::kKernelShared3), g4 = row_groups(g, lscd::kKernelShared);
+    const int s3 = plan_splits(g, h->cus, occ3, g3, 2, false, true, format_bytes);
+    const int s4 = h->S[2];
+    auto busiest = [&](int64_t groups, int w, int s) {
+        return (double)((groups * s + h->cus - 1) / h->cus) * (double)w * (double)g.KT / (double)s;
+    };
+    if (occ3 < 2) return;  // no instantiation for this stage and tile height, or one per CU
+    const double l3 = busiest(g3, 3, s3), l4 = busiest(g4, 4, s4);
+    const bool tie_fewer_splits = l3 >= 0.99 * l4 && l3 <= 1.01 * l4 && s3 < s4;
+    const bool lighter_short_k = l3 < 0.99 * l4 && g.KT <= 64 * (int64_t)s3;
+    if (force3 || tie_fewer_splits || lighter_short_k) {
+        h->kind[2] = lscd::kKernelShared3;
+        h->S[2] = s3;
+    }
+}
+
 }  // namespace
 
 namespace lscd {
 
 // Staging registers per lane (vectors of 4 words) of the register stage, from the instantiated
 // choices; LSCD_MAX_R caps it (tests use it to force the path past the stage).
-static const int kRegChoices[] = {2, 3, 4, 5, 6, 8, 10, 12, 16};
+static const int kRegChoices[] = {2, 3, 4, 5, 6, 7, 8, 10, 12, 16};
 
 int pick_reg_vectors(int32_t max_tile_words) {
     const int need = ((max_tile_words / 4) + 63) / 64;
@@ -186,7 +222,7 @@ int pick_reg_vectors(int32_t max_tile_words) {
 
 int pick_reg_vectors_tall(int32_t max_tile_words) {
     const int r = pick_reg_vectors(max_tile_words);
-    return r <= 4 ? 4 : (r <= 6 ? 6 : (r >= 12 ? 12 : r));
+    return r <= 4 ? 4 : (r <= 6 ? 6 : (r <= 8 ? 8 : (r >= 12 ? 12 : r)));
 }
 
 int pick_reg_vectors_wide(int32_t max_tile_words) {
@@ -247,6 +283,7 @@ lscd_status_t new_handle(const Grid& g, int64_t nnz, int64_t nwords, int32_t max
         const int min_tiles = h->kind[i] == kKernelIndep ? 8 : (h->kind[i] == kKernelIndep8 ? 16 : 2);
         const bool indep = h->kind[i] == kKernelIndep || h->kind[i] == kKernelIndep8;
         h->S[i] = plan_splits(g, h->cus, occ, row_groups(g, h->kind[i]), min_tiles, indep, true, 4 * nwords);
+        if (h->kind[i] == kKernelShared && i == 2) plan_shared_rows(g, h, 4 * nwords);
         if (h->S[i] > 1) part = std::max<int64_t>(part, (int64_t)h->S[i] * g.M * (16 << i) * 4);
     }
     h->Rw = pick_reg_vectors_wide(maxw);

@@ -222,10 +222,10 @@ __device__ __forceinline__ void scatter_tile_wg(const u32x4 (&wb)[R], int nvec, 
 // holds the B chunks of the same k tile as its packed words, so that waiting for a stage
 // (the oldest loads in flight; the vector-memory counter retires in order) never waits on
 // loads issued for later tiles.
-template <int NPAD, bool VEC>
+template <int NPAD, bool VEC, int THREADS = kThreads>
 struct BStage {
     static constexpr int kChunks = NPAD * 8;
-    static constexpr int kPer = (kChunks + kThreads - 1) / kThreads;
+    static constexpr int kPer = (kChunks + THREADS - 1) / THREADS;
     u32x4 r[kPer];
 
     // VEC (K % 8 == 0): one 16-byte buffer load per chunk; chunks outside B (n >= N, k >= K,
@@ -235,7 +235,7 @@ struct BStage {
                                          int tid, bool valid) {
 #pragma unroll
         for (int u = 0; u < kPer; ++u) {
-            const int ch = tid + u * kThreads;
+            const int ch = tid + u * THREADS;
             const int n = ch >> 3, c = ch & 7;
             const int k0 = kt * kTileK + c * 8;
             const bool in = valid && ch < kChunks && n < N && k0 < K;
@@ -261,7 +261,7 @@ struct BStage {
     __device__ __forceinline__ void store(unsigned char* Bs, int N, int tid) const {
 #pragma unroll
         for (int u = 0; u < kPer; ++u) {
-            const int ch = tid + u * kThreads;
+            const int ch = tid + u * THREADS;
             const int n = ch >> 3, c = ch & 7;
             if (ch < kChunks && n < N) *reinterpret_cast<u32x4*>(Bs + lds_chunk(n, c)) = r[u];
         }

@@ -128,6 +128,8 @@ constexpr int kBitmapSlackBytes = 16;
 // kernel, launches of <= 64 columns.
 constexpr int kKernelThreeLevel = 5;
 constexpr int kThreeLevelMaxN = 64;
+// Tiled-CSL shared-B kernel with three row blocks per workgroup (N padded to 64 only).
+constexpr int kKernelShared3 = 6;
 hipError_t launch_decode_three_level(const DecodeArgs& a, int grid, hipStream_t s);
 hipError_t launch_decode_bitmap(const DecodeArgs& a, int grid, hipStream_t s);
 // Staging registers per thread and tile of the wide variant (1, 2 or 4).

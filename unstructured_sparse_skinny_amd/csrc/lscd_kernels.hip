@@ -121,6 +121,7 @@ hipError_t launch_decode_rg(int R, const DecodeArgs& a, int grid, hipStream_t st
             case 2: return go(decode_kernel<2, RG>);
             case 3: return go(decode_kernel<3, RG>);
             case 5: return go(decode_kernel<5, RG>);
+            case 7: return go(decode_kernel<7, RG>);
             case 16: return go(decode_kernel<16, RG>);
             default: break;
         }

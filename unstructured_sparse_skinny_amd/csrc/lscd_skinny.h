@@ -8,16 +8,22 @@
 namespace lscd {
 namespace {
 
-template <int NPAD, int R, int P, bool VEC, int RG>
-__global__ __launch_bounds__(kThreads) void spmm_kernel(SpmmArgs a) {
+// Shared-B variant: a workgroup of W wavefronts takes W consecutive row blocks over one K
+// split; they share each staged B tile (double-buffered in LDS, one barrier per k step).  W = 4
+// in general; W = 3 where it spreads the work more evenly over the CUs (see the planner).
+// (Three wavefronts alone would let the compiler take every register of a SIMD; two
+// workgroups of three per CU need two wavefronts per SIMD, as four-wavefront workgroups get.)
+template <int NPAD, int R, int P, bool VEC, int RG, int W = kWaves>
+__global__ __launch_bounds__(64 * W, W == 3 ? 2 : 1) void spmm_kernel(SpmmArgs a) {
     constexpr int TM = 16 * RG;          // rows of the format's tiles
     constexpr int kTB = TM * kRowBytes;  // one wavefront's LDS tile
-    __shared__ __attribute__((aligned(16))) unsigned char smem[kWaves * kTB + 2 * NPAD * kRowBytes];
+    constexpr int THREADS = 64 * W;
+    __shared__ __attribute__((aligned(16))) unsigned char smem[W * kTB + 2 * NPAD * kRowBytes];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     unsigned char* As = smem + wave * kTB;
-    unsigned char* Bs0 = smem + kWaves * kTB;
+    unsigned char* Bs0 = smem + W * kTB;
 
     // XCD-aware work mapping: hardware places workgroup b on XCD b % 8; give each XCD a
     // contiguous run of work items (items are split-major, so a run shares a B slice).
@@ -28,7 +34,7 @@ __global__ __launch_bounds__(kThreads) void spmm_kernel(SpmmArgs a) {
     const int g = item - s * a.G;
     const int kt0 = (int)(((int64_t)s * a.KT) / a.S);
     const int kt1 = (int)(((int64_t)(s + 1) * a.KT) / a.S);
-    const int rb = g * kWaves + wave;
+    const int rb = g * W + wave;
     const bool active = rb < a.MB;
     // Tile offsets are read through the constant address space: the offsets are never
     // written by the kernel, and this lets the compiler use scalar loads (counted apart
@@ -39,7 +45,7 @@ __global__ __launch_bounds__(kThreads) void spmm_kernel(SpmmArgs a) {
         __builtin_amdgcn_make_buffer_rsrc((void*)a.B, (short)0, a.N * a.K * 2, kBufWord3);
 
     // B rows n >= N stay zero for the whole kernel (both buffers).
-    for (int ch = tid; ch < 2 * NPAD * 8; ch += kThreads) {
+    for (int ch = tid; ch < 2 * NPAD * 8; ch += THREADS) {
         const int row = ch >> 3;
         if (row % NPAD >= a.N) {
             const u32x4 z = {0u, 0u, 0u, 0u};
@@ -52,7 +58,7 @@ __global__ __launch_bounds__(kThreads) void spmm_kernel(SpmmArgs a) {
     auto off_at = [&](int i) -> uint32_t { return (active && i <= kt1) ? toff[i] : 0u; };
 
     u32x4 wb[P][R];
-    BStage<NPAD, VEC> bst[P];
+    BStage<NPAD, VEC, THREADS> bst[P];
     int nv[P];
     uint32_t first[P];
 #pragma unroll
@@ -271,6 +277,10 @@ template <int R>
 constexpr int stages() {
     return R <= 4 ? 4 : (R <= 8 ? 3 : 2);
 }
+template <int R, int RG>
+constexpr bool shared3_fits() {
+    return RG == 4 ? (R != 8 && R != 16) : (RG == 5 ? R <= 10 : (RG <= 7 ? R <= 8 : R <= 6));
+}
 template <int NPAD, int R>
 constexpr int stages_indep() {
     return (NPAD == 16 && R <= 4) ? 3 : 2;
@@ -300,6 +310,15 @@ hipError_t launch_spmm_rg(int kind, const SpmmArgs& a, int grid, hipStream_t st,
                        occ, 512);
         }
     }
+    if constexpr (NPAD == 64) {
+        if (kind == kKernelShared3) {
+            // only where two workgroups of three fit a CU without spilling registers (the
+            // three-wavefront B stage takes 3 registers of 4 per stage and thread, not 2)
+            if constexpr (shared3_fits<R, RG>())
+                if (vec) return run(spmm_kernel<NPAD, R, (RG == 4 ? stages<R>() : 2), true, RG, 3>, a, grid, st, occ, 192);
+            return hipErrorInvalidValue;
+        }
+    }
     if (kind != kKernelShared) return hipErrorInvalidValue;
     if (!vec) return run(spmm_kernel<NPAD, (RG == 4 ? 16 : 12), 2, false, RG>, a, grid, st, occ);
     // tall tiles: two stages (the accumulators of RG row groups leave no room for a third)
@@ -313,6 +332,7 @@ hipError_t launch_spmm_r(int kind, int R, const SpmmArgs& a, int grid, hipStream
             case 2: return launch_spmm_rg<NPAD, 2, RG>(kind, a, grid, st, occ);
             case 3: return launch_spmm_rg<NPAD, 3, RG>(kind, a, grid, st, occ);
             case 5: return launch_spmm_rg<NPAD, 5, RG>(kind, a, grid, st, occ);
+            case 7: return launch_spmm_rg<NPAD, 7, RG>(kind, a, grid, st, occ);
             case 16: return launch_spmm_rg<NPAD, 16, RG>(kind, a, grid, st, occ);
             default: break;
         }
