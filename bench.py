@@ -352,6 +352,7 @@ def sweep_n(args, case, L, torch, np):
         for h in hs[:nd]:
             L.lscd_set_linear_crossover(h, -1)
         path = L.lscd_linear_path(hs[0], N)
+        lt_s, lt_d, lt_measured = L.lscd_linear_times(hs[0], N)
         tl = ts if path == 0 else tt
         ms, md = L.lscd_linear_model(M, K, info["nnz_padded"], info["num_tiles"], N)
         if args.format != "tiled-csl":
@@ -364,6 +365,7 @@ def sweep_n(args, case, L, torch, np):
                           "tune_us": [round(t, 1) for t in tune], "linear_us": round(tl * 1e3, 1),
                           "linear_path": ["sparse", "dense"][path],
                           "linear_picks_faster": (path == 0) == (ts <= tt),
+                          "linear_compared_us": [round(lt_s, 1), round(lt_d, 1)], "linear_measured": lt_measured,
                           "model_sparse_us": None if ms is None else round(ms, 1), "model_dense_us": round(md, 1),
                           "sparse_pct_roofline": round(100 * (4 * info["nnz"] + 4 * (info["num_tiles"] + 1) +
                                                               2 * K * N + 2 * M * N) / (ts * 1e-3) / 1e9 /

@@ -310,23 +310,36 @@ lscd_status_t lscd_linear(lscd_handle_t h, const void* B, void* C, int32_t N, vo
  * this handle at width N (the comparison the pages make against the vendor dense library,
  * Flash-LLM review section 6) and keep the fastest for lscd_linear's dense path.  B (N x K)
  * and C (N x M) are caller device buffers as for lscd_spmm; C is overwritten.  Each candidate
- * runs twice untimed, then 20 times back to back between two events on the default stream,
- * rotating over copies of the dense matrix whose total exceeds three times the 256 MiB
- * Infinity Cache (2 to 8 copies), so the weights come from HBM as in a model's layer loop
- * rather than from the cache.  *best_us receives the fastest candidate's mean time per GEMM,
- * *candidates how many were timed.  Synchronous.  Needs lscd_attach_dense first (NOT_SUPPORTED
- * otherwise); allocates a 64 MiB workspace on its first call, freed by lscd_destroy, and the
- * extra copies (1 to 7 times M*K*2 bytes) for the duration of the call.
+ * is timed as 20 calls captured into one HIP graph on a private stream (replayed twice
+ * untimed, then once between two events; 2 + 20 eager calls on the default stream if the
+ * calls cannot be captured), rotating over copies of the dense matrix whose total exceeds
+ * three times the 256 MiB Infinity Cache (2 to 8 copies), so the weights come from HBM as in
+ * a model's layer loop rather than from the cache.  *best_us receives the fastest candidate's
+ * mean time per GEMM, *candidates how many were timed.  It then times the handle's sparse
+ * product at this N the same way (rotating over 2 to 8 copies of the packed words), so that
+ * lscd_linear compares two measurements taken alike (lscd_linear_times).  Synchronous.  Needs
+ * lscd_attach_dense first (NOT_SUPPORTED otherwise); allocates a 64 MiB workspace on its first
+ * call, freed by lscd_destroy, and the extra copies (1 to 7 times M*K*2 bytes, then 1 to 7
+ * times the packed words) for the duration of the call; when the copies of the words cannot
+ * be allocated the sparse time stays the model's.
  */
 lscd_status_t lscd_tune_dense(lscd_handle_t h, const void* B, void* C, int32_t N, double* best_us,
                               int32_t* candidates);
 
+/*
+ * lscd_linear_times -- the two times lscd_linear_path compares for N (microseconds): the
+ * sparse product's and the dense GEMM's.  *measured = 1 when both come from lscd_tune_dense
+ * for this N, 0 when one or both are lscd_linear_model's predictions (or, for bitmap and
+ * three-level handles, the per-tile cost).  No device work.
+ */
+lscd_status_t lscd_linear_times(lscd_handle_t h, int32_t N, double* sparse_us, double* dense_us, int32_t* measured);
+
 /* lscd_linear_path -- the path lscd_linear takes for N: *path = 0 sparse, 1 dense (dense
  * only with a dense copy attached): dense iff its time is below the sparse product's, taking
- * the time lscd_tune_dense measured for this N when there is one and lscd_linear_model's
- * prediction otherwise.  The sparse time is lscd_linear_model's for a Tiled-CSL handle.  A
- * bitmap or three-level handle runs one launch per 64 columns whose kernels cost about the
- * same per tile at any density: its sparse time is a fixed part plus a time per tile for each
+ * both times from lscd_tune_dense when it has run for this N (lscd_linear_times), and
+ * predictions otherwise: lscd_linear_model's for a Tiled-CSL handle, while for a bitmap or
+ * three-level handle, which runs one launch per 64 columns whose kernels cost about the
+ * same per tile at any density, the sparse time is a fixed part plus a time per tile for each
  * launch (bitmap about 0.9, 1.0 and 1.2 ns per tile for N padded to 16, 32 and 64;
  * three-level 1.0, 1.2 and 1.5).  No device work. */
 lscd_status_t lscd_linear_path(lscd_handle_t h, int32_t N, int32_t* path);

@@ -78,11 +78,14 @@ def test_tuned_dense_path(N):
     with pytest.raises(L.LSCDError):
         L.lscd_tune_dense(h, B, C)                              # no dense copy yet
     L.lscd_attach_dense(h)
+    ts0, td0, measured0 = L.lscd_linear_times(h, N)
+    assert not measured0
+    assert (ts0, td0) == L.lscd_linear_model(case.M, case.K, h.info["nnz_padded"], h.info["num_tiles"], N)
     us, n = L.lscd_tune_dense(h, B, C)
-    say(f"tuned dense N={N}: {us:.1f} us over {n} candidates")
-    assert n >= 1 and us > 0
-    ts, _ = L.lscd_linear_model(case.M, case.K, h.info["nnz_padded"], h.info["num_tiles"], N)
-    assert L.lscd_linear_path(h, N) == (1 if us < ts else 0)     # the measured dense time decides
+    ts, td, measured = L.lscd_linear_times(h, N)
+    say(f"tuned dense N={N}: {us:.1f} us over {n} candidates; sparse {ts:.1f} us")
+    assert n >= 1 and us > 0 and measured and td == us and ts > 0
+    assert L.lscd_linear_path(h, N) == (1 if us < ts else 0)     # the two measured times decide
     L.lscd_set_linear_crossover(h, 0)
     want = osp.fp16_rne(osp.spmm_f64(case.A16, case.mask, case.B16))
     assert np.array_equal(run(L.lscd_linear, h, case.B16, case.M), want)

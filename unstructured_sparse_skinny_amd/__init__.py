@@ -38,7 +38,7 @@ EXPORTS = ("lscd_pack_size", "lscd_pack", "lscd_default_tile_m", "lscd_encode", 
            "lscd_import", "lscd_export",
            "lscd_get_info", "lscd_spmm", "lscd_debug_decode", "lscd_attach_dense", "lscd_linear",
            "lscd_linear_path", "lscd_set_linear_crossover", "lscd_linear_model", "lscd_tune_dense", "lscd_destroy",
-           "lscd_status_string", "lscd_stream_read", "lscd_spmm_noalloc")
+           "lscd_status_string", "lscd_stream_read", "lscd_spmm_noalloc", "lscd_linear_times")
 
 
 class lscd_info_t(ctypes.Structure):
@@ -90,6 +90,7 @@ def _load():
         "lscd_tune_dense": [VP, VP, VP, I32, P(ctypes.c_double), P(I32)],
         "lscd_destroy": [VP],
         "lscd_stream_read": [VP, I64, I32, VP, VP],
+        "lscd_linear_times": [VP, I32, P(ctypes.c_double), P(ctypes.c_double), P(I32)],
         "lscd_spmm_noalloc": [VP, VP, VP, I32, VP],
     }
     for name, args in sig.items():
@@ -334,6 +335,15 @@ def lscd_tune_dense(h: Handle, B, C):
     _check(_lib.lscd_tune_dense(ctypes.c_void_p(h.ptr), pb, pc, N, ctypes.byref(us), ctypes.byref(n)),
            "lscd_tune_dense")
     return us.value, n.value
+
+
+def lscd_linear_times(h: Handle, N: int):
+    """The (sparse, dense) microseconds lscd_linear compares for N, and whether both were
+    measured by lscd_tune_dense (else model predictions)."""
+    ts, td, m = ctypes.c_double(), ctypes.c_double(), ctypes.c_int32()
+    _check(_lib.lscd_linear_times(ctypes.c_void_p(h.ptr), N, ctypes.byref(ts), ctypes.byref(td), ctypes.byref(m)),
+           "lscd_linear_times")
+    return ts.value, td.value, bool(m.value)
 
 
 def lscd_linear_path(h: Handle, N: int) -> int:

@@ -174,9 +174,10 @@ int npad_index(int N) { return N <= 16 ? 0 : (N <= 32 ? 1 : 2); }
 //   - a tie with fewer splits: MLP1 230.5 -> 199.8 (50 % sparsity) and 189.2 -> 174.1 (60 %)
 //     (four: 4 splits, 1.5 waves of workgroups; three: 2 splits, one wave), QKV 169.6 -> 162.3;
 //   - 6 % less work on the busiest CU with short K ranges: OutProj 57.7 -> 55.3 (60 %);
-//   - the same with long ones (96 k tiles per workgroup): the OPT-175B MLP2 shape at 60 %,
-//     172.4 -> 173.7 -- with fewer wavefronts per CU (six, not eight) its deeper pipelines lose
-//     what the balance gains, so four stay.
+//   - the same with long ones (96 k tiles per workgroup): the OPT-175B MLP2 shape gains at
+//     50 % sparsity, 219.2 -> 199.9, where its tiles take two pipeline stages, and loses at
+//     60 %, 172.3 -> 173.3 (config 4 likewise), where they take three: with six wavefronts per
+//     CU instead of eight the deeper pipelines lose what the balance gains, so four stay.
 // LSCD_KERNEL=shared keeps four, =shared3 forces three.
 void plan_shared_rows(const Grid& g, lscd_handle_s* h, int64_t format_bytes) {
     const char* e = getenv("LSCD_KERNEL");
@@ -192,8 +193,8 @@ void plan_shared_rows(const Grid& g, lscd_handle_s* h, int64_t format_bytes) {
     if (occ3 < 2) return;  // no instantiation for this stage and tile height, or one per CU
     const double l3 = busiest(g3, 3, s3), l4 = busiest(g4, 4, s4);
     const bool tie_fewer_splits = l3 >= 0.99 * l4 && l3 <= 1.01 * l4 && s3 < s4;
-    const bool lighter_short_k = l3 < 0.99 * l4 && g.KT <= 64 * (int64_t)s3;
-    if (force3 || tie_fewer_splits || lighter_short_k) {
+    const bool lighter = l3 < 0.99 * l4 && (g.KT <= 64 * (int64_t)s3 || lscd::shared_stages(h->R, g.tm) < 3);
+    if (force3 || tie_fewer_splits || lighter) {
         h->kind[2] = lscd::kKernelShared3;
         h->S[2] = s3;
     }

@@ -130,6 +130,10 @@ constexpr int kKernelThreeLevel = 5;
 constexpr int kThreeLevelMaxN = 64;
 // Tiled-CSL shared-B kernel with three row blocks per workgroup (N padded to 64 only).
 constexpr int kKernelShared3 = 6;
+// Register stages of the shared-B kernels' prefetch pipeline for R staging vectors per lane
+// and TM-row tiles: deeper when a tile needs few registers; taller tiles take two (their
+// accumulators leave no room for a third).
+constexpr int shared_stages(int R, int TM) { return TM != kTileM ? 2 : (R <= 4 ? 4 : (R <= 8 ? 3 : 2)); }
 hipError_t launch_decode_three_level(const DecodeArgs& a, int grid, hipStream_t s);
 hipError_t launch_decode_bitmap(const DecodeArgs& a, int grid, hipStream_t s);
 // Staging registers per thread and tile of the wide variant (1, 2 or 4).

@@ -272,10 +272,9 @@ __global__ __launch_bounds__(WK * 64) void spmm_indep_kernel(SpmmArgs a) {
     }
 }
 
-// Register stages of the prefetch pipeline: deeper when a tile needs few registers.
 template <int R>
 constexpr int stages() {
-    return R <= 4 ? 4 : (R <= 8 ? 3 : 2);
+    return shared_stages(R, kTileM);
 }
 template <int R, int RG>
 constexpr bool shared3_fits() {
