@@ -223,7 +223,7 @@ int pick_reg_vectors(int32_t max_tile_words) {
 
 int pick_reg_vectors_tall(int32_t max_tile_words) {
     const int r = pick_reg_vectors(max_tile_words);
-    return r <= 4 ? 4 : (r <= 6 ? 6 : (r <= 8 ? 8 : (r >= 12 ? 12 : r)));
+    return r <= 4 ? 4 : (r <= 6 ? 6 : (r >= 12 ? 12 : r));
 }
 
 int pick_reg_vectors_wide(int32_t max_tile_words) {

@@ -121,7 +121,6 @@ hipError_t launch_decode_rg(int R, const DecodeArgs& a, int grid, hipStream_t st
             case 2: return go(decode_kernel<2, RG>);
             case 3: return go(decode_kernel<3, RG>);
             case 5: return go(decode_kernel<5, RG>);
-            case 7: return go(decode_kernel<7, RG>);
             case 16: return go(decode_kernel<16, RG>);
             default: break;
         }
@@ -129,6 +128,7 @@ hipError_t launch_decode_rg(int R, const DecodeArgs& a, int grid, hipStream_t st
     switch (R) {
         case 4: return go(decode_kernel<4, RG>);
         case 6: return go(decode_kernel<6, RG>);
+        case 7: return go(decode_kernel<7, RG>);
         case 8: return go(decode_kernel<8, RG>);
         case 10: return go(decode_kernel<10, RG>);
         case 12: return go(decode_kernel<12, RG>);

@@ -288,8 +288,11 @@ constexpr int stages_indep() {
 // Tile heights with kernel instantiations: 64 rows for every variant; 80, 96, 112 and 128
 // rows (RG = 5..8 row groups of 16) for the 8-wavefront independent variant (N <= 32), the
 // shared-B variant (N <= 64), the wide variant and the decode kernel.  Taller tiles come
-// with staging stages R in {4, 6, 8, 10, 12}; denser tiles take the path past the stage
-// (R = 16 with eight wavefronts spills registers).
+// with staging stages R in {4, 6, 7, 8, 10, 12}; denser tiles take the path past the stage
+// (R = 16 with eight wavefronts spills registers).  Each load of a stage past the tile's end
+// still issues (reading nothing), so a stage close to the tiles' size pays: OPT-30B MLP1 at
+// 80 % sparsity (112-row tiles of at most 1584 words) 29.9 -> 29.6 us with 7 vectors
+// instead of 8 at N = 16, 33.6 -> 33.2 at N = 32, 57.7 -> 56.8 at N = 64.
 //
 // K % 8 != 0 (rows of B not 16-byte aligned) runs the element-wise B path, instantiated
 // only with the largest register stage.  occ != nullptr: report resident workgroups per CU
@@ -331,7 +334,6 @@ hipError_t launch_spmm_r(int kind, int R, const SpmmArgs& a, int grid, hipStream
             case 2: return launch_spmm_rg<NPAD, 2, RG>(kind, a, grid, st, occ);
             case 3: return launch_spmm_rg<NPAD, 3, RG>(kind, a, grid, st, occ);
             case 5: return launch_spmm_rg<NPAD, 5, RG>(kind, a, grid, st, occ);
-            case 7: return launch_spmm_rg<NPAD, 7, RG>(kind, a, grid, st, occ);
             case 16: return launch_spmm_rg<NPAD, 16, RG>(kind, a, grid, st, occ);
             default: break;
         }
@@ -339,6 +341,7 @@ hipError_t launch_spmm_r(int kind, int R, const SpmmArgs& a, int grid, hipStream
     switch (R) {
         case 4: return launch_spmm_rg<NPAD, 4, RG>(kind, a, grid, st, occ);
         case 6: return launch_spmm_rg<NPAD, 6, RG>(kind, a, grid, st, occ);
+        case 7: return launch_spmm_rg<NPAD, 7, RG>(kind, a, grid, st, occ);
         case 8: return launch_spmm_rg<NPAD, 8, RG>(kind, a, grid, st, occ);
         case 10: return launch_spmm_rg<NPAD, 10, RG>(kind, a, grid, st, occ);
         case 12: return launch_spmm_rg<NPAD, 12, RG>(kind, a, grid, st, occ);
