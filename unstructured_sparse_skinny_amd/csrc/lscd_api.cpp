@@ -206,7 +206,7 @@ namespace lscd {
 
 // Staging registers per lane (vectors of 4 words) of the register stage, from the instantiated
 // choices; LSCD_MAX_R caps it (tests use it to force the path past the stage).
-static const int kRegChoices[] = {2, 3, 4, 5, 6, 7, 8, 10, 12, 16};
+static const int kRegChoices[] = {2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 16};
 
 int pick_reg_vectors(int32_t max_tile_words) {
     const int need = ((max_tile_words / 4) + 63) / 64;

@@ -104,7 +104,7 @@ struct DecodeArgs {
 
 // Staging registers per lane and tile that have kernel instantiations.
 int pick_reg_vectors(int32_t max_tile_words);
-// The same for tiles taller than 64 rows (their kernels exist for R in {4, 6, 7, 8, 10, 12}).
+// The same for tiles taller than 64 rows (their kernels exist for R in {4, 6 .. 12}).
 int pick_reg_vectors_tall(int32_t max_tile_words);
 // Product kernel variants: kKernelShared -- four row blocks per workgroup sharing a B tile
 // in LDS (any N); kKernelIndep -- one row block per workgroup, its k range split over the

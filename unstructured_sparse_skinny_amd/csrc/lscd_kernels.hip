@@ -130,7 +130,9 @@ hipError_t launch_decode_rg(int R, const DecodeArgs& a, int grid, hipStream_t st
         case 6: return go(decode_kernel<6, RG>);
         case 7: return go(decode_kernel<7, RG>);
         case 8: return go(decode_kernel<8, RG>);
+        case 9: return go(decode_kernel<9, RG>);
         case 10: return go(decode_kernel<10, RG>);
+        case 11: return go(decode_kernel<11, RG>);
         case 12: return go(decode_kernel<12, RG>);
         default: return hipErrorInvalidValue;
     }

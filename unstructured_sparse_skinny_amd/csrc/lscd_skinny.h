@@ -288,11 +288,13 @@ constexpr int stages_indep() {
 // Tile heights with kernel instantiations: 64 rows for every variant; 80, 96, 112 and 128
 // rows (RG = 5..8 row groups of 16) for the 8-wavefront independent variant (N <= 32), the
 // shared-B variant (N <= 64), the wide variant and the decode kernel.  Taller tiles come
-// with staging stages R in {4, 6, 7, 8, 10, 12}; denser tiles take the path past the stage
-// (R = 16 with eight wavefronts spills registers).  Each load of a stage past the tile's end
-// still issues (reading nothing), so a stage close to the tiles' size pays: OPT-30B MLP1 at
-// 80 % sparsity (112-row tiles of at most 1584 words) 29.9 -> 29.6 us with 7 vectors
-// instead of 8 at N = 16, 33.6 -> 33.2 at N = 32, 57.7 -> 56.8 at N = 64.
+// with staging stages R in {4, 6 .. 12}; denser tiles take the path past the stage (R = 16
+// with eight wavefronts spills registers).  Each load of a stage past the tile's end still
+// issues (reading nothing), so a stage close to the tiles' size pays: OPT-30B MLP1 at 80 %
+// sparsity (112-row tiles of at most 1584 words) 29.9 -> 29.6 us with 7 vectors instead of
+// 8 at N = 16, 57.7 -> 56.8 at N = 64; the OPT-175B shapes at 50 % (64-row tiles of at most
+// about 2200 words, 80-row ones of 2712) 0.5-1.4 % faster with 9 and 11 vectors instead of 10
+// and 12, except QKV at N = 64 (0.9 % slower).
 //
 // K % 8 != 0 (rows of B not 16-byte aligned) runs the element-wise B path, instantiated
 // only with the largest register stage.  occ != nullptr: report resident workgroups per CU
@@ -343,7 +345,9 @@ hipError_t launch_spmm_r(int kind, int R, const SpmmArgs& a, int grid, hipStream
         case 6: return launch_spmm_rg<NPAD, 6, RG>(kind, a, grid, st, occ);
         case 7: return launch_spmm_rg<NPAD, 7, RG>(kind, a, grid, st, occ);
         case 8: return launch_spmm_rg<NPAD, 8, RG>(kind, a, grid, st, occ);
+        case 9: return launch_spmm_rg<NPAD, 9, RG>(kind, a, grid, st, occ);
         case 10: return launch_spmm_rg<NPAD, 10, RG>(kind, a, grid, st, occ);
+        case 11: return launch_spmm_rg<NPAD, 11, RG>(kind, a, grid, st, occ);
         case 12: return launch_spmm_rg<NPAD, 12, RG>(kind, a, grid, st, occ);
         default: return hipErrorInvalidValue;
     }
