@@ -1,10 +1,13 @@
 """lscd_spmm_noalloc: the product with its split-K partial sums in the library's static per-GPU
 array instead of the handle's workspace (for callers that cannot allocate).
 
-Called through the C ABI and checked against lscd_spmm on the same handle: the same kernels
-and plan, so the results are bit-identical; and against the oracle's gates.  Two calls in a
-row, the second with a smaller problem, show that the array's left-over contents do not
-matter; a plan whose partials exceed the array is refused with NOT_SUPPORTED.
+Called through the C ABI and checked against the oracle's gates and against lscd_spmm on the same
+handle: the same kernels and plan, so the results are bit-identical.  The first call on each
+handle is lscd_spmm_noalloc, before anything has written the handle's own workspace, and a last
+call follows an lscd_spmm of another product: neither that workspace's contents nor its absence
+may show in the result.  Two problems in a row, the second smaller, show that the array's
+left-over contents do not matter; a plan whose partials exceed the array is refused with
+NOT_SUPPORTED.
 """
 import ctypes
 
@@ -32,11 +35,19 @@ def _call(fn, h, B16, M):
 
 
 def _both(h, case):
-    st0, ref = _call(L._lib.lscd_spmm, h, case.B16, case.M)
+    # first on a fresh handle, whose own workspace no call has written yet
     st1, got = _call(L._lib.lscd_spmm_noalloc, h, case.B16, case.M)
-    assert st0 == L.LSCD_SUCCESS and st1 == L.LSCD_SUCCESS, (st0, st1)
-    assert np.array_equal(got, ref)
+    assert st1 == L.LSCD_SUCCESS, st1
     assert_gates(got, osp.spmm_f64(case.A16, case.mask, case.B16), case.name)
+    st0, ref = _call(L._lib.lscd_spmm, h, case.B16, case.M)
+    assert st0 == L.LSCD_SUCCESS, st0
+    assert np.array_equal(got, ref)
+    # the handle's workspace now holds the partial sums of another product (B with its signs
+    # flipped); lscd_spmm_noalloc must neither read them nor be disturbed by them
+    st2, neg = _call(L._lib.lscd_spmm, h, case.B16 ^ np.uint16(0x8000), case.M)
+    assert st2 == L.LSCD_SUCCESS and not np.array_equal(neg, ref)
+    st3, again = _call(L._lib.lscd_spmm_noalloc, h, case.B16, case.M)
+    assert st3 == L.LSCD_SUCCESS and np.array_equal(again, ref)
 
 
 @pytest.mark.parametrize("fmt", ["tiled-csl", "bitmap", "three-level"])

@@ -757,7 +757,7 @@ lscd_status_t spmm_impl(lscd_handle_t h, const void* B, void* C, int32_t N, void
             hipError_t e = lscd::launch_spmm(lscd::kKernelBitmap, npad, 0, a, 8 * a.per_xcd, s);
             if (e != hipSuccess) return hip_status(e);
             if (a.S > 1) {
-                e = lscd::launch_reduce(h->d_part, a.C, a.S, (int64_t)n * h->g.M, s);
+                e = lscd::launch_reduce(part, a.C, a.S, (int64_t)n * h->g.M, s);
                 if (e != hipSuccess) return hip_status(e);
             }
         }
@@ -779,7 +779,7 @@ lscd_status_t spmm_impl(lscd_handle_t h, const void* B, void* C, int32_t N, void
             hipError_t e = lscd::launch_spmm(lscd::kKernelThreeLevel, npad, 0, a, 8 * a.per_xcd, s);
             if (e != hipSuccess) return hip_status(e);
             if (a.S > 1) {
-                e = lscd::launch_reduce(h->d_part, a.C, a.S, (int64_t)n * h->g.M, s);
+                e = lscd::launch_reduce(part, a.C, a.S, (int64_t)n * h->g.M, s);
                 if (e != hipSuccess) return hip_status(e);
             }
         }
@@ -813,7 +813,7 @@ lscd_status_t spmm_impl(lscd_handle_t h, const void* B, void* C, int32_t N, void
         hipError_t e = lscd::launch_spmm(kind, npad, R, a, 8 * a.per_xcd, s);
         if (e != hipSuccess) return hip_status(e);
         if (S > 1) {
-            e = lscd::launch_reduce(h->d_part, a.C, S, (int64_t)n * h->g.M, s);
+            e = lscd::launch_reduce(part, a.C, S, (int64_t)n * h->g.M, s);
             if (e != hipSuccess) return hip_status(e);
         }
     }
