@@ -269,7 +269,8 @@ lscd_status_t lscd_spmm(lscd_handle_t h, const void* B, void* C, int32_t N, void
  * process ends), not to the handle's workspace.  Allocates nothing and calls no allocating
  * routine; the first call on a device looks up that device's copy of the array.
  * Errors: those of lscd_spmm, plus NOT_SUPPORTED when one launch's partials (splits x N x M x
- * 4 bytes, at most 256 columns per launch) exceed 64 MiB.  The array is shared by every call
+ * 4 bytes, at most 256 columns per launch; M rounded up to whole tiles where N is padded to 64)
+ * exceed 64 MiB.  The array is shared by every call
  * on that GPU and keeps the last call's contents (each launch writes every partial it reads,
  * so nothing needs clearing): calls that overlap on one GPU -- on different streams, or from
  * different threads -- race and must be serialized by the caller.

@@ -50,7 +50,7 @@ hipError_t hipStreamSynchronize(hipStream_t) { return hipSuccess; }
 namespace lscd {
 
 hipError_t launch_spmm(int, int, int, const SpmmArgs&, int, hipStream_t) { return hipErrorNoDevice; }
-hipError_t launch_reduce(const float*, uint16_t*, int, int64_t, hipStream_t) { return hipErrorNoDevice; }
+hipError_t launch_reduce(const float*, uint16_t*, int, int, int, int, int, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_decode(int, const DecodeArgs&, int, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_decode_bitmap(const DecodeArgs&, int, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_decode_three_level(const DecodeArgs&, int, hipStream_t) { return hipErrorNoDevice; }

@@ -285,13 +285,21 @@ lscd_status_t new_handle(const Grid& g, int64_t nnz, int64_t nwords, int32_t max
         const bool indep = h->kind[i] == kKernelIndep || h->kind[i] == kKernelIndep8;
         h->S[i] = plan_splits(g, h->cus, occ, row_groups(g, h->kind[i]), min_tiles, indep, true, 4 * nwords);
         if (h->kind[i] == kKernelShared && i == 2) plan_shared_rows(g, h, 4 * nwords);
-        if (h->S[i] > 1) part = std::max<int64_t>(part, (int64_t)h->S[i] * g.M * (16 << i) * 4);
+        // the shared-B kernels store partial sums in blocks of whole tiles (MB * tm rows)
+        const bool blocked = h->kind[i] == kKernelShared || h->kind[i] == kKernelShared3;
+        if (h->S[i] > 1) part = std::max<int64_t>(part, (int64_t)h->S[i] * (blocked ? g.MB * g.tm : g.M) * (16 << i) * 4);
     }
     h->Rw = pick_reg_vectors_wide(maxw);
     for (int i = 0; i < 3 && kernel_tile && format == 0; ++i) {
         const int npad = 128 + 64 * i;
         const int occ = spmm_blocks_per_cu(kKernelWide, npad, h->Rw, (int)std::min<int64_t>(g.K, 1 << 30), g.tm);
         h->Sw[i] = plan_splits(g, h->cus, occ, g.MB, 4, false, true);
+        // Row blocks that about fill the CUs by themselves (0.9 - 2 per CU): at most two splits.
+        // Filling every resident slot instead (three splits where three workgroups fit a CU)
+        // measured 6 - 10 % slower at N = 96 and 128 on the OPT-30B MLP1 and OPT-66B QKV shapes
+        // (256 and 247 row blocks of 112: 72.5 -> 65.7, 83.4 -> 76.4 and 112.6 -> 105.7 us).
+        if (!getenv("LSCD_SPLITK") && g.MB * 10 >= (int64_t)h->cus * 9 && g.MB < 2 * (int64_t)h->cus)
+            h->Sw[i] = std::min(h->Sw[i], 2);
         if (h->Sw[i] > 1) part = std::max<int64_t>(part, (int64_t)h->Sw[i] * g.M * npad * 4);
     }
     // Tall tiles denser than the shared-B kernel's register stage (R vectors of 4 words per
@@ -741,6 +749,7 @@ lscd_status_t spmm_impl(lscd_handle_t h, const void* B, void* C, int32_t N, void
     a.MB = (int32_t)h->g.MB;
     a.KT = (int32_t)h->g.KT;
     a.TM = h->g.tm;
+    a.PB = 0;
     if (h->format == 1) {
         // bitmap tiles: launches of up to 64 columns (the packed tile is read once per launch)
         for (int32_t c0 = 0; c0 < N; c0 += lscd::kBitmapMaxN) {
@@ -757,7 +766,7 @@ lscd_status_t spmm_impl(lscd_handle_t h, const void* B, void* C, int32_t N, void
             hipError_t e = lscd::launch_spmm(lscd::kKernelBitmap, npad, 0, a, 8 * a.per_xcd, s);
             if (e != hipSuccess) return hip_status(e);
             if (a.S > 1) {
-                e = lscd::launch_reduce(part, a.C, a.S, (int64_t)n * h->g.M, s);
+                e = lscd::launch_reduce(part, a.C, a.S, n, a.M, 0, 0, s);
                 if (e != hipSuccess) return hip_status(e);
             }
         }
@@ -779,7 +788,7 @@ lscd_status_t spmm_impl(lscd_handle_t h, const void* B, void* C, int32_t N, void
             hipError_t e = lscd::launch_spmm(lscd::kKernelThreeLevel, npad, 0, a, 8 * a.per_xcd, s);
             if (e != hipSuccess) return hip_status(e);
             if (a.S > 1) {
-                e = lscd::launch_reduce(part, a.C, a.S, (int64_t)n * h->g.M, s);
+                e = lscd::launch_reduce(part, a.C, a.S, n, a.M, 0, 0, s);
                 if (e != hipSuccess) return hip_status(e);
             }
         }
@@ -809,11 +818,14 @@ lscd_status_t spmm_impl(lscd_handle_t h, const void* B, void* C, int32_t N, void
         a.S = S;
         a.items = a.G * a.S;
         a.per_xcd = (a.items + 7) / 8;
-        if (a.S > 1 && (int64_t)a.S * a.N * h->g.M * 4 > part_bytes) return LSCD_ERROR_NOT_SUPPORTED;
+        // the shared-B kernels store partial sums in blocks of whole tiles
+        a.PB = (kind == lscd::kKernelShared || kind == lscd::kKernelShared3) ? h->g.tm : 0;
+        const int64_t part_rows = a.PB ? (int64_t)a.MB * a.PB : h->g.M;
+        if (a.S > 1 && (int64_t)a.S * a.N * part_rows * 4 > part_bytes) return LSCD_ERROR_NOT_SUPPORTED;
         hipError_t e = lscd::launch_spmm(kind, npad, R, a, 8 * a.per_xcd, s);
         if (e != hipSuccess) return hip_status(e);
         if (S > 1) {
-            e = lscd::launch_reduce(part, a.C, S, (int64_t)n * h->g.M, s);
+            e = lscd::launch_reduce(part, a.C, S, n, a.M, a.PB, a.MB, s);
             if (e != hipSuccess) return hip_status(e);
         }
     }

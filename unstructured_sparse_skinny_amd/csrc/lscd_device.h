@@ -425,6 +425,10 @@ __device__ __forceinline__ void store_results(const f32x4 (&acc)[RG][NCB], float
                     for (int e = 0; e < 4; ++e)
                         if (m + e < a.M) dst[e] = f16_bits(v[e]);
                 }
+            } else if (a.PB) {
+                // partial sums in blocks of TM rows: the workgroup's rows of every column lie
+                // together; rows past M in the last block are padding the split-K pass never reads
+                *reinterpret_cast<f32x4*>(a.part + (((int64_t)s * a.MB + m0 / TM) * a.N + n) * TM + ml) = v;
             } else {
                 float* dst = a.part + ((int64_t)s * a.N + n) * a.M + m;
                 if (vec_m && m + 3 < a.M) {

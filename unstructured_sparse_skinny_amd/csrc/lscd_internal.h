@@ -91,6 +91,7 @@ struct SpmmArgs {
     int32_t G, S;              // row groups (kWaves row blocks each), K splits
     int32_t items, per_xcd;    // G * S work items, items per XCD slot range
     int32_t TM;                // rows of the format's tiles: 64, 80, 96, 112 or 128
+    int32_t PB;                // partial sums in blocks of PB rows, [S][MB][N][PB]; 0: [S][N][M]
 };
 
 struct DecodeArgs {
@@ -149,7 +150,9 @@ hipError_t launch_kind_bitmap(int npad, const SpmmArgs& a, int grid, hipStream_t
 hipError_t launch_kind_three_level(int npad, const SpmmArgs& a, int grid, hipStream_t s, int* occ);
 // Workgroups of a product kernel (variant, N padding, stage size) resident per CU.
 int spmm_blocks_per_cu(int kind, int npad, int R, int K, int TM = kTileM);
-hipError_t launch_reduce(const float* part, uint16_t* C, int S, int64_t NM, hipStream_t s);
+// Split-K pass: C[n][m] = fp16(sum over s of the partial sums), layout [S][N][M] (PB = 0) or
+// [S][MB][N][PB] (MB blocks of PB rows).
+hipError_t launch_reduce(const float* part, uint16_t* C, int S, int N, int M, int PB, int MB, hipStream_t s);
 hipError_t launch_decode(int R, const DecodeArgs& a, int grid, hipStream_t s);
 // Partial-sum scratch of lscd_spmm_noalloc: a file-scope device array of kScratchBytes, one
 // per GPU, held until the process ends.  scratch_partials returns its address on `device`

@@ -4,6 +4,7 @@
 
 #include <stdlib.h>
 
+#include <algorithm>
 #include <mutex>
 #include <vector>
 
@@ -33,6 +34,37 @@ __global__ __launch_bounds__(256) void reduce_kernel(const float* __restrict__ p
             float acc = part[i];
             for (int s = 1; s < S; ++s) acc += part[(int64_t)s * NM + i];
             C[i] = f16_bits(acc);
+        }
+    }
+}
+
+// The same over partial sums in blocks of PB rows ([S][MB][N][PB]): workgroup row y of the grid
+// takes column n = y, its threads four consecutive rows m at a time (one block holds them all:
+// PB and m are multiples of 4), or one row where M is not a multiple of 4.
+__global__ __launch_bounds__(256) void reduce_blocked_kernel(const float* __restrict__ part, uint16_t* __restrict__ C,
+                                                             int S, int N, int M, int PB, int MB) {
+    const int n = blockIdx.y;
+    const int64_t split = (int64_t)MB * N * PB;
+    const int step = gridDim.x * 256;
+    uint16_t* c = C + (int64_t)n * M;
+    if ((M & 3) == 0) {
+        for (int m = 4 * (blockIdx.x * 256 + threadIdx.x); m < M; m += 4 * step) {
+            const int b = m / PB;
+            const int64_t idx = ((int64_t)b * N + n) * PB + (m - b * PB);
+            f32x4 acc = *reinterpret_cast<const f32x4*>(part + idx);
+            for (int s = 1; s < S; ++s) acc += *reinterpret_cast<const f32x4*>(part + s * split + idx);
+            uint2 pk;
+            pk.x = (uint32_t)f16_bits(acc[0]) | ((uint32_t)f16_bits(acc[1]) << 16);
+            pk.y = (uint32_t)f16_bits(acc[2]) | ((uint32_t)f16_bits(acc[3]) << 16);
+            *reinterpret_cast<uint2*>(c + m) = pk;
+        }
+    } else {
+        for (int m = blockIdx.x * 256 + threadIdx.x; m < M; m += step) {
+            const int b = m / PB;
+            const int64_t idx = ((int64_t)b * N + n) * PB + (m - b * PB);
+            float acc = part[idx];
+            for (int s = 1; s < S; ++s) acc += part[s * split + idx];
+            c[m] = f16_bits(acc);
         }
     }
 }
@@ -171,7 +203,18 @@ int spmm_blocks_per_cu(int kind, int npad, int R, int K, int TM) {
     return (e == hipSuccess && occ > 0) ? occ : 1;
 }
 
-hipError_t launch_reduce(const float* part, uint16_t* C, int S, int64_t NM, hipStream_t st) {
+hipError_t launch_reduce(const float* part, uint16_t* C, int S, int N, int M, int PB, int MB, hipStream_t st) {
+    if (PB > 0) {
+        const int64_t work = (M & 3) == 0 ? M / 4 : M;
+        int64_t bx = (work + 255) / 256;
+        const int64_t cap = std::max<int64_t>(1, 4096 / std::max(N, 1));
+        if (bx > cap) bx = cap;
+        if (bx < 1) bx = 1;
+        hipLaunchKernelGGL(reduce_blocked_kernel, dim3((unsigned)bx, (unsigned)N), dim3(256), 0, st, part, C, S, N, M,
+                           PB, MB);
+        return hipGetLastError();
+    }
+    const int64_t NM = (int64_t)N * M;
     const int64_t work = (NM & 3) == 0 ? NM / 4 : NM;
     int64_t blocks = (work + 255) / 256;
     if (blocks > 4096) blocks = 4096;
@@ -179,7 +222,6 @@ hipError_t launch_reduce(const float* part, uint16_t* C, int S, int64_t NM, hipS
     hipLaunchKernelGGL(reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, st, part, C, S, NM);
     return hipGetLastError();
 }
-
 // The partial sums of lscd_spmm_noalloc live here instead of in a handle's workspace.  In host
 // code `scratch` names a host-side stand-in, not device memory: only the address that
 // hipGetSymbolAddress returns for the current device may be handed to kernels or copies.
