@@ -130,11 +130,11 @@ def test_wide_limits():
     torch.cuda.synchronize()
 
 
-def test_split_plan_low_fill_doubles():
-    """192 row blocks of 64 rows at 50 % sparsity: the N > 64 kernel's slot-filling count (2,
-    75 % of the resident slots on 256 CUs) is doubled to 4, while the shared-B launch at
-    N = 64 (10 splits, 94 % of the slots) keeps its count.  The product at N = 128 with the
-    doubled plan is bit-exact on integer inputs (sampled rows)."""
+def test_split_plan_192_row_blocks():
+    """192 row blocks of 64 rows at 50 % sparsity on 256 CUs: the N > 64 kernel takes 4 splits
+    (768 workgroups, three per CU: the resident slots, and the most the planner allows), the
+    shared-B launch at N = 64 fills its slots.  The product at N = 128 with this plan is
+    bit-exact on integer inputs (sampled rows)."""
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([31337, 128])))
     M, K, N = 12288, 2048, 128

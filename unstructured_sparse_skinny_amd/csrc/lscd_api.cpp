@@ -294,12 +294,18 @@ lscd_status_t new_handle(const Grid& g, int64_t nnz, int64_t nwords, int32_t max
         const int npad = 128 + 64 * i;
         const int occ = spmm_blocks_per_cu(kKernelWide, npad, h->Rw, (int)std::min<int64_t>(g.K, 1 << 30), g.tm);
         h->Sw[i] = plan_splits(g, h->cus, occ, g.MB, 4, false, true);
-        // Row blocks that about fill the CUs by themselves (0.9 - 2 per CU): at most two splits.
-        // Filling every resident slot instead (three splits where three workgroups fit a CU)
-        // measured 6 - 10 % slower at N = 96 and 128 on the OPT-30B MLP1 and OPT-66B QKV shapes
-        // (256 and 247 row blocks of 112: 72.5 -> 65.7, 83.4 -> 76.4 and 112.6 -> 105.7 us).
-        if (!getenv("LSCD_SPLITK") && g.MB * 10 >= (int64_t)h->cus * 9 && g.MB < 2 * (int64_t)h->cus)
-            h->Sw[i] = std::min(h->Sw[i], 2);
+        // Fewer splits than would fill every resident slot: each split adds fp32 partial sums,
+        // and past about three workgroups per CU they cost more than the extra workgroups hide.
+        // At most 3 * CUs / row blocks splits (measured: OPT-175B MLP2 shape at 60 % and N = 96
+        // and 128, 192 row blocks, 4 splits instead of 5: 297.1 -> 277.9 and 340.2 -> 317.9 us;
+        // OPT-175B QKV at 50 % and N = 128, 576 row blocks, 1 instead of 2: 266.8 -> 248.7 us),
+        // and at most two where the row blocks alone about fill the CUs (0.9 - 2 per CU; OPT-30B
+        // MLP1 and OPT-66B QKV shapes, 256 and 247 row blocks of 112, at N = 96 and 128: 72.5 ->
+        // 65.7, 83.4 -> 76.4 and 112.6 -> 105.7 us against three).
+        if (!getenv("LSCD_SPLITK")) {
+            h->Sw[i] = (int)std::min<int64_t>(h->Sw[i], std::max<int64_t>(1, 3 * (int64_t)h->cus / g.MB));
+            if (g.MB * 10 >= (int64_t)h->cus * 9 && g.MB < 2 * (int64_t)h->cus) h->Sw[i] = std::min(h->Sw[i], 2);
+        }
         if (h->Sw[i] > 1) part = std::max<int64_t>(part, (int64_t)h->Sw[i] * g.M * npad * 4);
     }
     // Tall tiles denser than the shared-B kernel's register stage (R vectors of 4 words per
