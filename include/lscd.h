@@ -93,8 +93,8 @@ typedef struct {
  *          +0/-0 ((bits & 0x7FFF) != 0).  With a mask, kept zeros are stored as well.
  *   tile_m, tile_k  tile shape, 1 <= tile_m*tile_k <= 65536.
  *   nnz_padded, num_tiles  out: words and tiles of the encoding.
- * Returns INVALID_VALUE for null outputs/A, M or K < 1, or a bad tile; NOT_SUPPORTED when
- * the encoding would need 2^32 words or more.
+ * Returns INVALID_VALUE for null outputs/A, M or K < 1 or above 2^30 (every encoder and
+ * lscd_import), or a bad tile; NOT_SUPPORTED when the encoding would need 2^32 words or more.
  */
 lscd_status_t lscd_pack_size(const uint16_t* A, const uint8_t* mask, int64_t M, int64_t K,
                              int32_t tile_m, int32_t tile_k, int64_t* nnz_padded, int64_t* num_tiles);

@@ -145,6 +145,14 @@ def test_argument_errors_are_statuses():
     # too-short output arrays are refused by the C entry point
     st = L._lib.lscd_pack(A.ctypes.data, None, 4, 4, 2, 2, None, 0, None, 0)
     assert st == L.LSCD_ERROR_INVALID_VALUE
+    # M or K above 2^30 is refused before A is read (the kernels index in 32 bits)
+    nw, nt = L.ctypes.c_int64(), L.ctypes.c_int64()
+    for M, K in ((2**30 + 1, 1), (1, 2**30 + 1), (2**31, 4)):
+        st = L._lib.lscd_pack_size(A.ctypes.data, None, M, K, 64, 64, L.ctypes.byref(nw), L.ctypes.byref(nt))
+        assert st == L.LSCD_ERROR_INVALID_VALUE, (M, K)
+    h = L.ctypes.c_void_p()
+    st = L._lib.lscd_import(None, 0, np.zeros(2, np.uint32).ctypes.data, 2**30 + 64, 64, 64, 64, L.ctypes.byref(h))
+    assert st == L.LSCD_ERROR_INVALID_VALUE and not h.value
     assert L._lib.lscd_spmm(None, None, None, 16, None) == L.LSCD_ERROR_INVALID_VALUE
     assert L._lib.lscd_destroy(None) == L.LSCD_SUCCESS
     assert L._lib.lscd_get_info(None, None) == L.LSCD_ERROR_INVALID_VALUE

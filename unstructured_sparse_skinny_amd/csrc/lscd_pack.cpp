@@ -28,7 +28,8 @@ namespace lscd {
 
 bool make_grid(int64_t M, int64_t K, int32_t tm, int32_t tk, Grid* g) {
     if (M < 1 || K < 1 || tm < 1 || tk < 1 || (int64_t)tm * tk > 65536) return false;
-    if (M > (int64_t)1 << 31 || K > (int64_t)1 << 31) return false;
+    // The kernels index rows and columns, the last row block's padding included, in 32 bits.
+    if (M > kMaxDim || K > kMaxDim) return false;
     g->M = M;
     g->K = K;
     g->tm = tm;
