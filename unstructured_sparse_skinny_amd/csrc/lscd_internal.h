@@ -20,8 +20,6 @@ constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 
 // ---------------------------------------------------------------- host encoder
-// Largest M and K an encoding accepts.
-constexpr int64_t kMaxDim = (int64_t)1 << 30;
 struct Grid {
     int64_t M, K;
     int32_t tm, tk;

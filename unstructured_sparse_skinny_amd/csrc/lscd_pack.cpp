@@ -26,6 +26,9 @@
 
 namespace lscd {
 
+// Largest M and K an encoding accepts.
+constexpr int64_t kMaxDim = (int64_t)1 << 30;
+
 bool make_grid(int64_t M, int64_t K, int32_t tm, int32_t tk, Grid* g) {
     if (M < 1 || K < 1 || tm < 1 || tk < 1 || (int64_t)tm * tk > 65536) return false;
     // The kernels index rows and columns, the last row block's padding included, in 32 bits.
